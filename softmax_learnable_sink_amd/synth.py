@@ -1,0 +1,117 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the smoke run.
+
+This module holds no attention arithmetic.  It draws N(0,1) tensors with
+``numpy.random.default_rng(seed)``, rounds them to bfloat16 (round to nearest
+even) when the case is bf16, and builds paged KV caches with a seeded random
+page permutation.  The same bits go to the GPU library and to the CPU oracle.
+
+bf16 tensors are returned as ``uint16`` bit patterns; ``bf16_to_f32`` gives
+their exact float values.  fp32 tensors are returned as ``float32``.
+
+Draw order (fixed, so a seed names one input set):
+  prefill:  q, k, v, [dout], sink
+  decode:   q, sink, context lengths, page permutation, k pool, v pool
+"""
+
+import numpy as np
+
+BF16 = "bf16"
+F32 = "f32"
+
+
+def f32_to_bf16_bits(x):
+    """Round float32 values to bfloat16 (nearest even) and return the bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_to_f32(bits):
+    """Exact float32 values of bfloat16 bit patterns."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def values(x, dtype):
+    """Exact float32 values of a synth tensor of the given dtype."""
+    return bf16_to_f32(x) if dtype == BF16 else np.asarray(x, dtype=np.float32)
+
+
+def _normal(rng, shape, dtype):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return f32_to_bf16_bits(x) if dtype == BF16 else x
+
+
+def prefill_case(B, Sq, Sk, Hq, Hkv, D, dtype=BF16, seed=0, sink=True, dout=False):
+    """Q [B,Sq,Hq,D], K/V [B,Sk,Hkv,D], optional dO [B,Sq,Hq,D], sink [Hq] fp32."""
+    rng = np.random.default_rng(seed)
+    case = {
+        "dtype": dtype,
+        "q": _normal(rng, (B, Sq, Hq, D), dtype),
+        "k": _normal(rng, (B, Sk, Hkv, D), dtype),
+        "v": _normal(rng, (B, Sk, Hkv, D), dtype),
+    }
+    if dout:
+        case["dout"] = _normal(rng, (B, Sq, Hq, D), dtype)
+    case["sink"] = rng.standard_normal(size=(Hq,), dtype=np.float32) if sink else None
+    return case
+
+
+def decode_case(B, Hq, Hkv, D, page_size, len_lo, len_hi, dtype=BF16, seed=0,
+                sink=True, max_len=None, lengths=None, nan_poison=False):
+    """Paged decode inputs.
+
+    Context lengths L_b ~ integers U[len_lo, len_hi] (inclusive), or `lengths`.
+    Sequence b owns ceil(L_b / P) pages; a seeded random permutation of all
+    page ids is handed out in order (b, page).  block_table is int32
+    [B, ceil(max_len / P)] padded with -1.  Pools are [num_pages, P, Hkv, D].
+    With nan_poison, the slots past L_b in each sequence's last page hold NaN.
+    """
+    rng = np.random.default_rng(seed)
+    case = {"dtype": dtype, "q": _normal(rng, (B, Hq, D), dtype)}
+    case["sink"] = rng.standard_normal(size=(Hq,), dtype=np.float32) if sink else None
+    if lengths is None:
+        lengths = rng.integers(len_lo, len_hi, size=B, endpoint=True)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    max_len = int(max_len if max_len is not None else max(len_hi, int(lengths.max())))
+    npages = (lengths.astype(np.int64) + page_size - 1) // page_size
+    total = int(npages.sum())
+    perm = rng.permutation(total).astype(np.int32)
+    max_pages = (max_len + page_size - 1) // page_size
+    bt = np.full((B, max_pages), -1, dtype=np.int32)
+    pos = 0
+    for b in range(B):
+        n = int(npages[b])
+        bt[b, :n] = perm[pos:pos + n]
+        pos += n
+    shape = (total, page_size, Hkv, D)
+    kc = _normal(rng, shape, dtype)
+    vc = _normal(rng, shape, dtype)
+    if nan_poison:
+        nan = f32_to_bf16_bits(np.float32(np.nan)) if dtype == BF16 else np.float32(np.nan)
+        for b in range(B):
+            L = int(lengths[b])
+            last = L - 1
+            page = bt[b, last // page_size]
+            off = last % page_size + 1
+            kc[page, off:] = nan
+            vc[page, off:] = nan
+    case.update({"k_cache": kc, "v_cache": vc, "block_table": bt, "seqlens": lengths,
+                 "page_size": page_size, "num_pages": total, "max_len": max_len})
+    return case
+
+
+def poison_unselected(case, window):
+    """Write NaN into every cached token that the window leaves out (for tests)."""
+    w1, w2 = window
+    P = case["page_size"]
+    nan = f32_to_bf16_bits(np.float32(np.nan)) if case["dtype"] == BF16 else np.float32(np.nan)
+    for b, L in enumerate(case["seqlens"].tolist()):
+        if L <= w1 + w2:
+            continue
+        t = np.arange(w1, L - w2)
+        pages = case["block_table"][b, t // P]
+        case["k_cache"][pages, t % P] = nan
+        case["v_cache"][pages, t % P] = nan
+    return case
