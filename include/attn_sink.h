@@ -1,0 +1,184 @@
+/*
+ * attn_sink.h -- C ABI of libattn_sink.so: attention with a learnable per-head
+ * sink logit on AMD MI355X (gfx950).
+ *
+ * What is computed.  For query head h (KV head h / (Hq/Hkv)), query row i and
+ * its visible key set V_i:
+ *     s_ij  = softmax_scale * <q_i, k_j>
+ *     Z_i   = exp(sink[h]) + sum_{j in V_i} exp(s_ij)
+ *     O_i   = sum_{j in V_i} exp(s_ij) * v_j / Z_i
+ *     LSE_i = ln Z_i
+ * The sink is one learnable value per head (a tensor of shape (nheads,)),
+ * added as an extra logit before the softmax; it takes part in the denominator
+ * only and has no value row.  Its gradient is returned by the backward pass.
+ *   -- flash-attention PR #1819 "feat: Implement Sink Attention", Description;
+ *      sglang PR #8825 "feat: openai oss attention sink support with
+ *      trtllm-gen backend", Summary of Changes (an additional per-head value in
+ *      the softmax denominator, None when the layer has no sink, passed to
+ *      both the decode and the extend path).
+ * The sink is in the units of the scaled scores (it is not multiplied by
+ * softmax_scale).  sink == NULL means "no sink", identical to -inf.
+ *
+ * Visibility.  Causal masking is bottom-right aligned: query row i of Sq sits
+ * at absolute position p = Sk - Sq + i and sees keys j <= p.  An optional
+ * first/last window (W1, W2) = (window_first, window_last) further keeps only
+ * keys with j < W1 or j > p - W2: the first W1 tokens and the last W2 tokens
+ * up to and including the current one.  For the newest token of a sequence
+ * of length L this is the whole prefix when L <= W1 + W2, and otherwise
+ * tokens [0, W1) followed by [L - W2, L).
+ *   -- sglang PR #12504 "To implement attention-sink", Motivation (first
+ *      window 1024, last window 7168), Modifications and the bot's Code
+ *      Review (page table = first-window slice followed by last-window slice,
+ *      only when the sequence is longer than 1024 + 7168; kernel length
+ *      becomes 1024 + 7168), and the maintainer's request to keep the last
+ *      7168 tokens of each sequence.
+ * Passing window_first = window_last = -1 disables the window.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major
+ *     tensors, 16-byte aligned.  Shapes are given with each function.
+ *   - The caller allocates and owns every buffer, including workspaces.  The
+ *     library allocates no device memory, keeps no state other than a
+ *     thread-local error message, and never synchronises: work is enqueued on
+ *     `hip_stream` (a hipStream_t; NULL = the default stream).
+ *   - Outputs are overwritten (never accumulated into) and must not alias
+ *     inputs.  Inputs are never written.
+ *   - Every argument is validated on the host BEFORE any HIP call.  On error
+ *     nothing is enqueued, a status below is returned and
+ *     attn_sink_last_error() describes the problem.
+ *   - Values that live on the device (seqlens_k, block_table entries) are
+ *     preconditions and are not validated: 0 <= block_table entries used <
+ *     num_pages and 1 <= seqlens_k[b] <= max_pages_per_seq * page_size.
+ *   - dtype: ATTN_SINK_BF16 (q/k/v/o/dO/dQ/dK/dV in bfloat16, all
+ *     accumulation in fp32) or ATTN_SINK_F32 (fp32 everywhere; forward
+ *     prefill only).  sink, lse and dsink are always fp32.
+ */
+#ifndef ATTN_SINK_H
+#define ATTN_SINK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_SINK_ABI_VERSION 1
+
+typedef enum {
+  ATTN_SINK_OK = 0,
+  ATTN_SINK_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, misalignment     */
+  ATTN_SINK_ERR_UNSUPPORTED = 2, /* valid but not implemented (D, dtype ...) */
+  ATTN_SINK_ERR_WORKSPACE = 3,   /* workspace missing or too small           */
+  ATTN_SINK_ERR_HIP = 4          /* a HIP launch error (message has details) */
+} attn_sink_status;
+
+typedef enum { ATTN_SINK_BF16 = 0, ATTN_SINK_F32 = 1 } attn_sink_dtype;
+
+/* Version of this ABI (ATTN_SINK_ABI_VERSION of the built library). */
+int attn_sink_abi_version(void);
+
+/* Message of the last failing call on this thread ("" if none). The pointer
+ * stays valid until the next call on this thread. */
+const char* attn_sink_last_error(void);
+
+/*
+ * Forward prefill / extend with Sq queries against Sk keys per sequence.
+ *   q     [B, Sq, Hq, D]         (dtype)
+ *   k, v  [B, Sk, Hkv, D]        (dtype)
+ *   sink  [Hq] fp32, or NULL for no sink
+ *   o     [B, Sq, Hq, D]         (dtype)            -- output
+ *   lse   [B, Hq, Sq] fp32 natural log, sink included, or NULL -- output
+ * Requirements: B, Sq, Hq, Hkv >= 1; Sk >= 0; Hq % Hkv == 0; D in {64, 128};
+ * softmax_scale finite and > 0; a window needs causal = 1, window_first >= 0
+ * and window_last >= 1.  A row that sees no key gets O = 0 and LSE = sink
+ * (or -inf without a sink).
+ */
+int attn_sink_fwd_prefill(const void* q, const void* k, const void* v, const float* sink,
+                          void* o, float* lse, int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                          float softmax_scale, int causal, int window_first, int window_last,
+                          int dtype, void* hip_stream);
+
+/*
+ * Forward paged decode: one new query token per sequence, whose K/V is already
+ * stored in the cache and counted in seqlens_k.
+ *   q            [B, Hq, D] bf16
+ *   k_cache,
+ *   v_cache      [num_pages, page_size, Hkv, D] bf16
+ *   block_table  [B, max_pages_per_seq] int32: token t of sequence b lives in
+ *                page block_table[b, t / page_size] at offset t % page_size
+ *                (slot = page * page_size + t % page_size). Entries past the
+ *                sequence's last selected page are never read.
+ *   seqlens_k    [B] int32 device, context length L_b including the new token
+ *   sink         [Hq] fp32 or NULL
+ *   o            [B, Hq, D] bf16                   -- output
+ *   lse          [B, Hq] fp32 or NULL              -- output
+ *   num_splits   split-K parts per sequence; 0 picks a heuristic. The result
+ *                does not depend on it beyond fp32 rounding order.
+ *   workspace    device scratch of at least attn_sink_decode_workspace_bytes()
+ *                bytes for the same arguments; contents need no initialisation.
+ * Requirements: D in {64, 128}; page_size a power of two in [1, 256];
+ * Hq % Hkv == 0; max_pages_per_seq >= 1; num_pages >= 1.
+ * With a window only the selected tokens are read from the cache.
+ */
+int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* seqlens_k,
+                               const float* sink, void* o, float* lse, int B, int Hq, int Hkv,
+                               int D, int page_size, int max_pages_per_seq, int num_pages,
+                               float softmax_scale, int window_first, int window_last,
+                               int num_splits, void* workspace, size_t workspace_bytes,
+                               int dtype, void* hip_stream);
+
+/* Workspace needed by attn_sink_fwd_decode_paged with the same arguments
+ * (0 on invalid arguments). */
+size_t attn_sink_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int page_size,
+                                        int max_pages_per_seq, int window_first,
+                                        int window_last, int num_splits);
+
+/*
+ * Backward of the forward prefill (bf16).  Gradients of sum(dO * O):
+ *   q, k, v, o, dout   as in the forward (o is the forward's output)
+ *   lse    [B, Hq, Sq] fp32 from the forward (sink included)
+ *   sink   [Hq] fp32 or NULL
+ *   dq     [B, Sq, Hq, D], dk, dv [B, Sk, Hkv, D] (dtype) -- outputs
+ *   dsink  [Hq] fp32, required iff sink != NULL      -- output
+ * dSink_h = -sum_{b,i} exp(sink_h - LSE_i) * <dO_i, O_i>, reduced in fp32 in
+ * a fixed order.
+ * workspace: at least attn_sink_bwd_workspace_bytes() bytes.
+ */
+int attn_sink_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, const float* sink, void* dq, void* dk, void* dv,
+                  float* dsink, int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                  float softmax_scale, int causal, int window_first, int window_last,
+                  void* workspace, size_t workspace_bytes, int dtype, void* hip_stream);
+
+/* Workspace needed by attn_sink_bwd (0 on invalid arguments). */
+size_t attn_sink_bwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D);
+
+/*
+ * Test / debug exports that run the same device index map as the decode
+ * kernel.  Selection of sequence b: if a window is given and L_b > W1 + W2,
+ * logical index u maps to token u for u < W1 and to L_b - W2 + (u - W1)
+ * otherwise; without a window (or L_b <= W1 + W2) token = u.
+ *
+ * select_slots: slots [B, max_sel] int64 -- slot of the u-th selected token,
+ *               -1 past the sequence's selection; counts [B] int32 = number
+ *               of selected tokens (may exceed max_sel; only max_sel written).
+ */
+int attn_sink_decode_select_slots(const int32_t* block_table, const int32_t* seqlens_k, int B,
+                                  int max_pages_per_seq, int page_size, int window_first,
+                                  int window_last, int64_t* slots, int32_t* counts, int max_sel,
+                                  void* hip_stream);
+
+/* gather_kv: k_out, v_out [B, max_sel, Hkv, D] (dtype) -- rows of the selected
+ * slots in selection order; rows past the selection are zero-filled. */
+int attn_sink_gather_kv(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                        const int32_t* seqlens_k, int B, int Hkv, int D, int page_size,
+                        int max_pages_per_seq, int window_first, int window_last, void* k_out,
+                        void* v_out, int max_sel, int dtype, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_SINK_H */

@@ -1,0 +1,250 @@
+"""Thin ctypes binding of libattn_sink.so (C ABI in include/attn_sink.h).
+
+Argument marshalling only: tensors are checked for device, dtype and layout,
+outputs and workspaces are allocated with torch when the caller passes none,
+and the pointers plus the current HIP stream go to the C entry points.  Every
+step of the computation runs in the library's HIP kernels.  The functions
+carry the C names.  A missing library raises; there is no fallback.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_sink.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+BF16, F32 = 0, 1
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "attn_sink_abi_version": ([], _i),
+    "attn_sink_last_error": ([], ctypes.c_char_p),
+    "attn_sink_fwd_prefill": ([_vp, _vp, _vp, _vp, _vp, _vp] + [_i] * 6 + [_f, _i, _i, _i, _i, _vp], _i),
+    "attn_sink_fwd_decode_paged": ([_vp] * 8 + [_i] * 7 + [_f, _i, _i, _i, _vp, _sz, _i, _vp], _i),
+    "attn_sink_decode_workspace_bytes": ([_i] * 9, _sz),
+    "attn_sink_bwd": ([_vp] * 11 + [_i] * 6 + [_f, _i, _i, _i, _vp, _sz, _i, _vp], _i),
+    "attn_sink_bwd_workspace_bytes": ([_i] * 6, _sz),
+    "attn_sink_decode_select_slots": ([_vp, _vp] + [_i] * 5 + [_vp, _vp, _i, _vp], _i),
+    "attn_sink_gather_kv": ([_vp] * 4 + [_i] * 7 + [_vp, _vp, _i, _i, _vp], _i),
+}
+
+
+def lib():
+    """Load libattn_sink.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m softmax_learnable_sink_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+class AttnSinkError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"attn_sink status {status}: {message}")
+        self.status = status
+
+
+def _check(status):
+    if status != OK:
+        raise AttnSinkError(status, lib().attn_sink_last_error().decode())
+
+
+def abi_version():
+    return lib().attn_sink_abi_version()
+
+
+def last_error():
+    return lib().attn_sink_last_error().decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _window(window):
+    if window is None:
+        return -1, -1
+    w1, w2 = window
+    return int(w1), int(w2)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t, name, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def attn_sink_fwd_prefill(q, k, v, sink=None, causal=True, softmax_scale=None, window=None,
+                          out=None, lse=None, return_lse=True):
+    """O [B,Sq,Hq,D], LSE [B,Hq,Sq] for q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D], sink [Hq] fp32."""
+    dev = q.device
+    _need(q, "q")
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Sk, Hkv, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if sink is not None:
+        _need(sink, "sink", torch.float32, dev)
+        if sink.shape != (Hq,):
+            raise ValueError(f"sink must have shape ({Hq},)")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    w1, w2 = _window(window)
+    _check(lib().attn_sink_fwd_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(out), _ptr(lse),
+                                       B, Sq, Sk, Hq, Hkv, D, scale, int(bool(causal)), w1, w2,
+                                       _dtype_code(q), _stream(dev)))
+    return out, lse
+
+
+def attn_sink_decode_workspace_bytes(B, Hq, Hkv, D, page_size, max_pages_per_seq, window=None,
+                                     num_splits=0):
+    w1, w2 = _window(window)
+    return lib().attn_sink_decode_workspace_bytes(B, Hq, Hkv, D, page_size, max_pages_per_seq,
+                                                  w1, w2, num_splits)
+
+
+def attn_sink_fwd_decode_paged(q, k_cache, v_cache, block_table, seqlens_k, sink=None,
+                               softmax_scale=None, window=None, num_splits=0, out=None, lse=None,
+                               workspace=None, return_lse=True):
+    """O [B,Hq,D], LSE [B,Hq] for one new token per sequence against a paged KV cache."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(seqlens_k, "seqlens_k", torch.int32, dev)
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (num_pages, page_size, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [num_pages, page_size, Hkv, D]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seqlens_k.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seqlens_k [B]")
+    max_pages = block_table.shape[1]
+    if sink is not None:
+        _need(sink, "sink", torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    w1, w2 = _window(window)
+    need = lib().attn_sink_decode_workspace_bytes(B, Hq, Hkv, D, page_size, max_pages, w1, w2,
+                                                  num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib().attn_sink_fwd_decode_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seqlens_k), _ptr(sink),
+        _ptr(out), _ptr(lse), B, Hq, Hkv, D, page_size, max_pages, num_pages, scale, w1, w2,
+        num_splits, _ptr(workspace), workspace.numel() * workspace.element_size(), BF16,
+        _stream(dev)))
+    return out, lse
+
+
+def attn_sink_bwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D):
+    return lib().attn_sink_bwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D)
+
+
+def attn_sink_bwd(q, k, v, o, dout, lse, sink=None, causal=True, softmax_scale=None, window=None,
+                  dq=None, dk=None, dv=None, dsink=None, workspace=None):
+    """(dq, dk, dv, dsink) of sum(dout * O); dsink is None when sink is None."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, name, torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if sink is not None:
+        _need(sink, "sink", torch.float32, dev)
+        if dsink is None:
+            dsink = torch.empty_like(sink)
+    need = lib().attn_sink_bwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    w1, w2 = _window(window)
+    _check(lib().attn_sink_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(sink), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(dsink), B, Sq, Sk, Hq, Hkv, D, scale, int(bool(causal)), w1, w2,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), BF16, _stream(dev)))
+    return dq, dk, dv, dsink
+
+
+def attn_sink_decode_select_slots(block_table, seqlens_k, page_size, max_sel, window=None):
+    """(slots [B, max_sel] int64, counts [B] int32) from the decode kernel's index map."""
+    dev = block_table.device
+    _need(block_table, "block_table", torch.int32)
+    _need(seqlens_k, "seqlens_k", torch.int32, dev)
+    B, max_pages = block_table.shape
+    slots = torch.empty((B, max_sel), dtype=torch.int64, device=dev)
+    counts = torch.empty((B,), dtype=torch.int32, device=dev)
+    w1, w2 = _window(window)
+    _check(lib().attn_sink_decode_select_slots(_ptr(block_table), _ptr(seqlens_k), B, max_pages,
+                                               page_size, w1, w2, _ptr(slots), _ptr(counts),
+                                               max_sel, _stream(dev)))
+    return slots, counts
+
+
+def attn_sink_gather_kv(k_cache, v_cache, block_table, seqlens_k, max_sel, window=None):
+    """K/V rows [B, max_sel, Hkv, D] of the selected tokens (zero past the selection)."""
+    dev = k_cache.device
+    _need(k_cache, "k_cache")
+    _need(v_cache, "v_cache", k_cache.dtype, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(seqlens_k, "seqlens_k", torch.int32, dev)
+    num_pages, page_size, Hkv, D = k_cache.shape
+    B, max_pages = block_table.shape
+    k_out = torch.empty((B, max_sel, Hkv, D), dtype=k_cache.dtype, device=dev)
+    v_out = torch.empty_like(k_out)
+    w1, w2 = _window(window)
+    _check(lib().attn_sink_gather_kv(_ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                     _ptr(seqlens_k), B, Hkv, D, page_size, max_pages, w1, w2,
+                                     _ptr(k_out), _ptr(v_out), max_sel, _dtype_code(k_cache),
+                                     _stream(dev)))
+    return k_out, v_out

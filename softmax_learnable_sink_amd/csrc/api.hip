@@ -1,0 +1,258 @@
+// C ABI of libattn_sink.so (declared in include/attn_sink.h).
+//
+// Every entry point validates all host-visible arguments before it makes any
+// HIP call, so invalid input never reaches the device; device-resident values
+// (sequence lengths, block-table entries) are documented preconditions.
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "attn_sink.h"
+#include "launch.h"
+
+using namespace attn_sink;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATTN_SINK_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATTN_SINK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+// Window arguments: both -1 (off) or w1 >= 0 and w2 >= 1.
+int check_window(int w1, int w2) {
+  const bool off = (w1 == -1 && w2 == -1);
+  REQUIRE(off || (w1 >= 0 && w2 >= 1), ATTN_SINK_ERR_INVALID_ARG,
+          "window_first/window_last must both be -1 (no window) or satisfy "
+          "window_first >= 0 and window_last >= 1 (got %d, %d)", w1, w2);
+  return ATTN_SINK_OK;
+}
+
+int check_heads(int Hq, int Hkv, int D) {
+  REQUIRE(Hq >= 1 && Hkv >= 1, ATTN_SINK_ERR_INVALID_ARG, "Hq and Hkv must be >= 1 (got %d, %d)",
+          Hq, Hkv);
+  REQUIRE(Hq % Hkv == 0, ATTN_SINK_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq,
+          Hkv);
+  REQUIRE(D == 64 || D == 128, ATTN_SINK_ERR_UNSUPPORTED, "head dim D must be 64 or 128 (got %d)",
+          D);
+  return ATTN_SINK_OK;
+}
+
+int check_scale(float scale) {
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_SINK_ERR_INVALID_ARG,
+          "softmax_scale must be finite and > 0 (got %g)", (double)scale);
+  return ATTN_SINK_OK;
+}
+
+bool fits_int32(long long x) { return x >= 0 && x <= INT_MAX; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_sink_abi_version(void) { return ATTN_SINK_ABI_VERSION; }
+
+const char* attn_sink_last_error(void) { return g_last_error.c_str(); }
+
+int attn_sink_fwd_prefill(const void* q, const void* k, const void* v, const float* sink, void* o,
+                          float* lse, int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                          float softmax_scale, int causal, int window_first, int window_last,
+                          int dtype, void* hip_stream) {
+  REQUIRE(dtype == ATTN_SINK_BF16 || dtype == ATTN_SINK_F32, ATTN_SINK_ERR_UNSUPPORTED,
+          "unknown dtype %d", dtype);
+  REQUIRE(B >= 1 && Sq >= 1 && Sk >= 0, ATTN_SINK_ERR_INVALID_ARG,
+          "need B >= 1, Sq >= 1, Sk >= 0 (got %d, %d, %d)", B, Sq, Sk);
+  if (int r = check_heads(Hq, Hkv, D)) return r;
+  if (int r = check_scale(softmax_scale)) return r;
+  if (int r = check_window(window_first, window_last)) return r;
+  REQUIRE(causal == 0 || causal == 1, ATTN_SINK_ERR_INVALID_ARG, "causal must be 0 or 1");
+  REQUIRE(window_last < 0 || causal, ATTN_SINK_ERR_UNSUPPORTED,
+          "the first/last window needs causal = 1");
+  REQUIRE(q && o && (Sk == 0 || (k && v)), ATTN_SINK_ERR_INVALID_ARG,
+          "q, k, v and o must not be NULL");
+  REQUIRE(aligned16(q) && aligned16(o) && aligned16(k) && aligned16(v), ATTN_SINK_ERR_INVALID_ARG,
+          "q, k, v and o must be 16-byte aligned");
+  REQUIRE(aligned4(sink) && aligned4(lse), ATTN_SINK_ERR_INVALID_ARG,
+          "sink and lse must be 4-byte aligned");
+  REQUIRE(fits_int32((long long)B * Sq * Hq) && fits_int32((long long)B * Sk * Hkv),
+          ATTN_SINK_ERR_UNSUPPORTED, "too many rows for 32-bit row indices");
+  PrefillArgs a{q, k, v, sink, o, lse, B, Sq, Sk, Hq, Hkv, D, softmax_scale, causal,
+                window_first, window_last};
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  return hip_status(dtype == ATTN_SINK_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st),
+                    "attn_sink_fwd_prefill launch");
+}
+
+static int check_decode_common(int B, int Hq, int Hkv, int D, int page_size, int max_pages,
+                               int w1, int w2, int num_splits) {
+  REQUIRE(B >= 1, ATTN_SINK_ERR_INVALID_ARG, "B must be >= 1 (got %d)", B);
+  if (int r = check_heads(Hq, Hkv, D)) return r;
+  REQUIRE(pow2(page_size) && page_size <= 256, ATTN_SINK_ERR_UNSUPPORTED,
+          "page_size must be a power of two in [1, 256] (got %d)", page_size);
+  REQUIRE(max_pages >= 1, ATTN_SINK_ERR_INVALID_ARG, "max_pages_per_seq must be >= 1");
+  REQUIRE(fits_int32((long long)max_pages * page_size), ATTN_SINK_ERR_UNSUPPORTED,
+          "max_pages_per_seq * page_size exceeds 2^31 - 1");
+  REQUIRE(num_splits >= 0, ATTN_SINK_ERR_INVALID_ARG, "num_splits must be >= 0");
+  return check_window(w1, w2);
+}
+
+size_t attn_sink_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int page_size,
+                                        int max_pages_per_seq, int window_first, int window_last,
+                                        int num_splits) {
+  if (check_decode_common(B, Hq, Hkv, D, page_size, max_pages_per_seq, window_first, window_last,
+                          num_splits) != ATTN_SINK_OK)
+    return 0;
+  return plan_decode(B, Hq, Hkv, D, page_size, max_pages_per_seq, window_first, window_last,
+                     num_splits)
+      .workspace_bytes;
+}
+
+int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* seqlens_k,
+                               const float* sink, void* o, float* lse, int B, int Hq, int Hkv,
+                               int D, int page_size, int max_pages_per_seq, int num_pages,
+                               float softmax_scale, int window_first, int window_last,
+                               int num_splits, void* workspace, size_t workspace_bytes, int dtype,
+                               void* hip_stream) {
+  REQUIRE(dtype == ATTN_SINK_BF16, ATTN_SINK_ERR_UNSUPPORTED,
+          "paged decode supports bf16 only (dtype %d)", dtype);
+  if (int r = check_decode_common(B, Hq, Hkv, D, page_size, max_pages_per_seq, window_first,
+                                  window_last, num_splits))
+    return r;
+  if (int r = check_scale(softmax_scale)) return r;
+  REQUIRE(num_pages >= 1, ATTN_SINK_ERR_INVALID_ARG, "num_pages must be >= 1");
+  REQUIRE(fits_int32((long long)num_pages * page_size), ATTN_SINK_ERR_UNSUPPORTED,
+          "num_pages * page_size exceeds 2^31 - 1");
+  REQUIRE(q && k_cache && v_cache && block_table && seqlens_k && o, ATTN_SINK_ERR_INVALID_ARG,
+          "q, k_cache, v_cache, block_table, seqlens_k and o must not be NULL");
+  REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(o),
+          ATTN_SINK_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
+  REQUIRE(aligned4(block_table) && aligned4(seqlens_k) && aligned4(sink) && aligned4(lse),
+          ATTN_SINK_ERR_INVALID_ARG, "block_table, seqlens_k, sink and lse must be 4-byte aligned");
+  const DecodePlan plan = plan_decode(B, Hq, Hkv, D, page_size, max_pages_per_seq, window_first,
+                                      window_last, num_splits);
+  REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
+          "a 16-byte aligned workspace of %zu bytes is required", plan.workspace_bytes);
+  REQUIRE(workspace_bytes >= plan.workspace_bytes, ATTN_SINK_ERR_WORKSPACE,
+          "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+          plan.workspace_bytes);
+  DecodeArgs a{q, k_cache, v_cache, block_table, seqlens_k, sink, o, lse, B, Hq, Hkv, D,
+               page_size, max_pages_per_seq, num_pages, softmax_scale, window_first, window_last,
+               plan.chunk, plan.max_splits, static_cast<float*>(workspace)};
+  return hip_status(launch_decode_bf16(a, static_cast<hipStream_t>(hip_stream)),
+                    "attn_sink_fwd_decode_paged launch");
+}
+
+size_t attn_sink_bwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D) {
+  if (B < 1 || Sq < 1 || Sk < 0 || check_heads(Hq, Hkv, D) != ATTN_SINK_OK) return 0;
+  return backward_workspace_bytes(B, Sq, Sk, Hq, Hkv, D);
+}
+
+int attn_sink_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, const float* sink, void* dq, void* dk, void* dv, float* dsink,
+                  int B, int Sq, int Sk, int Hq, int Hkv, int D, float softmax_scale, int causal,
+                  int window_first, int window_last, void* workspace, size_t workspace_bytes,
+                  int dtype, void* hip_stream) {
+  REQUIRE(dtype == ATTN_SINK_BF16, ATTN_SINK_ERR_UNSUPPORTED,
+          "the backward supports bf16 only (dtype %d)", dtype);
+  REQUIRE(B >= 1 && Sq >= 1 && Sk >= 1, ATTN_SINK_ERR_INVALID_ARG,
+          "need B, Sq, Sk >= 1 (got %d, %d, %d)", B, Sq, Sk);
+  if (int r = check_heads(Hq, Hkv, D)) return r;
+  if (int r = check_scale(softmax_scale)) return r;
+  if (int r = check_window(window_first, window_last)) return r;
+  REQUIRE(causal == 0 || causal == 1, ATTN_SINK_ERR_INVALID_ARG, "causal must be 0 or 1");
+  REQUIRE(window_last < 0 || causal, ATTN_SINK_ERR_UNSUPPORTED,
+          "the first/last window needs causal = 1");
+  REQUIRE(q && k && v && o && dout && lse && dq && dk && dv, ATTN_SINK_ERR_INVALID_ARG,
+          "q, k, v, o, dout, lse, dq, dk and dv must not be NULL");
+  REQUIRE(!sink || dsink, ATTN_SINK_ERR_INVALID_ARG, "dsink is required when sink is given");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) && aligned16(dout) &&
+              aligned16(dq) && aligned16(dk) && aligned16(dv),
+          ATTN_SINK_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  REQUIRE(aligned4(lse) && aligned4(sink) && aligned4(dsink), ATTN_SINK_ERR_INVALID_ARG,
+          "lse, sink and dsink must be 4-byte aligned");
+  REQUIRE(fits_int32((long long)B * Sq * Hq) && fits_int32((long long)B * Sk * Hkv),
+          ATTN_SINK_ERR_UNSUPPORTED, "too many rows for 32-bit row indices");
+  const size_t need = backward_workspace_bytes(B, Sq, Sk, Hq, Hkv, D);
+  REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
+          "a 16-byte aligned workspace of %zu bytes is required", need);
+  REQUIRE(workspace_bytes >= need, ATTN_SINK_ERR_WORKSPACE,
+          "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  BackwardArgs a{q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, B, Sq, Sk, Hq, Hkv, D,
+                 softmax_scale, causal, window_first, window_last, workspace};
+  return hip_status(launch_backward_bf16(a, static_cast<hipStream_t>(hip_stream)),
+                    "attn_sink_bwd launch");
+}
+
+int attn_sink_decode_select_slots(const int32_t* block_table, const int32_t* seqlens_k, int B,
+                                  int max_pages_per_seq, int page_size, int window_first,
+                                  int window_last, int64_t* slots, int32_t* counts, int max_sel,
+                                  void* hip_stream) {
+  REQUIRE(B >= 1 && max_pages_per_seq >= 1 && max_sel >= 1, ATTN_SINK_ERR_INVALID_ARG,
+          "need B, max_pages_per_seq, max_sel >= 1");
+  REQUIRE(pow2(page_size) && page_size <= 256, ATTN_SINK_ERR_UNSUPPORTED,
+          "page_size must be a power of two in [1, 256] (got %d)", page_size);
+  if (int r = check_window(window_first, window_last)) return r;
+  REQUIRE(block_table && seqlens_k && slots && counts, ATTN_SINK_ERR_INVALID_ARG,
+          "block_table, seqlens_k, slots and counts must not be NULL");
+  REQUIRE(aligned4(block_table) && aligned4(seqlens_k) && aligned4(counts) &&
+              (reinterpret_cast<uintptr_t>(slots) & 7u) == 0,
+          ATTN_SINK_ERR_INVALID_ARG, "misaligned pointer");
+  return hip_status(launch_select_slots(block_table, seqlens_k, B, max_pages_per_seq, page_size,
+                                        window_first, window_last, slots, counts, max_sel,
+                                        static_cast<hipStream_t>(hip_stream)),
+                    "attn_sink_decode_select_slots launch");
+}
+
+int attn_sink_gather_kv(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                        const int32_t* seqlens_k, int B, int Hkv, int D, int page_size,
+                        int max_pages_per_seq, int window_first, int window_last, void* k_out,
+                        void* v_out, int max_sel, int dtype, void* hip_stream) {
+  REQUIRE(dtype == ATTN_SINK_BF16 || dtype == ATTN_SINK_F32, ATTN_SINK_ERR_UNSUPPORTED,
+          "unknown dtype %d", dtype);
+  REQUIRE(B >= 1 && Hkv >= 1 && D >= 1 && max_pages_per_seq >= 1 && max_sel >= 1,
+          ATTN_SINK_ERR_INVALID_ARG, "sizes must be >= 1");
+  REQUIRE(pow2(page_size) && page_size <= 256, ATTN_SINK_ERR_UNSUPPORTED,
+          "page_size must be a power of two in [1, 256] (got %d)", page_size);
+  if (int r = check_window(window_first, window_last)) return r;
+  REQUIRE(k_cache && v_cache && block_table && seqlens_k && k_out && v_out,
+          ATTN_SINK_ERR_INVALID_ARG, "pointers must not be NULL");
+  REQUIRE(aligned4(block_table) && aligned4(seqlens_k) && aligned4(k_cache) && aligned4(v_cache) &&
+              aligned4(k_out) && aligned4(v_out),
+          ATTN_SINK_ERR_INVALID_ARG, "misaligned pointer");
+  return hip_status(launch_gather_kv(k_cache, v_cache, block_table, seqlens_k, B, Hkv, D,
+                                     page_size, max_pages_per_seq, window_first, window_last,
+                                     k_out, v_out, max_sel, dtype == ATTN_SINK_BF16 ? 2 : 4,
+                                     static_cast<hipStream_t>(hip_stream)),
+                    "attn_sink_gather_kv launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,581 @@
+// Backward of attention with a learnable per-head sink (bf16, fp32 accumulate).
+//
+// With P_ij = exp(s_ij - LSE_i) (LSE from the forward, sink included) and
+// Di = <dO_i, O_i>:
+//   dV_j = sum_i P_ij dO_i,  dS_ij = P_ij (<dO_i, v_j> - Di),
+//   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
+//   dSink_h = -sum_{b,i} exp(sink_h - LSE_i) Di
+// (flash-attention PR #1819 "feat: Implement Sink Attention", Description:
+// the backward returns the sink's gradient).  Because the sink has no value
+// row and LSE already contains it, the sink needs no term in the main
+// kernels: its gradient is a by-product of the Di pass.
+//
+// Kernels (all deterministic, no atomics):
+//   bwd_preprocess   Di and per-(b, h, 64-row block) dSink partials
+//   bwd_dkdv         KV-stationary: a wave owns 32 keys and accumulates dK/dV
+//                    over all query heads of its GQA group and all query tiles
+//                    that can see them
+//   bwd_dq           Q-stationary (the forward's frame): recomputes S and dP
+//                    and accumulates dQ in registers
+//   bwd_dsink_reduce fixed-order sum of the dSink partials
+#include "common.h"
+#include "launch.h"
+
+namespace attn_sink {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;  // rows per query tile / keys per KV tile
+constexpr int kPad = 8;    // LDS row padding (elements, 16 B)
+
+__device__ __forceinline__ int perm_row(int j) { return ((j & 15) >> 2) * 8 + (j >> 4) * 4 + (j & 3); }
+__device__ __forceinline__ int lds_row(int j) { return (j & ~31) + perm_row(j & 31); }
+
+__device__ __forceinline__ uint32_t pick16(const uint4& x, int e) {
+  const uint32_t w = e < 2 ? x.x : (e < 4 ? x.y : (e < 6 ? x.z : x.w));
+  return (w >> (16 * (e & 1))) & 0xffffu;
+}
+
+// 64 rows x D tile of a [.., rows, heads, D] tensor: each thread loads one
+// (row pair, 16-byte chunk) item per 256 items and writes it both in natural
+// layout (rows permuted within 32-blocks, see lds_row) and transposed.
+template <int D>
+struct PairTile {
+  static constexpr int CH = D / 8;
+  static constexpr int N = (kTile / 2) * CH / kThreads;
+  uint4 r[N][2];
+  __device__ __forceinline__ void load(const __bf16* base, size_t rs, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + i * kThreads;
+      const int pr = idx % (kTile / 2), c = idx / (kTile / 2);
+      const int j = row0 + 2 * pr;
+      r[i][0] = j < nrows ? *reinterpret_cast<const uint4*>(base + (size_t)j * rs + 8 * c)
+                          : make_uint4(0, 0, 0, 0);
+      r[i][1] = j + 1 < nrows ? *reinterpret_cast<const uint4*>(base + (size_t)(j + 1) * rs + 8 * c)
+                              : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* nat, __bf16* tr, int tid) const {
+    constexpr int NS = D + kPad, TS = kTile + kPad;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + i * kThreads;
+      const int pr = idx % (kTile / 2), c = idx / (kTile / 2);
+      if (nat) {
+        *reinterpret_cast<uint4*>(nat + lds_row(2 * pr) * NS + 8 * c) = r[i][0];
+        *reinterpret_cast<uint4*>(nat + lds_row(2 * pr + 1) * NS + 8 * c) = r[i][1];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint32_t*>(tr + (8 * c + e) * TS + 2 * pr) =
+            pick16(r[i][0], e) | (pick16(r[i][1], e) << 16);
+    }
+  }
+};
+
+// 64 rows x D tile stored in natural layout only (rows permuted).
+template <int D>
+struct RowTile {
+  static constexpr int CH = D / 8;
+  static constexpr int N = kTile * CH / kThreads;
+  uint4 r[N];
+  __device__ __forceinline__ void load(const __bf16* base, size_t rs, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + i * kThreads;
+      const int j = row0 + idx / CH, c = idx % CH;
+      r[i] = j < nrows ? *reinterpret_cast<const uint4*>(base + (size_t)j * rs + 8 * c)
+                       : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* nat, int tid) const {
+    constexpr int NS = D + kPad;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = tid + i * kThreads;
+      *reinterpret_cast<uint4*>(nat + lds_row(idx / CH) * NS + 8 * (idx % CH)) = r[i];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Di = <dO_i, O_i> and dSink partials.  Grid (ceil(Sq/64), Hq, B); 4 threads
+// per row.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
+    const __bf16* __restrict__ o, const __bf16* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ sink, float* __restrict__ di, float* __restrict__ dsink_part, int Sq,
+    int Hq) {
+  constexpr int PER = D / 4;  // elements per thread
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int row = blockIdx.x * 64 + tid / 4;
+  const int part = tid % 4;
+  float acc = 0.f;
+  if (row < Sq) {
+    const size_t off = (((size_t)b * Sq + row) * Hq + h) * D + part * PER;
+#pragma unroll
+    for (int c = 0; c < PER / 8; ++c) {
+      const uint4 a = *reinterpret_cast<const uint4*>(o + off + 8 * c);
+      const uint4 g = *reinterpret_cast<const uint4*>(dout + off + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc = __builtin_fmaf(bf16_bits_to_f32(pick16(a, e)), bf16_bits_to_f32(pick16(g, e)), acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  float contrib = 0.f;
+  if (row < Sq && part == 0) {
+    di[((size_t)b * Hq + h) * Sq + row] = acc;
+    if (sink) {
+      const float L = lse[((size_t)b * Hq + h) * Sq + row];
+      contrib = -exp2_fast((sink[h] - L) * kLog2e) * acc;
+    }
+  }
+  if (!sink) return;
+  // fixed-order block sum: wave tree, then waves in order
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) contrib += __shfl_xor(contrib, x, 64);
+  __shared__ float ws[4];
+  if ((tid & 63) == 0) ws[tid >> 6] = contrib;
+  __syncthreads();
+  if (tid == 0)
+    dsink_part[((size_t)b * Hq + h) * gridDim.x + blockIdx.x] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+}
+
+__global__ void bwd_dsink_reduce_kernel(const float* __restrict__ part, float* __restrict__ dsink,
+                                        int B, int Hq, int nblk) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= Hq) return;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int k = 0; k < nblk; ++k) s += part[((size_t)b * Hq + h) * nblk + k];
+  dsink[h] = s;
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV.  Grid (ceil(Sk/128), Hkv, B).  Wave w owns keys k0 + 32w .. +31,
+// held as MFMA B operands (K^T, V^T) in registers.  Per (head, query tile):
+//   S  = Q K^T,  dP = dO V^T        (A = Q, dO from LDS, natural layout)
+//   P = 2^(S*sl2 - LSE*log2e), dS = P (dP - Di)
+//   dV^T += dO^T P,  dK^T += Q^T dS (A = dO^T, Q^T from LDS, transposed)
+// Lane (hh, l32) holds key l32 and query rows 32*qb + 16*hh + i.
+// ---------------------------------------------------------------------------
+template <int D>
+struct DkdvLds {
+  __bf16 q[2][kTile * (D + kPad)];
+  __bf16 dO[2][kTile * (D + kPad)];
+  __bf16 qt[2][D * (kTile + kPad)];
+  __bf16 dOt[2][D * (kTile + kPad)];
+  float lse2[2][kTile];
+  float di[2][kTile];
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Sq, int Sk, int Hq, int Hkv, float scale,
+    float sl2, int causal, int w1, int w2) {
+  __shared__ DkdvLds<D> s;
+  constexpr int NS = D + kPad, TS = kTile + kPad;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int g = Hq / Hkv;
+  const int k0 = blockIdx.x * 128;
+  const int k1 = min(Sk, k0 + 128);
+  const int key = k0 + 32 * wave + l32;
+  const int off = Sk - Sq;
+
+  // K^T / V^T B operands: column key, k = d = 16*ks + 8*hh ..
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    if (key < Sk) {
+      const size_t base = (((size_t)b * Sk + key) * Hkv + kvh) * D + 16 * ks + 8 * hh;
+      kf[ks] = *reinterpret_cast<const bf16x8*>(k + base);
+      vf[ks] = *reinterpret_cast<const bf16x8*>(v + base);
+    } else {
+      kf[ks] = bf16x8{};
+      vf[ks] = bf16x8{};
+    }
+  }
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+
+  // query rows that can see keys [k0, k1)
+  int i_lo = 0, i_hi = Sq;
+  if (causal) i_lo = max(0, k0 - off);
+  if (w2 > 0 && k0 >= w1) i_hi = min(Sq, (k1 - 1) + w2 - 1 - off + 1);
+  const int t_lo = i_lo / kTile;
+  const int t_hi = i_hi > i_lo ? (i_hi + kTile - 1) / kTile : t_lo;
+  const int nq = t_hi - t_lo;
+  const int niter = nq * g;
+
+  const size_t rs = (size_t)Hq * D;
+  PairTile<D> tq, tdo;
+  float lse_r = 0.f, di_r = 0.f;
+  auto load_iter = [&](int it) {
+    const int h = kvh * g + it / nq;
+    const int i0 = (t_lo + it % nq) * kTile;
+    const size_t base = ((size_t)b * Sq * Hq + h) * D;
+    tq.load(q + base, rs, i0, Sq, tid);
+    tdo.load(dout + base, rs, i0, Sq, tid);
+    if (tid < kTile) {
+      const int i = i0 + tid;
+      const size_t x = ((size_t)b * Hq + h) * Sq + i;
+      lse_r = i < Sq ? lse[x] * kLog2e : 0.f;
+      di_r = i < Sq ? di[x] : 0.f;
+    }
+  };
+  auto store_iter = [&](int buf) {
+    tq.store(s.q[buf], s.qt[buf], tid);
+    tdo.store(s.dO[buf], s.dOt[buf], tid);
+    if (tid < kTile) {
+      s.lse2[buf][tid] = lse_r;
+      s.di[buf][tid] = di_r;
+    }
+  };
+
+  if (niter > 0) {
+    load_iter(0);
+    store_iter(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < niter; ++it) {
+    const int buf = it & 1;
+    const int i0 = (t_lo + it % nq) * kTile;
+    if (it + 1 < niter) load_iter(it + 1);
+
+    f32x16 sa[2], pa[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      sa[qb] = f32x16{};
+      pa[qb] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int r = (32 * qb + l32) * NS + 16 * ks + 8 * hh;
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&s.q[buf][r]);
+        const bf16x8 da = *reinterpret_cast<const bf16x8*>(&s.dO[buf][r]);
+        sa[qb] = mfma32(qa, kf[ks], sa[qb]);
+        pa[qb] = mfma32(da, vf[ks], pa[qb]);
+      }
+
+    const int p0 = off + i0;
+    const bool need_mask = (i0 + kTile > Sq) || (causal && p0 < k1 - 1) ||
+                           (w2 > 0 && k1 - 1 >= w1 && p0 + kTile - 1 - w2 >= k0);
+    bf16x8 pb[2][2], sb[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int rbase = 32 * qb + 16 * hh;
+      float lv[16], dv16[16];
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&s.lse2[buf][rbase + 4 * c4]);
+        const f32x4 d2 = *reinterpret_cast<const f32x4*>(&s.di[buf][rbase + 4 * c4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lv[4 * c4 + e] = a[e];
+          dv16[4 * c4 + e] = d2[e];
+        }
+      }
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = exp2_fast(__builtin_fmaf(sa[qb][i], sl2, -lv[i]));
+        if (need_mask) {
+          const int row = i0 + rbase + i;
+          const bool ok = row < Sq && key < Sk && key_visible(key, off + row, causal, w1, w2);
+          p = ok ? p : 0.f;
+        }
+        pv[i] = p;
+        dsv[i] = p * (pa[qb][i] - dv16[i]);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        pb[qb][c] = to_bf16x8(pv[8 * c], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3], pv[8 * c + 4],
+                              pv[8 * c + 5], pv[8 * c + 6], pv[8 * c + 7]);
+        sb[qb][c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
+                              dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
+      }
+    }
+
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = 32 * db + l32;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int qb = t >> 1, c = t & 1;
+        const int col = 32 * qb + 16 * hh + 8 * c;
+        const bf16x8 dot = *reinterpret_cast<const bf16x8*>(&s.dOt[buf][d * TS + col]);
+        const bf16x8 qt = *reinterpret_cast<const bf16x8*>(&s.qt[buf][d * TS + col]);
+        dva[db] = mfma32(dot, pb[qb][c], dva[db]);
+        dka[db] = mfma32(qt, sb[qb][c], dka[db]);
+      }
+    }
+
+    if (it + 1 < niter) store_iter(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (key < Sk) {
+    const size_t base = (((size_t)b * Sk + key) * Hkv + kvh) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d = 32 * db + 8 * a + 4 * hh;
+        *reinterpret_cast<bf16x4*>(dk + base + d) =
+            to_bf16x4(dka[db][4 * a] * scale, dka[db][4 * a + 1] * scale,
+                      dka[db][4 * a + 2] * scale, dka[db][4 * a + 3] * scale);
+        *reinterpret_cast<bf16x4*>(dv + base + d) =
+            to_bf16x4(dva[db][4 * a], dva[db][4 * a + 1], dva[db][4 * a + 2], dva[db][4 * a + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  Same frame and schedule as the forward: 4 waves = 4 query heads of one
+// GQA group (or 4 row blocks when the group size is not a multiple of 4), 32
+// query rows per wave.  Per KV tile:
+//   S^T = K Q^T, dP^T = V dO^T (A = K, V from LDS natural layout)
+//   dS^T = P^T (dP^T - Di),  dQ^T += K^T dS^T (A = K^T from LDS transposed)
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqLds {
+  __bf16 k[2][kTile * (D + kPad)];
+  __bf16 v[2][kTile * (D + kPad)];
+  __bf16 kt[2][D * (kTile + kPad)];
+};
+
+struct QRange {
+  int n1, b_start, n2;
+  __device__ __forceinline__ int count() const { return n1 + n2; }
+  __device__ __forceinline__ int tile(int it) const { return it < n1 ? it : b_start + (it - n1); }
+};
+
+__device__ __forceinline__ QRange kv_tiles(int Sk, int p_min, int p_max, int causal, int w1, int w2) {
+  QRange r{0, 0, 0};
+  const int kend = causal ? min(Sk, p_max + 1) : Sk;
+  if (kend <= 0) return r;
+  const int tend = (kend + kTile - 1) / kTile;
+  if (w2 <= 0) {
+    r.n1 = tend;
+    return r;
+  }
+  const int a_end = (min(w1, kend) + kTile - 1) / kTile;
+  const int b_beg = max(0, p_min - w2 + 1) / kTile;
+  if (b_beg <= a_end) {
+    r.n1 = tend;
+    return r;
+  }
+  r.n1 = a_end;
+  r.b_start = b_beg;
+  r.n2 = tend - b_beg;
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
+    __bf16* __restrict__ dq, int Sq, int Sk, int Hq, int Hkv, int hpw, float scale, float sl2,
+    int causal, int w1, int w2) {
+  __shared__ DqLds<D> s;
+  constexpr int NS = D + kPad, TS = kTile + kPad;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int g = Hq / Hkv;
+  const int groups = g / hpw;
+  const int kvh = blockIdx.y / groups;
+  const int h = kvh * g + (blockIdx.y % groups) * hpw + (wave % hpw);
+  const int rb = wave / hpw;
+  const int R = 32 * (4 / hpw);
+  const int b = blockIdx.z;
+  const int row0 = (gridDim.x - 1 - blockIdx.x) * R;
+  const int row = row0 + rb * 32 + l32;
+  const int off = Sk - Sq;
+  const int p = off + row;
+  const int p_min = off + row0;
+  const int p_max = off + min(Sq, row0 + R) - 1;
+
+  bf16x8 qf[D / 16], of[D / 16];
+  float lse2 = 0.f, di_r = 0.f;
+  if (row < Sq) {
+    const size_t base = (((size_t)b * Sq + row) * Hq + h) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(q + base + 16 * ks);
+      of[ks] = *reinterpret_cast<const bf16x8*>(dout + base + 16 * ks);
+    }
+    lse2 = lse[((size_t)b * Hq + h) * Sq + row] * kLog2e;
+    di_r = di[((size_t)b * Hq + h) * Sq + row];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = bf16x8{};
+      of[ks] = bf16x8{};
+    }
+  }
+  f32x16 dqa[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dqa[db] = f32x16{};
+
+  const QRange tr = kv_tiles(Sk, p_min, p_max, causal, w1, w2);
+  const int ntiles = tr.count();
+  const size_t rs = (size_t)Hkv * D;
+  const __bf16* kbase = k + ((size_t)b * Sk * Hkv + kvh) * D;
+  const __bf16* vbase = v + ((size_t)b * Sk * Hkv + kvh) * D;
+  PairTile<D> tk;
+  RowTile<D> tv;
+  if (ntiles > 0) {
+    tk.load(kbase, rs, tr.tile(0) * kTile, Sk, tid);
+    tv.load(vbase, rs, tr.tile(0) * kTile, Sk, tid);
+    tk.store(s.k[0], s.kt[0], tid);
+    tv.store(s.v[0], tid);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int key0 = tr.tile(it) * kTile;
+    if (it + 1 < ntiles) {
+      tk.load(kbase, rs, tr.tile(it + 1) * kTile, Sk, tid);
+      tv.load(vbase, rs, tr.tile(it + 1) * kTile, Sk, tid);
+    }
+    f32x16 st[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      st[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r = (32 * kb + l32) * NS + 16 * ks + 8 * hh;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&s.k[buf][r]);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&s.v[buf][r]);
+        st[kb] = mfma32(ka, qf[ks], st[kb]);
+        dp[kb] = mfma32(va, of[ks], dp[kb]);
+      }
+    const bool need_mask = (key0 + kTile > Sk) || (causal && key0 + kTile - 1 > p_min) ||
+                           (w2 > 0 && key0 + kTile - 1 >= w1 && key0 <= p_max - w2) ||
+                           (row0 + R > Sq);
+    bf16x8 sb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pr = exp2_fast(__builtin_fmaf(st[kb][i], sl2, -lse2));
+        if (need_mask) {
+          const int j = key0 + 32 * kb + 16 * hh + i;
+          const bool ok = row < Sq && j < Sk && key_visible(j, p, causal, w1, w2);
+          pr = ok ? pr : 0.f;
+        }
+        dsv[i] = pr * (dp[kb][i] - di_r);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        sb[kb][c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
+                              dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = 32 * db + l32;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kb = t >> 1, c = t & 1;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+            &s.kt[buf][d * TS + 32 * kb + 16 * hh + 8 * c]);
+        dqa[db] = mfma32(ka, sb[kb][c], dqa[db]);
+      }
+    }
+    if (it + 1 < ntiles) {
+      tk.store(s.k[buf ^ 1], s.kt[buf ^ 1], tid);
+      tv.store(s.v[buf ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  if (row < Sq) {
+    __bf16* dst = dq + (((size_t)b * Sq + row) * Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * a + 4 * hh) =
+            to_bf16x4(dqa[db][4 * a] * scale, dqa[db][4 * a + 1] * scale,
+                      dqa[db][4 * a + 2] * scale, dqa[db][4 * a + 3] * scale);
+  }
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D) {
+  (void)Sk;
+  (void)Hkv;
+  (void)D;
+  const size_t nblk = (size_t)(Sq + 63) / 64;
+  const size_t di = (size_t)B * Hq * Sq;
+  const size_t part = (size_t)B * Hq * nblk;
+  return (di + part) * sizeof(float);
+}
+
+hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
+  const int g = a.Hq / a.Hkv;
+  const int hpw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
+  const float sl2 = a.scale * kLog2e;
+  const int nblk = (a.Sq + 63) / 64;
+  float* di = static_cast<float*>(a.workspace);
+  float* part = di + (size_t)a.B * a.Hq * a.Sq;
+  const auto* q = static_cast<const __bf16*>(a.q);
+  const auto* k = static_cast<const __bf16*>(a.k);
+  const auto* v = static_cast<const __bf16*>(a.v);
+  const auto* o = static_cast<const __bf16*>(a.o);
+  const auto* dout = static_cast<const __bf16*>(a.dout);
+  auto* dq = static_cast<__bf16*>(a.dq);
+  auto* dk = static_cast<__bf16*>(a.dk);
+  auto* dv = static_cast<__bf16*>(a.dv);
+  const dim3 pgrid(nblk, a.Hq, a.B);
+  const dim3 kgrid((a.Sk + 127) / 128, a.Hkv, a.B);
+  const int R = 32 * (4 / hpw);
+  const dim3 qgrid((a.Sq + R - 1) / R, a.Hkv * (g / hpw), a.B);
+  if (a.D == 64) {
+    bwd_preprocess_kernel<64><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di, part,
+                                                              a.Sq, a.Hq);
+    bwd_dkdv_kernel<64><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dk, dv, a.Sq,
+                                                        a.Sk, a.Hq, a.Hkv, a.scale, sl2, a.causal,
+                                                        a.w1, a.w2);
+    bwd_dq_kernel<64><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, a.Sq, a.Sk,
+                                                      a.Hq, a.Hkv, hpw, a.scale, sl2, a.causal,
+                                                      a.w1, a.w2);
+  } else {
+    bwd_preprocess_kernel<128><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di, part,
+                                                               a.Sq, a.Hq);
+    bwd_dkdv_kernel<128><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dk, dv, a.Sq,
+                                                         a.Sk, a.Hq, a.Hkv, a.scale, sl2,
+                                                         a.causal, a.w1, a.w2);
+    bwd_dq_kernel<128><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, a.Sq, a.Sk,
+                                                       a.Hq, a.Hkv, hpw, a.scale, sl2, a.causal,
+                                                       a.w1, a.w2);
+  }
+  if (a.sink && a.dsink)
+    bwd_dsink_reduce_kernel<<<(a.Hq + 63) / 64, 64, 0, stream>>>(part, a.dsink, a.B, a.Hq, nblk);
+  return hipGetLastError();
+}
+
+}  // namespace attn_sink

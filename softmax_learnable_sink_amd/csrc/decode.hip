@@ -1,0 +1,396 @@
+// Paged decode with a learnable per-head sink and optional first/last window.
+//
+// Split-K: each sequence's selected tokens are cut into chunks of `chunk`
+// tokens; one workgroup handles one (chunk, KV head, sequence) and computes the
+// scores of all query heads of that KV head (GQA group, up to 16 per
+// workgroup), so every K/V byte is read from HBM once.  Inside a workgroup the
+// 4 waves take interleaved steps of 32 tokens:
+//   * the slots of the chunk's tokens are computed once into LDS from the
+//     block table and the window rule (sglang PR #12504 "To implement
+//     attention-sink": first W1 tokens followed by the last W2 tokens of each
+//     sequence, or the whole prefix when it is not longer than W1 + W2);
+//   * S^T (16 tokens x 16 heads) = K Q^T on 16x16x32 bf16 MFMA, K rows loaded
+//     straight from the paged cache;
+//   * a running max / sum per head WITHOUT the sink;
+//   * V is transposed through a wave-private LDS tile and O^T += V^T P^T.
+// The 4 waves merge through LDS and write one partial (acc[D], m, l) per
+// (sequence, head, chunk).  The combine kernel merges the chunks and folds the
+// sink into the denominator exactly once (sglang PR #8825, Summary of Changes:
+// the decode path receives the per-head sink; flash-attention PR #1819 review
+// thread: decoding with a sink through the KV-cache entry point was reported
+// wrong, so the merge is where the sink must enter, once).
+#include "common.h"
+#include "launch.h"
+
+namespace attn_sink {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSub = 1024;  // selected tokens whose slots are staged in LDS at once
+constexpr int kVTS = 40;    // V^T staging row stride: 32 tokens + 16 B padding
+
+template <int D>
+struct DecLds {
+  int slot[kSub];
+  union {
+    __bf16 vt[4][D * kVTS];
+    struct {
+      float m[4][16];
+      float l[4][16];
+      float o[4][16][D];
+    } red;
+  } u;
+};
+
+template <int D>
+struct KVRegs {
+  static constexpr int KS = D / 32;       // k-steps of the score MFMA
+  static constexpr int TPL = D / 16;      // V tokens per lane
+  static constexpr int NTG = 32 / TPL;    // lanes sharing one d-chunk
+  uint4 kr[2][KS];
+  uint4 vr[TPL];
+
+  __device__ __forceinline__ void load(const int* slot, int base, const __bf16* kbase,
+                                       const __bf16* vbase, size_t rs, int lane) {
+    const int kg = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      // MFMA row r of token group G holds token 8*(r/4) + 4*G + r%4 of the step
+      const int sl = slot[base + 8 * (r >> 2) + 4 * G + (r & 3)];
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        kr[G][s] = sl >= 0 ? *reinterpret_cast<const uint4*>(kbase + (size_t)sl * rs + 32 * s + 8 * kg)
+                           : make_uint4(0, 0, 0, 0);
+    }
+    const int tg = lane % NTG, c = lane / NTG;
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      const int sl = slot[base + TPL * tg + t];
+      vr[t] = sl >= 0 ? *reinterpret_cast<const uint4*>(vbase + (size_t)sl * rs + 8 * c)
+                      : make_uint4(0, 0, 0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ uint32_t half16(const uint4& x, int e) {
+  const uint32_t w = e < 2 ? x.x : (e < 4 ? x.y : (e < 6 ? x.z : x.w));
+  return (w >> (16 * (e & 1))) & 0xffffu;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ seqlens, float* __restrict__ part,
+    int Hq, int Hkv, int hgroups, int page_shift, int max_pages, float sl2, int w1, int w2,
+    int chunk, int max_splits) {
+  __shared__ DecLds<D> s;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int kg = lane >> 4, hl = lane & 15;
+  const int split = blockIdx.x, b = blockIdx.z;
+  const int kvh = blockIdx.y / hgroups, hgi = blockIdx.y % hgroups;
+  const int g = Hq / Hkv;
+  const int g_eff = min(16, g - 16 * hgi);
+  const int h0 = kvh * g + 16 * hgi;
+  const int L = seqlens[b];
+  const int nsel = n_selected(L, w1, w2);
+  const int u0 = split * chunk;
+  if (u0 >= nsel) return;  // uniform over the workgroup
+  const int u1 = min(nsel, u0 + chunk);
+  const int32_t* bt_row = bt + (size_t)b * max_pages;
+  const size_t rs = (size_t)Hkv * D;
+  const __bf16* kbase = kc + (size_t)kvh * D;
+  const __bf16* vbase = vc + (size_t)kvh * D;
+
+  // Q^T fragments (B operand): column = head hl, k = d = 32*s + 8*kg ..
+  bf16x8 qf[D / 32];
+#pragma unroll
+  for (int s2 = 0; s2 < D / 32; ++s2)
+    qf[s2] = hl < g_eff ? *reinterpret_cast<const bf16x8*>(q + ((size_t)b * Hq + h0 + hl) * D +
+                                                           32 * s2 + 8 * kg)
+                        : bf16x8{};
+
+  float m = kNegInf, l = 0.f;
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{};
+
+  constexpr int TPL = KVRegs<D>::TPL, NTG = KVRegs<D>::NTG;
+  __bf16* vt = s.u.vt[wave];
+
+  for (int sub0 = u0; sub0 < u1; sub0 += kSub) {
+    const int nsub = min(kSub, u1 - sub0);
+    for (int x = tid; x < kSub; x += kThreads)
+      s.slot[x] = x < nsub ? slot_of(bt_row, token_of(sub0 + x, L, w1, w2), page_shift) : -1;
+    __syncthreads();
+    const int nsteps = (nsub + 31) >> 5;
+    KVRegs<D> cur, nxt;
+    int st = wave;
+    if (st < nsteps) cur.load(s.slot, 32 * st, kbase, vbase, rs, lane);
+    for (; st < nsteps; st += 4) {
+      const int base = 32 * st;
+      if (st + 4 < nsteps) nxt.load(s.slot, base + 128, kbase, vbase, rs, lane);
+
+      // scores of tokens 8*kg + 4*G + j for head hl
+      f32x4 sc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int s2 = 0; s2 < D / 32; ++s2)
+          sc[G] = mfma16(__builtin_bit_cast(bf16x8, cur.kr[G][s2]), qf[s2], sc[G]);
+      float x[8];
+#pragma unroll
+      for (int G = 0; G < 2; ++G)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          x[4 * G + j] = (base + 8 * kg + 4 * G + j < nsub) ? sc[G][j] : kNegInf;
+      float mx = x[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      const float m_new = fmaxf(m, mx * sl2);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = exp2_fast(m - m_use);
+      m = m_new;
+      float p[8], rsum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = exp2_fast(__builtin_fmaf(x[e], sl2, -m_use));
+        rsum += p[e];
+      }
+      l = l * alpha + rsum;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
+      const bf16x8 pf = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+
+      // V^T staging: row d = 8*c + e, tokens TPL*tg .. +TPL-1
+      {
+        const int tg = lane % NTG, c = lane / NTG;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          __bf16* dst = vt + (8 * c + e) * kVTS + TPL * tg;
+          if constexpr (TPL == 4) {
+            uint2 w;
+            w.x = half16(cur.vr[0], e) | (half16(cur.vr[1], e) << 16);
+            w.y = half16(cur.vr[2], e) | (half16(cur.vr[3], e) << 16);
+            *reinterpret_cast<uint2*>(dst) = w;
+          } else {
+            uint4 w;
+            w.x = half16(cur.vr[0], e) | (half16(cur.vr[1], e) << 16);
+            w.y = half16(cur.vr[2], e) | (half16(cur.vr[3], e) << 16);
+            w.z = half16(cur.vr[4], e) | (half16(cur.vr[5], e) << 16);
+            w.w = half16(cur.vr[6], e) | (half16(cur.vr[7], e) << 16);
+            *reinterpret_cast<uint4*>(dst) = w;
+          }
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + (16 * db + hl) * kVTS + 8 * kg);
+        acc[db] = mfma16(vf, pf, acc[db]);
+      }
+      wave_lds_sync();
+      cur = nxt;
+    }
+    __syncthreads();
+  }
+
+  // ---- merge the 4 waves (each holds head hl, d = 16*db + 4*kg + j)
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (kg == 0) {
+    s.u.red.m[wave][hl] = m;
+    s.u.red.l[wave][hl] = l;
+  }
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s.u.red.o[wave][hl][16 * db + 4 * kg + j] = acc[db][j];
+  __syncthreads();
+  for (int x2 = tid; x2 < 16 * D; x2 += kThreads) {
+    const int hh = x2 / D, d = x2 % D;
+    if (hh >= g_eff) break;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s.u.red.m[w][hh]);
+    float od = 0.f, lw = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = exp2_fast(s.u.red.m[w][hh] - M);
+      od += f * s.u.red.o[w][hh][d];
+      lw += f * s.u.red.l[w][hh];
+    }
+    float* dst = part + (((size_t)b * Hq + h0 + hh) * max_splits + split) * (D + 2);
+    dst[d] = od;
+    if (d == 0) {
+      dst[D] = M;
+      dst[D + 1] = lw;
+    }
+  }
+}
+
+// One wave per (sequence, query head): merge the chunk partials and fold the
+// sink in once: M = max(sink', m_k), Z = 2^(sink'-M) + sum 2^(m_k-M) l_k,
+// O = sum 2^(m_k-M) acc_k / Z, LSE = (M + log2 Z) ln 2.
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ seqlens,
+    const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq,
+    int w1, int w2, int chunk, int max_splits) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + wave;
+  if (bh >= B * Hq) return;
+  const int b = bh / Hq, h = bh % Hq;
+  const int nsel = n_selected(seqlens[b], w1, w2);
+  const int nsp = nsel > 0 ? (nsel + chunk - 1) / chunk : 0;
+  const float* base = part + (size_t)bh * max_splits * (D + 2);
+  const float sig2 = sink ? sink[h] * kLog2e : kNegInf;
+
+  float M = sig2;
+  for (int k = lane; k < nsp; k += 64) M = fmaxf(M, base[(size_t)k * (D + 2) + D]);
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) M = wave_max_xor(M, x);
+
+  constexpr int DPL = D / 64;
+  float od[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) od[i] = 0.f;
+  float z = 0.f;
+  for (int k = 0; k < nsp; ++k) {
+    const float* pk = base + (size_t)k * (D + 2);
+    const float f = exp2_fast(pk[D] - M);
+    z += f * pk[D + 1];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) od[i] += f * pk[lane + 64 * i];
+  }
+  if (sig2 != kNegInf) z += exp2_fast(sig2 - M);
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) o[(size_t)bh * D + lane + 64 * i] = (__bf16)(od[i] * inv);
+  if (lse && lane == 0) lse[bh] = z > 0.f ? (M + log2_fast(z)) * kLn2 : kNegInf;
+}
+
+__global__ void select_slots_kernel(const int32_t* __restrict__ bt,
+                                    const int32_t* __restrict__ seqlens, int max_pages,
+                                    int page_shift, int w1, int w2, int64_t* __restrict__ slots,
+                                    int32_t* __restrict__ counts, int max_sel) {
+  const int b = blockIdx.x;
+  const int L = seqlens[b];
+  const int nsel = n_selected(L, w1, w2);
+  const int32_t* bt_row = bt + (size_t)b * max_pages;
+  for (int u = threadIdx.x; u < max_sel; u += blockDim.x)
+    slots[(size_t)b * max_sel + u] =
+        u < nsel ? (int64_t)slot_of(bt_row, token_of(u, L, w1, w2), page_shift) : -1;
+  if (threadIdx.x == 0) counts[b] = nsel;
+}
+
+// One workgroup per (selected index, sequence); copies Hkv*D elements.
+__global__ void gather_kv_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                                 const int32_t* __restrict__ bt,
+                                 const int32_t* __restrict__ seqlens, int row_elems,
+                                 int max_pages, int page_shift, int w1, int w2,
+                                 uint16_t* __restrict__ ko, uint16_t* __restrict__ vo,
+                                 int max_sel, int elem_halves) {
+  const int u = blockIdx.x, b = blockIdx.y;
+  const int L = seqlens[b];
+  const int nsel = n_selected(L, w1, w2);
+  const size_t n = (size_t)row_elems * elem_halves;  // row length in 16-bit words
+  uint16_t* kd = ko + ((size_t)b * max_sel + u) * n;
+  uint16_t* vd = vo + ((size_t)b * max_sel + u) * n;
+  if (u >= nsel) {
+    for (size_t x = threadIdx.x; x < n; x += blockDim.x) kd[x] = vd[x] = 0;
+    return;
+  }
+  const size_t slot = (size_t)slot_of(bt + (size_t)b * max_pages, token_of(u, L, w1, w2), page_shift);
+  for (size_t x = threadIdx.x; x < n; x += blockDim.x) {
+    kd[x] = kc[slot * n + x];
+    vd[x] = vc[slot * n + x];
+  }
+}
+
+int log2_exact(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pages, int w1, int w2,
+                       int num_splits) {
+  DecodePlan p{0, 0, 0};
+  const long long maxL = (long long)max_pages * page_size;
+  const long long max_sel = (w2 > 0) ? std::min<long long>(maxL, (long long)w1 + w2) : maxL;
+  const int g = Hq / Hkv;
+  const long long units = (long long)B * Hkv * ((g + 15) / 16);
+  long long chunk;
+  if (num_splits > 0) {
+    chunk = (max_sel + num_splits - 1) / num_splits;
+    chunk = (chunk + 31) / 32 * 32;
+  } else {
+    chunk = 1024;
+    while (chunk > 128 && units * ((max_sel + chunk - 1) / chunk) < 2048) chunk /= 2;
+  }
+  if (chunk < 32) chunk = 32;
+  p.chunk = (int)chunk;
+  p.max_splits = (int)((max_sel + chunk - 1) / chunk);
+  if (p.max_splits < 1) p.max_splits = 1;
+  p.workspace_bytes = (size_t)B * Hq * p.max_splits * (D + 2) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
+  const int g = a.Hq / a.Hkv;
+  const int hgroups = (g + 15) / 16;
+  const int page_shift = log2_exact(a.page_size);
+  const float sl2 = a.scale * kLog2e;
+  const auto* q = static_cast<const __bf16*>(a.q);
+  const auto* kc = static_cast<const __bf16*>(a.k_cache);
+  const auto* vc = static_cast<const __bf16*>(a.v_cache);
+  auto* o = static_cast<__bf16*>(a.o);
+  const dim3 grid(a.max_splits, a.Hkv * hgroups, a.B);
+  const dim3 cgrid((a.B * a.Hq + 3) / 4);
+  if (a.D == 64) {
+    decode_partial_kernel<64><<<grid, kThreads, 0, stream>>>(
+        q, kc, vc, a.block_table, a.seqlens, a.partials, a.Hq, a.Hkv, hgroups, page_shift,
+        a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits);
+    decode_combine_kernel<64><<<cgrid, kThreads, 0, stream>>>(
+        a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits);
+  } else {
+    decode_partial_kernel<128><<<grid, kThreads, 0, stream>>>(
+        q, kc, vc, a.block_table, a.seqlens, a.partials, a.Hq, a.Hkv, hgroups, page_shift,
+        a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits);
+    decode_combine_kernel<128><<<cgrid, kThreads, 0, stream>>>(
+        a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_slots(const int32_t* bt, const int32_t* seqlens, int B, int max_pages,
+                               int page_size, int w1, int w2, int64_t* slots, int32_t* counts,
+                               int max_sel, hipStream_t stream) {
+  select_slots_kernel<<<B, 256, 0, stream>>>(bt, seqlens, max_pages, log2_exact(page_size), w1, w2,
+                                             slots, counts, max_sel);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_kv(const void* kc, const void* vc, const int32_t* bt,
+                            const int32_t* seqlens, int B, int Hkv, int D, int page_size,
+                            int max_pages, int w1, int w2, void* k_out, void* v_out, int max_sel,
+                            int elem_bytes, hipStream_t stream) {
+  const dim3 grid(max_sel, B);
+  gather_kv_kernel<<<grid, 256, 0, stream>>>(
+      static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc), bt, seqlens, Hkv * D,
+      max_pages, log2_exact(page_size), w1, w2, static_cast<uint16_t*>(k_out),
+      static_cast<uint16_t*>(v_out), max_sel, elem_bytes / 2);
+  return hipGetLastError();
+}
+
+}  // namespace attn_sink

@@ -1,0 +1,83 @@
+// Host-side launchers of the sink-attention kernels.  Arguments are already
+// validated by the C-ABI layer (api.hip); these only pick a kernel and a grid
+// and enqueue it on `stream`.  They return the launch's hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn_sink {
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* sink;
+  void* o;
+  float* lse;
+  int B, Sq, Sk, Hq, Hkv, D;
+  float scale;
+  int causal, w1, w2;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const float* sink;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, D, page_size, max_pages, num_pages;
+  float scale;
+  int w1, w2;
+  int chunk;       // selected tokens per split
+  int max_splits;  // grid extent over splits
+  float* partials; // [B, Hq, max_splits, D + 2] fp32
+};
+
+// Split plan shared by the workspace query and the launch.
+struct DecodePlan {
+  int chunk;
+  int max_splits;
+  size_t workspace_bytes;
+};
+DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pages, int w1,
+                       int w2, int num_splits);
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_select_slots(const int32_t* bt, const int32_t* seqlens, int B, int max_pages,
+                               int page_size, int w1, int w2, int64_t* slots, int32_t* counts,
+                               int max_sel, hipStream_t stream);
+hipError_t launch_gather_kv(const void* kc, const void* vc, const int32_t* bt,
+                            const int32_t* seqlens, int B, int Hkv, int D, int page_size,
+                            int max_pages, int w1, int w2, void* k_out, void* v_out, int max_sel,
+                            int elem_bytes, hipStream_t stream);
+
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  const float* sink;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsink;
+  int B, Sq, Sk, Hq, Hkv, D;
+  float scale;
+  int causal, w1, w2;
+  void* workspace;
+};
+size_t backward_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D);
+hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream);
+
+}  // namespace attn_sink

@@ -1,0 +1,429 @@
+// Forward prefill of attention with a learnable per-head sink logit.
+//
+// bf16 path (gfx950 MFMA): one workgroup = 4 waves sharing one KV head.  When
+// the GQA group size is a multiple of 4 the 4 waves are 4 query heads of the
+// same group over the same query rows, so every K/V tile staged in LDS feeds 4
+// heads and all waves have the same causal extent.  Each wave owns 32*QB query
+// rows and works in the transposed frame
+//     S^T = K Q^T   (A = K tile from LDS, B = Q^T from registers)
+//     O^T += V^T P^T (A = V^T tile from LDS, B = P^T from registers)
+// so every lane owns one query row: the running max / sum are per-lane scalars
+// and the softmax needs a single cross-lane exchange (lane l <-> l^32).
+// The sink seeds the running max (m = sink * log2 e) and is added to the
+// denominator once, at the end (flash-attention PR #1819 "feat: Implement
+// Sink Attention", Description: one extra logit per head before the softmax;
+// sglang PR #8825, Summary of Changes: an additional value per head in the
+// softmax denominator).
+//
+// fp32 path: a plain VALU kernel, one thread per query row, K/V tiles in LDS.
+#include "common.h"
+#include "launch.h"
+
+namespace attn_sink {
+namespace {
+
+constexpr int kBN = 64;        // keys per KV tile
+constexpr int kThreads = 256;  // 4 waves of 64
+
+// LDS row (within a 32-key block) that holds key j of the block.  The MFMA
+// reading row r then sees key 16*((r>>2)&1) + 4*(r>>3) + (r&3), which puts
+// keys 16h .. 16h+15 of the block, in order, into accumulator half h.
+__device__ __forceinline__ int k_lds_row(int j) { return ((j & 15) >> 2) * 8 + (j >> 4) * 4 + (j & 3); }
+
+// V is stored transposed, [d][key], rows padded by 16 bytes: the transposed
+// writes of one wave cover 32 consecutive key pairs of one row, and the
+// 16-byte reads of 8 consecutive rows start 4 banks apart.
+__device__ __forceinline__ int vt_col(int pair) { return 2 * pair; }
+
+template <int D>
+struct Lds {
+  static constexpr int KS = D + 8;  // K row stride (elements), 16 B of padding
+  static constexpr int VS = kBN + 8; // V^T row stride (elements), 16 B of padding
+  __bf16 k[2][kBN * KS];
+  __bf16 vt[2][D * VS];
+};
+
+template <int D>
+struct TileRegs {
+  static constexpr int CH = D / 8;                        // 16-byte chunks per row
+  static constexpr int KN = kBN * CH / kThreads;          // K chunks per thread
+  static constexpr int VN = (kBN / 2) * CH / kThreads;    // (key pair, chunk) per thread
+  uint4 kr[KN];
+  uint4 vr[VN][2];
+
+  __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, size_t rs,
+                                       int key0, int Sk, int tid) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int idx = tid + i * kThreads;
+      const int j = key0 + idx / CH;
+      const int c = idx % CH;
+      kr[i] = j < Sk ? *reinterpret_cast<const uint4*>(kbase + (size_t)j * rs + c * 8)
+                     : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VN; ++i) {
+      // consecutive lanes take consecutive key pairs of one chunk
+      const int idx = tid + i * kThreads;
+      const int pr = idx % (kBN / 2);
+      const int c = idx / (kBN / 2);
+      const int j = key0 + 2 * pr;
+      vr[i][0] = j < Sk ? *reinterpret_cast<const uint4*>(vbase + (size_t)j * rs + c * 8)
+                        : make_uint4(0, 0, 0, 0);
+      vr[i][1] = j + 1 < Sk ? *reinterpret_cast<const uint4*>(vbase + (size_t)(j + 1) * rs + c * 8)
+                            : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void store(Lds<D>& s, int buf, int tid) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int idx = tid + i * kThreads;
+      const int key = idx / CH;
+      const int c = idx % CH;
+      const int row = (key & ~31) + k_lds_row(key & 31);
+      *reinterpret_cast<uint4*>(&s.k[buf][row * Lds<D>::KS + c * 8]) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VN; ++i) {
+      const int idx = tid + i * kThreads;
+      const int pr = idx % (kBN / 2);
+      const int c = idx / (kBN / 2);
+      const uint32_t a[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
+      const uint32_t b[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        const int d = c * 8 + e;
+        *reinterpret_cast<uint32_t*>(&s.vt[buf][d * Lds<D>::VS + vt_col(pr)]) = lo | (hi << 16);
+      }
+    }
+  }
+};
+
+// Tile schedule of one workgroup: tiles [0, n1) then [b_start, b_start + n2).
+struct TileRange {
+  int n1, b_start, n2;
+  __device__ __forceinline__ int count() const { return n1 + n2; }
+  __device__ __forceinline__ int tile(int it) const { return it < n1 ? it : b_start + (it - n1); }
+};
+
+__device__ __forceinline__ TileRange tile_range(int Sk, int p_min, int p_max, int causal, int w1,
+                                                int w2) {
+  TileRange r{0, 0, 0};
+  const int kend = causal ? min(Sk, p_max + 1) : Sk;
+  if (kend <= 0) return r;
+  const int tend = (kend + kBN - 1) / kBN;
+  if (w2 <= 0) {
+    r.n1 = tend;
+    return r;
+  }
+  // first window: keys [0, w1); last window: keys (p - w2, p] for p in [p_min, p_max]
+  const int a_end = (min(w1, kend) + kBN - 1) / kBN;
+  const int b_beg = max(0, p_min - w2 + 1) / kBN;
+  if (b_beg <= a_end) {
+    r.n1 = tend;
+    return r;
+  }
+  r.n1 = a_end;
+  r.b_start = b_beg;
+  r.n2 = tend - b_beg;
+  return r;
+}
+
+template <int D, int QB>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int Sq,
+    int Sk, int Hq, int Hkv, int hpw, float sl2, int causal, int w1, int w2) {
+  __shared__ Lds<D> s;
+  constexpr int RW = 32 * QB;  // query rows per wave
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int g = Hq / Hkv;
+  const int groups = g / hpw;  // workgroups per KV head along y
+  const int kvh = blockIdx.y / groups;
+  const int h = kvh * g + (blockIdx.y % groups) * hpw + (wave % hpw);
+  const int rb = wave / hpw;   // row block of this wave inside the workgroup
+  const int R = RW * (4 / hpw);
+  const int tile_idx = gridDim.x - 1 - blockIdx.x;  // heaviest causal tiles first
+  const int b = blockIdx.z;
+  const int row0 = tile_idx * R;
+  const int wrow0 = row0 + rb * RW;
+  const int off = Sk - Sq;  // bottom-right alignment
+  const int p_min = off + row0;
+  const int p_max = off + min(Sq, row0 + R) - 1;
+
+  // Q^T fragments (B operand): query row wrow0 + 32*qb + l32, d = 16*ks + 8*hh ..
+  bf16x8 qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wrow0 + 32 * qb + l32;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      if (row < Sq) {
+        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(
+            q + (((size_t)b * Sq + row) * Hq + h) * D + 16 * ks + 8 * hh);
+      } else {
+        qf[qb][ks] = bf16x8{};
+      }
+    }
+  }
+
+  const float sig2 = sink ? sink[h] * kLog2e : kNegInf;
+  float m[QB], l[QB];
+  f32x16 acc[D / 32][QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = sig2;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db][qb] = f32x16{};
+  }
+
+  const size_t rs = (size_t)Hkv * D;
+  const __bf16* kbase = k + ((size_t)b * Sk * Hkv + kvh) * D;
+  const __bf16* vbase = v + ((size_t)b * Sk * Hkv + kvh) * D;
+  const TileRange tr = tile_range(Sk, p_min, p_max, causal, w1, w2);
+  const int ntiles = tr.count();
+
+  TileRegs<D> regs;
+  if (ntiles > 0) {
+    regs.load(kbase, vbase, rs, tr.tile(0) * kBN, Sk, tid);
+    regs.store(s, 0, tid);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int key0 = tr.tile(it) * kBN;
+    if (it + 1 < ntiles) regs.load(kbase, vbase, rs, tr.tile(it + 1) * kBN, Sk, tid);
+
+    // ---- S^T = K Q^T : 2 key blocks x QB query blocks of 32x32
+    f32x16 st[2][QB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) st[kb][qb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            &s.k[buf][(32 * kb + l32) * Lds<D>::KS + 16 * ks + 8 * hh]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) st[kb][qb] = mfma32(kf, qf[qb][ks], st[kb][qb]);
+      }
+    }
+
+    // ---- mask (only on tiles that straddle a boundary)
+    const bool need_mask = (key0 + kBN > Sk) || (causal && key0 + kBN - 1 > p_min) ||
+                           (w2 > 0 && key0 + kBN - 1 >= w1 && key0 <= p_max - w2);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int p = off + wrow0 + 32 * qb + l32;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = key0 + 32 * kb + 16 * hh + i;
+            if (!(j < Sk && key_visible(j, p, causal, w1, w2))) st[kb][qb][i] = kNegInf;
+          }
+      }
+    }
+
+    // ---- online softmax (base 2), P in bf16
+    bf16x8 pf[2][QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb][qb][i]);
+      mx = wave_max_xor(mx, 32);
+      const float m_new = fmaxf(m[qb], mx * sl2);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = exp2_fast(m[qb] - m_use);
+      m[qb] = m_new;
+      float rsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = exp2_fast(__builtin_fmaf(st[kb][qb][i], sl2, -m_use));
+          st[kb][qb][i] = p;
+          rsum += p;
+        }
+      l[qb] = l[qb] * alpha + rsum;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db][qb] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const f32x16& x = st[kb][qb];
+          pf[kb][qb][c] = to_bf16x8(x[8 * c + 0], x[8 * c + 1], x[8 * c + 2], x[8 * c + 3],
+                                    x[8 * c + 4], x[8 * c + 5], x[8 * c + 6], x[8 * c + 7]);
+        }
+    }
+
+    // ---- O^T += V^T P^T : k-steps of 16 keys (key block kb, half c)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = 32 * db + l32;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kb = t >> 1, c = t & 1;
+        const int pair = 16 * kb + 8 * hh + 4 * c;
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+            &s.vt[buf][d * Lds<D>::VS + vt_col(pair)]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[db][qb] = mfma32(vf, pf[kb][qb][c], acc[db][qb]);
+      }
+    }
+
+    if (it + 1 < ntiles) regs.store(s, buf ^ 1, tid);
+    __syncthreads();
+  }
+
+  // ---- epilogue: fold the sink into the denominator once, normalise, store
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wrow0 + 32 * qb + l32;
+    float lt = l[qb] + __shfl_xor(l[qb], 32, 64);
+    if (sig2 != kNegInf) lt += exp2_fast(sig2 - m[qb]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (row < Sq) {
+      __bf16* orow = o + (((size_t)b * Sq + row) * Hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x16& x = acc[db][qb];
+          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * a + 4 * hh) =
+              to_bf16x4(x[4 * a] * inv, x[4 * a + 1] * inv, x[4 * a + 2] * inv, x[4 * a + 3] * inv);
+        }
+      if (lse && hh == 0)
+        lse[((size_t)b * Hq + h) * Sq + row] = lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 VALU path: one thread per query row, 32-key tiles of K and V in LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void prefill_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ sink, float* __restrict__ o, float* __restrict__ lse, int Sq, int Sk,
+    int Hq, int Hkv, float sl2, int causal, int w1, int w2) {
+  constexpr int TK = 32;
+  __shared__ float ks[TK][D];
+  __shared__ float vs[TK][D];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int kvh = h / (Hq / Hkv);
+  const int row = blockIdx.x * 64 + tid;
+  const int off = Sk - Sq;
+  const int p = off + row;
+  const int p_max = off + min(Sq, (int)blockIdx.x * 64 + 64) - 1;
+  const int kend = causal ? max(0, min(Sk, p_max + 1)) : Sk;
+
+  float qr[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qr[d] = row < Sq ? q[(((size_t)b * Sq + row) * Hq + h) * D + d] : 0.f;
+    acc[d] = 0.f;
+  }
+  const float sig2 = sink ? sink[h] * kLog2e : kNegInf;
+  float m = sig2, l = 0.f;
+
+  for (int key0 = 0; key0 < kend; key0 += TK) {
+    for (int x = tid; x < TK * D; x += 64) {
+      const int j = key0 + x / D, d = x % D;
+      const size_t src = (((size_t)b * Sk + j) * Hkv + kvh) * D + d;
+      ks[x / D][d] = j < Sk ? k[src] : 0.f;
+      vs[x / D][d] = j < Sk ? v[src] : 0.f;
+    }
+    __syncthreads();
+    for (int jj = 0; jj < TK; ++jj) {
+      const int j = key0 + jj;
+      if (j >= kend || !key_visible(j, p, causal, w1, w2)) continue;
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) dot = __builtin_fmaf(qr[d], ks[jj][d], dot);
+      const float sc = dot * sl2;
+      if (sc > m) {
+        const float alpha = exp2_fast(m - sc);
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc[d] *= alpha;
+        m = sc;
+      }
+      const float pj = exp2_fast(sc - m);
+      l += pj;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(pj, vs[jj][d], acc[d]);
+    }
+    __syncthreads();
+  }
+  if (row >= Sq) return;
+  if (sig2 != kNegInf) l += exp2_fast(sig2 - m);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float* orow = o + (((size_t)b * Sq + row) * Hq + h) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
+  if (lse) lse[((size_t)b * Hq + h) * Sq + row] = l > 0.f ? (m + log2f(l)) * kLn2 : kNegInf;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+  const int g = a.Hq / a.Hkv;
+  const int hpw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
+  const float sl2 = a.scale * kLog2e;
+  const dim3 block(kThreads);
+  const auto* q = static_cast<const __bf16*>(a.q);
+  const auto* k = static_cast<const __bf16*>(a.k);
+  const auto* v = static_cast<const __bf16*>(a.v);
+  auto* o = static_cast<__bf16*>(a.o);
+  if (a.D == 64) {
+    const int R = 64 * (4 / hpw);
+    const dim3 grid((a.Sq + R - 1) / R, a.Hkv * (g / hpw), a.B);
+    prefill_bf16_kernel<64, 2><<<grid, block, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.Sq, a.Sk,
+                                                           a.Hq, a.Hkv, hpw, sl2, a.causal, a.w1,
+                                                           a.w2);
+  } else {
+    const int R = 32 * (4 / hpw);
+    const dim3 grid((a.Sq + R - 1) / R, a.Hkv * (g / hpw), a.B);
+    prefill_bf16_kernel<128, 1><<<grid, block, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.Sq,
+                                                            a.Sk, a.Hq, a.Hkv, hpw, sl2, a.causal,
+                                                            a.w1, a.w2);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
+  const float sl2 = a.scale * kLog2e;
+  const dim3 grid((a.Sq + 63) / 64, a.Hq, a.B);
+  const auto* q = static_cast<const float*>(a.q);
+  const auto* k = static_cast<const float*>(a.k);
+  const auto* v = static_cast<const float*>(a.v);
+  auto* o = static_cast<float*>(a.o);
+  if (a.D == 64)
+    prefill_f32_kernel<64><<<grid, 64, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.Sq, a.Sk, a.Hq,
+                                                    a.Hkv, sl2, a.causal, a.w1, a.w2);
+  else
+    prefill_f32_kernel<128><<<grid, 64, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.Sq, a.Sk,
+                                                     a.Hq, a.Hkv, sl2, a.causal, a.w1, a.w2);
+  return hipGetLastError();
+}
+
+}  // namespace attn_sink

@@ -11,9 +11,19 @@ their exact float values.  fp32 tensors are returned as ``float32``.
 Draw order (fixed, so a seed names one input set):
   prefill:  q, k, v, [dout], sink
   decode:   q, sink, context lengths, page permutation, k pool, v pool
+Each N(0,1) tensor is drawn in blocks of 2^22 elements; block i of the n-th
+tensor of a case comes from numpy.random.default_rng((seed, n, i)), so large
+pools can be drawn by several threads with a result that does not depend on
+the thread count.  The small integer draws (lengths, permutation) come from
+numpy.random.default_rng((seed, 1000)).
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
+
+_BLOCK = 1 << 22
 
 BF16 = "bf16"
 F32 = "f32"
@@ -21,9 +31,12 @@ F32 = "f32"
 
 def f32_to_bf16_bits(x):
     """Round float32 values to bfloat16 (nearest even) and return the bits."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    lsb = u >> 16
+    lsb &= 1
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= 16
     return u.astype(np.uint16)
 
 
@@ -38,23 +51,49 @@ def values(x, dtype):
     return bf16_to_f32(x) if dtype == BF16 else np.asarray(x, dtype=np.float32)
 
 
-def _normal(rng, shape, dtype):
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    return f32_to_bf16_bits(x) if dtype == BF16 else x
+class _Draws:
+    """Numbered N(0,1) tensors of one case (see the module docstring)."""
+
+    def __init__(self, seed):
+        self.seed = int(seed)
+        self.n = 0
+
+    def normal(self, shape, dtype):
+        tid = self.n
+        self.n += 1
+        size = int(np.prod(shape))
+        out = np.empty(size, dtype=np.uint16 if dtype == BF16 else np.float32)
+        nblk = (size + _BLOCK - 1) // _BLOCK
+
+        def fill(i):
+            lo, hi = i * _BLOCK, min(size, (i + 1) * _BLOCK)
+            x = np.random.default_rng((self.seed, tid, i)).standard_normal(hi - lo, dtype=np.float32)
+            out[lo:hi] = f32_to_bf16_bits(x) if dtype == BF16 else x
+
+        if nblk > 1:
+            workers = min(16, len(os.sched_getaffinity(0)), nblk)
+            with ThreadPoolExecutor(workers) as ex:
+                list(ex.map(fill, range(nblk)))
+        elif nblk == 1:
+            fill(0)
+        return out.reshape(shape)
+
+    def sink(self, Hq):
+        return self.normal((Hq,), F32)
 
 
 def prefill_case(B, Sq, Sk, Hq, Hkv, D, dtype=BF16, seed=0, sink=True, dout=False):
     """Q [B,Sq,Hq,D], K/V [B,Sk,Hkv,D], optional dO [B,Sq,Hq,D], sink [Hq] fp32."""
-    rng = np.random.default_rng(seed)
+    dr = _Draws(seed)
     case = {
         "dtype": dtype,
-        "q": _normal(rng, (B, Sq, Hq, D), dtype),
-        "k": _normal(rng, (B, Sk, Hkv, D), dtype),
-        "v": _normal(rng, (B, Sk, Hkv, D), dtype),
+        "q": dr.normal((B, Sq, Hq, D), dtype),
+        "k": dr.normal((B, Sk, Hkv, D), dtype),
+        "v": dr.normal((B, Sk, Hkv, D), dtype),
     }
     if dout:
-        case["dout"] = _normal(rng, (B, Sq, Hq, D), dtype)
-    case["sink"] = rng.standard_normal(size=(Hq,), dtype=np.float32) if sink else None
+        case["dout"] = dr.normal((B, Sq, Hq, D), dtype)
+    case["sink"] = dr.sink(Hq) if sink else None
     return case
 
 
@@ -68,9 +107,10 @@ def decode_case(B, Hq, Hkv, D, page_size, len_lo, len_hi, dtype=BF16, seed=0,
     [B, ceil(max_len / P)] padded with -1.  Pools are [num_pages, P, Hkv, D].
     With nan_poison, the slots past L_b in each sequence's last page hold NaN.
     """
-    rng = np.random.default_rng(seed)
-    case = {"dtype": dtype, "q": _normal(rng, (B, Hq, D), dtype)}
-    case["sink"] = rng.standard_normal(size=(Hq,), dtype=np.float32) if sink else None
+    dr = _Draws(seed)
+    rng = np.random.default_rng((int(seed), 1000))
+    case = {"dtype": dtype, "q": dr.normal((B, Hq, D), dtype)}
+    case["sink"] = dr.sink(Hq) if sink else None
     if lengths is None:
         lengths = rng.integers(len_lo, len_hi, size=B, endpoint=True)
     lengths = np.asarray(lengths, dtype=np.int32)
@@ -86,8 +126,8 @@ def decode_case(B, Hq, Hkv, D, page_size, len_lo, len_hi, dtype=BF16, seed=0,
         bt[b, :n] = perm[pos:pos + n]
         pos += n
     shape = (total, page_size, Hkv, D)
-    kc = _normal(rng, shape, dtype)
-    vc = _normal(rng, shape, dtype)
+    kc = dr.normal(shape, dtype)
+    vc = dr.normal(shape, dtype)
     if nan_poison:
         nan = f32_to_bf16_bits(np.float32(np.nan)) if dtype == BF16 else np.float32(np.nan)
         for b in range(B):
@@ -101,17 +141,3 @@ def decode_case(B, Hq, Hkv, D, page_size, len_lo, len_hi, dtype=BF16, seed=0,
                  "page_size": page_size, "num_pages": total, "max_len": max_len})
     return case
 
-
-def poison_unselected(case, window):
-    """Write NaN into every cached token that the window leaves out (for tests)."""
-    w1, w2 = window
-    P = case["page_size"]
-    nan = f32_to_bf16_bits(np.float32(np.nan)) if case["dtype"] == BF16 else np.float32(np.nan)
-    for b, L in enumerate(case["seqlens"].tolist()):
-        if L <= w1 + w2:
-            continue
-        t = np.arange(w1, L - w2)
-        pages = case["block_table"][b, t // P]
-        case["k_cache"][pages, t % P] = nan
-        case["v_cache"][pages, t % P] = nan
-    return case

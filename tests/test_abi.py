@@ -1,0 +1,179 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before any HIP call
+(fake, never-dereferenced addresses are used for the pointer arguments)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from softmax_learnable_sink_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_sink.h")
+
+P = ctypes.c_void_p(0x10000)   # 16-byte aligned fake address, never dereferenced
+P_ODD = ctypes.c_void_p(0x10002)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from softmax_learnable_sink_amd import build
+        build.build()
+    return binding.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(attn_sink_\w+)\s*\(", text,
+                                 re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for n in ("attn_sink_fwd_prefill", "attn_sink_fwd_decode_paged", "attn_sink_bwd",
+              "attn_sink_decode_workspace_bytes", "attn_sink_bwd_workspace_bytes",
+              "attn_sink_decode_select_slots", "attn_sink_gather_kv", "attn_sink_last_error",
+              "attn_sink_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_abi_version(lib):
+    text = open(HEADER).read()
+    v = int(re.search(r"#define ATTN_SINK_ABI_VERSION (\d+)", text).group(1))
+    assert binding.abi_version() == v
+
+
+def _prefill(lib, **kw):
+    a = dict(q=P, k=P, v=P, sink=None, o=P, lse=None, B=1, Sq=8, Sk=8, Hq=4, Hkv=2, D=64,
+             scale=0.125, causal=1, w1=-1, w2=-1, dtype=binding.BF16)
+    a.update(kw)
+    return lib.attn_sink_fwd_prefill(a["q"], a["k"], a["v"], a["sink"], a["o"], a["lse"], a["B"],
+                                     a["Sq"], a["Sk"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+                                     a["causal"], a["w1"], a["w2"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(o=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(B=0), binding.ERR_INVALID_ARG, "B >= 1"),
+    (dict(Sq=0), binding.ERR_INVALID_ARG, "Sq >= 1"),
+    (dict(Hq=6, Hkv=4), binding.ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(D=96), binding.ERR_UNSUPPORTED, "64 or 128"),
+    (dict(scale=0.0), binding.ERR_INVALID_ARG, "softmax_scale"),
+    (dict(scale=float("nan")), binding.ERR_INVALID_ARG, "softmax_scale"),
+    (dict(w1=4, w2=0), binding.ERR_INVALID_ARG, "window"),
+    (dict(w1=-2, w2=5), binding.ERR_INVALID_ARG, "window"),
+    (dict(w1=4, w2=8, causal=0), binding.ERR_UNSUPPORTED, "causal"),
+    (dict(causal=2), binding.ERR_INVALID_ARG, "causal"),
+    (dict(dtype=7), binding.ERR_UNSUPPORTED, "dtype"),
+    (dict(q=P_ODD), binding.ERR_INVALID_ARG, "aligned"),
+])
+def test_prefill_rejects(lib, kw, status, msg):
+    assert _prefill(lib, **kw) == status
+    assert msg in binding.last_error()
+
+
+def _decode(lib, **kw):
+    a = dict(B=2, Hq=8, Hkv=2, D=64, P=16, maxp=4, npages=8, scale=0.125, w1=-1, w2=-1, ns=0,
+             ws=P, wsb=1 << 20, dtype=binding.BF16, q=P, bt=P, sl=P)
+    a.update(kw)
+    return lib.attn_sink_fwd_decode_paged(a["q"], P, P, a["bt"], a["sl"], None, P, None, a["B"],
+                                          a["Hq"], a["Hkv"], a["D"], a["P"], a["maxp"],
+                                          a["npages"], a["scale"], a["w1"], a["w2"], a["ns"],
+                                          a["ws"], a["wsb"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(P=12), binding.ERR_UNSUPPORTED, "power of two"),
+    (dict(P=512), binding.ERR_UNSUPPORTED, "power of two"),
+    (dict(D=32), binding.ERR_UNSUPPORTED, "64 or 128"),
+    (dict(Hq=9), binding.ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(maxp=0), binding.ERR_INVALID_ARG, "max_pages_per_seq"),
+    (dict(npages=0), binding.ERR_INVALID_ARG, "num_pages"),
+    (dict(ns=-1), binding.ERR_INVALID_ARG, "num_splits"),
+    (dict(ws=None), binding.ERR_WORKSPACE, "workspace"),
+    (dict(wsb=16), binding.ERR_WORKSPACE, "too small"),
+    (dict(bt=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(sl=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(dtype=binding.F32), binding.ERR_UNSUPPORTED, "bf16"),
+    (dict(w1=3, w2=-1), binding.ERR_INVALID_ARG, "window"),
+])
+def test_decode_rejects(lib, kw, status, msg):
+    assert _decode(lib, **kw) == status
+    assert msg in binding.last_error()
+
+
+def test_decode_workspace_query(lib):
+    # 64 sequences of up to 2048 pages of 16 tokens, 64/8 heads, D 64
+    n = binding.attn_sink_decode_workspace_bytes(64, 64, 8, 64, 16, 2048)
+    assert n > 0 and n % (64 * 64 * 66 * 4) == 0
+    # the window caps the selected length, so the workspace shrinks
+    assert binding.attn_sink_decode_workspace_bytes(64, 64, 8, 64, 16, 2048, (1024, 7168)) < n
+    # more requested splits never need less workspace
+    a = binding.attn_sink_decode_workspace_bytes(4, 8, 2, 64, 16, 64, None, 2)
+    b = binding.attn_sink_decode_workspace_bytes(4, 8, 2, 64, 16, 64, None, 8)
+    assert 0 < a < b
+    assert binding.attn_sink_decode_workspace_bytes(4, 8, 2, 96, 16, 64) == 0
+
+
+def _bwd(lib, **kw):
+    a = dict(sink=None, dsink=None, B=1, Sq=8, Sk=8, Hq=4, Hkv=2, D=64, scale=0.125, causal=1,
+             w1=-1, w2=-1, ws=P, wsb=1 << 20, dtype=binding.BF16, lse=P, dq=P)
+    a.update(kw)
+    return lib.attn_sink_bwd(P, P, P, P, P, a["lse"], a["sink"], a["dq"], P, P, a["dsink"], a["B"],
+                             a["Sq"], a["Sk"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"],
+                             a["w1"], a["w2"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(sink=P), binding.ERR_INVALID_ARG, "dsink"),
+    (dict(lse=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(dq=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(dtype=binding.F32), binding.ERR_UNSUPPORTED, "bf16"),
+    (dict(wsb=4), binding.ERR_WORKSPACE, "too small"),
+    (dict(ws=None), binding.ERR_WORKSPACE, "workspace"),
+    (dict(Sk=0), binding.ERR_INVALID_ARG, "Sk >= 1"),
+    (dict(D=256), binding.ERR_UNSUPPORTED, "64 or 128"),
+    (dict(w1=2, w2=3, causal=0), binding.ERR_UNSUPPORTED, "causal"),
+])
+def test_bwd_rejects(lib, kw, status, msg):
+    assert _bwd(lib, **kw) == status
+    assert msg in binding.last_error()
+
+
+def test_bwd_workspace_query(lib):
+    B, S, Hq = 2, 8192, 64
+    n = binding.attn_sink_bwd_workspace_bytes(B, S, S, Hq, 8, 64)
+    assert n == 4 * (B * Hq * S + B * Hq * (S // 64))
+    assert binding.attn_sink_bwd_workspace_bytes(B, S, S, Hq, 7, 64) == 0
+
+
+def test_select_and_gather_reject(lib):
+    r = lib.attn_sink_decode_select_slots(P, P, 1, 4, 3, -1, -1, P, P, 8, None)
+    assert r == binding.ERR_UNSUPPORTED and "power of two" in binding.last_error()
+    r = lib.attn_sink_decode_select_slots(None, P, 1, 4, 4, -1, -1, P, P, 8, None)
+    assert r == binding.ERR_INVALID_ARG
+    r = lib.attn_sink_gather_kv(P, P, P, P, 1, 2, 64, 16, 4, 5, 0, P, P, 8, binding.BF16, None)
+    assert r == binding.ERR_INVALID_ARG and "window" in binding.last_error()
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        binding.attn_sink_fwd_prefill(q, q, q)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()
