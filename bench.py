@@ -1,0 +1,306 @@
+"""Benchmark of the sink-attention hot path on one MI355X.
+
+One step runs every entry point once over its synthetic workload:
+  prefill   B4, S4096, 64 query / 8 KV heads, D64, causal, bf16, sink      (value)
+  decode    B64, 64/8 heads, D64, page 16, L ~ U[1024, 32768], sink
+  window32  B32, 32/8 heads, D128, page 16, L ~ U[16384, 65536], window 1024+7168, sink
+  window1   the same with B1 (latency bound, reported only)
+  train     B2, S8192, 64/8 heads, D64, causal: forward + backward with dSink
+Each entry point is bracketed by HIP events on the stream it is launched on;
+`value` is the prefill throughput in TFLOP/s of algorithmic work (4*D flops per
+visible (query, key) pair), `decode_gbps` the paged decode's algorithmic HBM
+bytes (K and V rows of the attended tokens + Q + O + block table) per second.
+A bounded sample of the fp64 CPU oracle is timed on the host for comparison.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--parts a,b] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attention TFLOP/s + paged-decode HBM GB/s (% of MI355X roofline)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PARTS = ("prefill", "decode", "window32", "window1", "train")
+
+
+def causal_pairs(B, Hq, Sq, Sk):
+    """Visible (query, key) pairs of a bottom-right causal attention."""
+    off = Sk - Sq
+    per_head = sum(max(0, min(Sk, off + i + 1)) for i in range(Sq))
+    return B * Hq * per_head
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "softmax_learnable_sink_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_hash):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    if data.get("kernel_source_hash") != kernel_hash:
+        return {}
+    return data.get("bytes_per_launch", {})
+
+
+class Workloads:
+    def __init__(self, parts, dev):
+        import numpy as np
+        import torch
+        from softmax_learnable_sink_amd import synth
+
+        def dt(x):
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        def i32(x):
+            return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+
+        self.parts = parts
+        self.info = {}
+        if "prefill" in parts:
+            B, S, Hq, Hkv, D = 4, 4096, 64, 8, 64
+            c = synth.prefill_case(B, S, S, Hq, Hkv, D, seed=0)
+            self.pf = dict(q=dt(c["q"]), k=dt(c["k"]), v=dt(c["v"]),
+                           sink=torch.from_numpy(c["sink"]).to(dev))
+            self.pf["o"] = torch.empty_like(self.pf["q"])
+            self.pf["lse"] = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+            pairs = causal_pairs(B, Hq, S, S)
+            self.info["prefill"] = dict(flops=4 * D * pairs, pairs=pairs,
+                                        shape=f"B{B} S{S} H{Hq}/{Hkv} D{D} causal bf16")
+            self.pf_case = c
+        for name, spec in (("decode", (64, 64, 8, 64, 1024, 32768, None)),
+                           ("window32", (32, 32, 8, 128, 16384, 65536, (1024, 7168))),
+                           ("window1", (1, 32, 8, 128, 16384, 65536, (1024, 7168)))):
+            if name not in parts:
+                continue
+            B, Hq, Hkv, D, lo, hi, w = spec
+            c = synth.decode_case(B, Hq, Hkv, D, 16, lo, hi, seed=0)
+            d = dict(q=dt(c["q"]), k=dt(c["k_cache"]), v=dt(c["v_cache"]), bt=i32(c["block_table"]),
+                     sl=i32(c["seqlens"]), sink=torch.from_numpy(c["sink"]).to(dev), window=w)
+            d["o"] = torch.empty_like(d["q"])
+            d["lse"] = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+            from softmax_learnable_sink_amd import binding
+            nbytes = binding.attn_sink_decode_workspace_bytes(B, Hq, Hkv, D, 16, c["block_table"].shape[1], w)
+            d["ws"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            L = c["seqlens"].astype(np.int64)
+            sel = np.minimum(L, sum(w)) if w else L
+            kv_bytes = int(sel.sum()) * Hkv * D * 2 * 2
+            # pages holding selected tokens: one int32 block-table entry each
+            pages = 0
+            for Lb in L.tolist():
+                if w and Lb > sum(w):
+                    toks = np.concatenate([np.arange(w[0]), np.arange(Lb - w[1], Lb)])
+                    pages += len(np.unique(toks // 16))
+                else:
+                    pages += (Lb + 15) // 16
+            # q in, o out (bf16), lse out (fp32), seqlens, sink, block-table entries
+            io_bytes = 2 * B * Hq * D * 2 + 4 * B * Hq + 4 * B + 4 * Hq + 4 * pages
+            self.info[name] = dict(bytes=kv_bytes + io_bytes, kv_bytes=kv_bytes,
+                                   flops=4 * D * Hq * int(sel.sum()),
+                                   shape=f"B{B} H{Hq}/{Hkv} D{D} P16 L~U[{lo},{hi}]"
+                                         + (f" window {w[0]}+{w[1]}" if w else ""))
+            setattr(self, name, d)
+            if name == "decode":
+                self.dec_case = c
+        if "train" in parts:
+            B, S, Hq, Hkv, D = 2, 8192, 64, 8, 64
+            c = synth.prefill_case(B, S, S, Hq, Hkv, D, seed=0, dout=True)
+            t = dict(q=dt(c["q"]), k=dt(c["k"]), v=dt(c["v"]), do=dt(c["dout"]),
+                     sink=torch.from_numpy(c["sink"]).to(dev))
+            t["o"] = torch.empty_like(t["q"])
+            t["lse"] = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+            t["dq"] = torch.empty_like(t["q"])
+            t["dk"] = torch.empty_like(t["k"])
+            t["dv"] = torch.empty_like(t["v"])
+            t["dsink"] = torch.empty_like(t["sink"])
+            from softmax_learnable_sink_amd import binding
+            t["ws"] = torch.empty(binding.attn_sink_bwd_workspace_bytes(B, S, S, Hq, Hkv, D),
+                                  dtype=torch.uint8, device=dev)
+            pairs = causal_pairs(B, Hq, S, S)
+            self.info["train"] = dict(flops=14 * D * pairs, fwd_flops=4 * D * pairs,
+                                      bwd_flops=10 * D * pairs, pairs=pairs,
+                                      shape=f"B{B} S{S} H{Hq}/{Hkv} D{D} causal bf16 fwd+bwd")
+            self.tr = t
+
+    def run(self, name):
+        from softmax_learnable_sink_amd import binding
+        if name == "prefill":
+            p = self.pf
+            binding.attn_sink_fwd_prefill(p["q"], p["k"], p["v"], p["sink"], causal=True,
+                                          softmax_scale=0.125, out=p["o"], lse=p["lse"])
+        elif name in ("decode", "window32", "window1"):
+            d = getattr(self, name)
+            D = d["q"].shape[-1]
+            binding.attn_sink_fwd_decode_paged(d["q"], d["k"], d["v"], d["bt"], d["sl"], d["sink"],
+                                               softmax_scale=1 / math.sqrt(D), window=d["window"],
+                                               out=d["o"], lse=d["lse"], workspace=d["ws"])
+        elif name == "train":
+            t = self.tr
+            binding.attn_sink_fwd_prefill(t["q"], t["k"], t["v"], t["sink"], causal=True,
+                                          softmax_scale=0.125, out=t["o"], lse=t["lse"])
+            binding.attn_sink_bwd(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], t["sink"],
+                                  causal=True, softmax_scale=0.125, dq=t["dq"], dk=t["dk"],
+                                  dv=t["dv"], dsink=t["dsink"], workspace=t["ws"])
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the prefill workload:
+    the first (batch, head) pairs, in order, that fit the time budget, all 4096
+    query rows each."""
+    import numpy as np
+    import oracle
+    from softmax_learnable_sink_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                    default=1)
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    c = wl.pf_case
+    B, S, Hq, Hkv, D = 4, 4096, 64, 8, 64
+    g = Hq // Hkv
+    t_total, n = 0.0, 0
+    while t_total < budget_s and n < B * Hq:
+        b, h = divmod(n, Hq)
+        q = synth.bf16_to_f32(c["q"][b:b + 1, :, h:h + 1]).astype(np.float64)
+        k = synth.bf16_to_f32(c["k"][b:b + 1, :, h // g:h // g + 1]).astype(np.float64)
+        v = synth.bf16_to_f32(c["v"][b:b + 1, :, h // g:h // g + 1]).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.prefill(q, k, v, c["sink"][h:h + 1], 0.125, causal=True)
+        t_total += time.perf_counter() - t0
+        n += 1
+    flops = 4 * D * causal_pairs(1, n, S, S)
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"prefill S4096 D64 causal, the first {n} of 256 (batch, head) pairs "
+                      f"in (batch, head) order, all rows; {t_total:.1f} s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--parts", default=",".join(PARTS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the sink-attention path has no multi-GPU code)", file=sys.stderr)
+        sys.exit(2)
+    parts = [p for p in args.parts.split(",") if p]
+    for p in parts:
+        if p not in PARTS:
+            sys.exit(f"unknown part {p}")
+
+    import torch
+    from softmax_learnable_sink_amd import binding
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    binding.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# building workloads: {parts}", file=sys.stderr, flush=True)
+    wl = Workloads(parts, dev)
+    torch.cuda.synchronize()
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    events = {p: [] for p in parts}
+
+    def step(record):
+        for p in parts:
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            wl.run(p)
+            if record:
+                e1.record(stream)
+                events[p].append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"# warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {p: sum(a.elapsed_time(b) for a, b in events[p]) / max(1, args.steps) for p in parts}
+
+    khash = kernel_source_hash()
+    traffic = load_traffic(khash)
+    out = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / max(1, args.steps), 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": "sink attention hot path: " + "; ".join(
+               f"{p} {wl.info[p]['shape']}" for p in parts)}}
+    parts_out = {}
+    for p in parts:
+        info = wl.info[p]
+        rec = {"ms": round(ms[p], 5), "shape": info["shape"]}
+        if "bytes" in info:
+            gbps = info["bytes"] / (ms[p] * 1e-3) / 1e9
+            rec.update(gbps=round(gbps, 2), hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
+                       algorithmic_bytes=info["bytes"])
+        if p in ("prefill", "train"):
+            tf = info["flops"] / (ms[p] * 1e-3) / 1e12
+            rec.update(tflops=round(tf, 2), mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4),
+                       algorithmic_flops=info["flops"])
+        parts_out[p] = rec
+    out["parts"] = parts_out
+    if "prefill" in parts:
+        pf = parts_out["prefill"]
+        out["value"] = pf["tflops"]
+        tb = traffic.get("prefill_bf16_kernel")
+        out["roofline"] = {"bound": "mfma", "achieved": pf["tflops"], "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": pf["mfma_frac"],
+                           "traffic": tb, "kernel": "prefill_bf16_kernel<64,2>",
+                           "kernel_source_hash": khash}
+    if "decode" in parts:
+        dc = parts_out["decode"]
+        out["decode_gbps"] = dc["gbps"]
+        out["decode_roofline"] = {"bound": "hbm", "achieved": dc["gbps"], "peak": PEAK_HBM_GBPS,
+                                  "unit": "GB/s", "frac": dc["hbm_frac"],
+                                  "traffic": traffic.get("decode_partial_kernel"),
+                                  "kernel": "decode_partial_kernel<64> + decode_combine_kernel<64>"}
+    if out["value"] is None:
+        first = parts_out[parts[0]]
+        out["value"] = first.get("tflops", first.get("gbps"))
+        out["unit"] = "TFLOP/s" if "tflops" in first else "GB/s"
+    if not args.no_cpu_baseline and "prefill" in parts:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
