@@ -38,22 +38,29 @@ __device__ __forceinline__ uint32_t pick16(const uint4& x, int e) {
 
 // 64 rows x D tile of a [.., rows, heads, D] tensor: each thread loads one
 // (row pair, 16-byte chunk) item per 256 items and writes it both in natural
-// layout (rows permuted within 32-blocks, see lds_row) and transposed.
+// layout (rows permuted within 32-blocks, see lds_row) and transposed.  Loads
+// go through a buffer resource per tile, so rows past the end read as zero.
 template <int D>
 struct PairTile {
   static constexpr int CH = D / 8;
   static constexpr int N = (kTile / 2) * CH / kThreads;
   uint4 r[N][2];
-  __device__ __forceinline__ void load(const __bf16* base, size_t rs, int row0, int nrows, int tid) {
+  uint32_t off[N][2];
+  __device__ __forceinline__ void init(size_t rs, int tid) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int idx = tid + i * kThreads;
       const int pr = idx % (kTile / 2), c = idx / (kTile / 2);
-      const int j = row0 + 2 * pr;
-      r[i][0] = j < nrows ? *reinterpret_cast<const uint4*>(base + (size_t)j * rs + 8 * c)
-                          : make_uint4(0, 0, 0, 0);
-      r[i][1] = j + 1 < nrows ? *reinterpret_cast<const uint4*>(base + (size_t)(j + 1) * rs + 8 * c)
-                              : make_uint4(0, 0, 0, 0);
+      off[i][0] = (uint32_t)(((size_t)(2 * pr) * rs + 8 * c) * 2);
+      off[i][1] = (uint32_t)(((size_t)(2 * pr + 1) * rs + 8 * c) * 2);
+    }
+  }
+  __device__ __forceinline__ void load(const __bf16* base, size_t rs, int row0, int nrows) {
+    const auto rsrc = make_rsrc(base + (size_t)row0 * rs, (uint32_t)((size_t)(nrows - row0) * rs * 2));
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      r[i][0] = buf_load16(rsrc, off[i][0]);
+      r[i][1] = buf_load16(rsrc, off[i][1]);
     }
   }
   __device__ __forceinline__ void store(__bf16* nat, __bf16* tr, int tid) const {
@@ -80,14 +87,18 @@ struct RowTile {
   static constexpr int CH = D / 8;
   static constexpr int N = kTile * CH / kThreads;
   uint4 r[N];
-  __device__ __forceinline__ void load(const __bf16* base, size_t rs, int row0, int nrows, int tid) {
+  uint32_t off[N];
+  __device__ __forceinline__ void init(size_t rs, int tid) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int idx = tid + i * kThreads;
-      const int j = row0 + idx / CH, c = idx % CH;
-      r[i] = j < nrows ? *reinterpret_cast<const uint4*>(base + (size_t)j * rs + 8 * c)
-                       : make_uint4(0, 0, 0, 0);
+      off[i] = (uint32_t)(((size_t)(idx / CH) * rs + 8 * (idx % CH)) * 2);
     }
+  }
+  __device__ __forceinline__ void load(const __bf16* base, size_t rs, int row0, int nrows) {
+    const auto rsrc = make_rsrc(base + (size_t)row0 * rs, (uint32_t)((size_t)(nrows - row0) * rs * 2));
+#pragma unroll
+    for (int i = 0; i < N; ++i) r[i] = buf_load16(rsrc, off[i]);
   }
   __device__ __forceinline__ void store(__bf16* nat, int tid) const {
     constexpr int NS = D + kPad;
@@ -157,7 +168,7 @@ __global__ void bwd_dsink_reduce_kernel(const float* __restrict__ part, float* _
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV.  Grid (ceil(Sk/128), Hkv, B).  Wave w owns keys k0 + 32w .. +31,
+// dK / dV.  Grid (Hkv, B, ceil(Sk/128)).  Wave w owns keys k0 + 32w .. +31,
 // held as MFMA B operands (K^T, V^T) in registers.  Per (head, query tile):
 //   S  = Q K^T,  dP = dO V^T        (A = Q, dO from LDS, natural layout)
 //   P = 2^(S*sl2 - LSE*log2e), dS = P (dP - Di)
@@ -175,7 +186,7 @@ struct DkdvLds {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Sq, int Sk, int Hq, int Hkv, float scale,
@@ -184,9 +195,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   constexpr int NS = D + kPad, TS = kTile + kPad;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, l32 = lane & 31;
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  // grid: (Hkv, B, key blocks) with the key block slowest, so the key blocks
+  // that see the most query rows (the first ones under a causal mask) start first
+  const int kvh = blockIdx.x, b = blockIdx.y;
   const int g = Hq / Hkv;
-  const int k0 = blockIdx.x * 128;
+  const int k0 = blockIdx.z * 128;
   const int k1 = min(Sk, k0 + 128);
   const int key = k0 + 32 * wave + l32;
   const int off = Sk - Sq;
@@ -222,29 +235,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   const size_t rs = (size_t)Hq * D;
   PairTile<D> tq, tdo;
+  tq.init(rs, tid);
+  tdo.init(rs, tid);
   float lse_r = 0.f, di_r = 0.f;
   auto load_iter = [&](int it) {
     const int h = kvh * g + it / nq;
     const int i0 = (t_lo + it % nq) * kTile;
     const size_t base = ((size_t)b * Sq * Hq + h) * D;
-    tq.load(q + base, rs, i0, Sq, tid);
-    tdo.load(dout + base, rs, i0, Sq, tid);
-    if (tid < kTile) {
-      const int i = i0 + tid;
-      const size_t x = ((size_t)b * Hq + h) * Sq + i;
-      lse_r = i < Sq ? lse[x] * kLog2e : 0.f;
-      di_r = i < Sq ? di[x] : 0.f;
-    }
+    tq.load(q + base, rs, i0, Sq);
+    tdo.load(dout + base, rs, i0, Sq);
+    // per-row LSE and Di of the tile (zero past Sq)
+    const size_t x = ((size_t)b * Hq + h) * Sq + i0;
+    const uint32_t nb = (uint32_t)(Sq - i0) * 4;
+    lse_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                          make_rsrc(lse + x, nb), (tid & 63) * 4, 0, 0));
+    di_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         make_rsrc(di + x, nb), (tid & 63) * 4, 0, 0));
   };
   auto store_iter = [&](int buf) {
     tq.store(s.q[buf], s.qt[buf], tid);
     tdo.store(s.dO[buf], s.dOt[buf], tid);
     if (tid < kTile) {
-      s.lse2[buf][tid] = lse_r;
+      s.lse2[buf][tid] = lse_r * kLog2e;
       s.di[buf][tid] = di_r;
     }
   };
 
+  __builtin_amdgcn_s_waitcnt(0);
   if (niter > 0) {
     load_iter(0);
     store_iter(0);
@@ -255,74 +272,60 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int buf = it & 1;
     const int i0 = (t_lo + it % nq) * kTile;
     if (it + 1 < niter) load_iter(it + 1);
-
-    f32x16 sa[2], pa[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      sa[qb] = f32x16{};
-      pa[qb] = f32x16{};
-    }
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int r = (32 * qb + l32) * NS + 16 * ks + 8 * hh;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&s.q[buf][r]);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(&s.dO[buf][r]);
-        sa[qb] = mfma32(qa, kf[ks], sa[qb]);
-        pa[qb] = mfma32(da, vf[ks], pa[qb]);
-      }
-
     const int p0 = off + i0;
     const bool need_mask = (i0 + kTile > Sq) || (causal && p0 < k1 - 1) ||
                            (w2 > 0 && k1 - 1 >= w1 && p0 + kTile - 1 - w2 >= k0);
-    bf16x8 pb[2][2], sb[2][2];
+
+    // one 32-row block at a time keeps the live registers low
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      f32x16 sa = f32x16{}, pa = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int r = (32 * qb + l32) * NS + 16 * ks + 8 * hh;
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&s.q[buf][r]);
+        const bf16x8 da = *reinterpret_cast<const bf16x8*>(&s.dO[buf][r]);
+        sa = mfma32(qa, kf[ks], sa);
+        pa = mfma32(da, vf[ks], pa);
+      }
       const int rbase = 32 * qb + 16 * hh;
-      float lv[16], dv16[16];
+      float pv[16], dsv[16];
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
         const f32x4 a = *reinterpret_cast<const f32x4*>(&s.lse2[buf][rbase + 4 * c4]);
         const f32x4 d2 = *reinterpret_cast<const f32x4*>(&s.di[buf][rbase + 4 * c4]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          lv[4 * c4 + e] = a[e];
-          dv16[4 * c4 + e] = d2[e];
+          const int i = 4 * c4 + e;
+          float p = exp2_fast(__builtin_fmaf(sa[i], sl2, -a[e]));
+          if (need_mask) {
+            const int row = i0 + rbase + i;
+            const bool ok = (row < Sq) & (key < Sk) & key_visible(key, off + row, causal, w1, w2);
+            p = ok ? p : 0.f;
+          }
+          pv[i] = p;
+          dsv[i] = p * (pa[i] - d2[e]);
         }
       }
-      float pv[16], dsv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = exp2_fast(__builtin_fmaf(sa[qb][i], sl2, -lv[i]));
-        if (need_mask) {
-          const int row = i0 + rbase + i;
-          const bool ok = row < Sq && key < Sk && key_visible(key, off + row, causal, w1, w2);
-          p = ok ? p : 0.f;
-        }
-        pv[i] = p;
-        dsv[i] = p * (pa[qb][i] - dv16[i]);
-      }
+      bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        pb[qb][c] = to_bf16x8(pv[8 * c], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3], pv[8 * c + 4],
-                              pv[8 * c + 5], pv[8 * c + 6], pv[8 * c + 7]);
-        sb[qb][c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
-                              dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
+        pb[c] = to_bf16x8(pv[8 * c], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3], pv[8 * c + 4],
+                          pv[8 * c + 5], pv[8 * c + 6], pv[8 * c + 7]);
+        sb[c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
+                          dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
       }
-    }
-
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int d = 32 * db + l32;
+      for (int db = 0; db < D / 32; ++db) {
+        const int d = 32 * db + l32;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int qb = t >> 1, c = t & 1;
-        const int col = 32 * qb + 16 * hh + 8 * c;
-        const bf16x8 dot = *reinterpret_cast<const bf16x8*>(&s.dOt[buf][d * TS + col]);
-        const bf16x8 qt = *reinterpret_cast<const bf16x8*>(&s.qt[buf][d * TS + col]);
-        dva[db] = mfma32(dot, pb[qb][c], dva[db]);
-        dka[db] = mfma32(qt, sb[qb][c], dka[db]);
+        for (int c = 0; c < 2; ++c) {
+          const int col = 32 * qb + 16 * hh + 8 * c;
+          const bf16x8 dot = *reinterpret_cast<const bf16x8*>(&s.dOt[buf][d * TS + col]);
+          const bf16x8 qt = *reinterpret_cast<const bf16x8*>(&s.qt[buf][d * TS + col]);
+          dva[db] = mfma32(dot, pb[c], dva[db]);
+          dka[db] = mfma32(qt, sb[c], dka[db]);
+        }
       }
     }
 
@@ -399,12 +402,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const int hh = lane >> 5, l32 = lane & 31;
   const int g = Hq / Hkv;
   const int groups = g / hpw;
-  const int kvh = blockIdx.y / groups;
-  const int h = kvh * g + (blockIdx.y % groups) * hpw + (wave % hpw);
+  // grid: (head groups, B, row tiles) with the row tile slowest and reversed,
+  // so the tiles with the most keys under a causal mask start first
+  const int kvh = blockIdx.x / groups;
+  const int h = kvh * g + (blockIdx.x % groups) * hpw + (wave % hpw);
   const int rb = wave / hpw;
   const int R = 32 * (4 / hpw);
-  const int b = blockIdx.z;
-  const int row0 = (gridDim.x - 1 - blockIdx.x) * R;
+  const int b = blockIdx.y;
+  const int row0 = (gridDim.z - 1 - blockIdx.z) * R;
   const int row = row0 + rb * 32 + l32;
   const int off = Sk - Sq;
   const int p = off + row;
@@ -440,9 +445,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
   const __bf16* vbase = v + ((size_t)b * Sk * Hkv + kvh) * D;
   PairTile<D> tk;
   RowTile<D> tv;
+  tk.init(rs, tid);
+  tv.init(rs, tid);
+  __builtin_amdgcn_s_waitcnt(0);
   if (ntiles > 0) {
-    tk.load(kbase, rs, tr.tile(0) * kTile, Sk, tid);
-    tv.load(vbase, rs, tr.tile(0) * kTile, Sk, tid);
+    tk.load(kbase, rs, tr.tile(0) * kTile, Sk);
+    tv.load(vbase, rs, tr.tile(0) * kTile, Sk);
     tk.store(s.k[0], s.kt[0], tid);
     tv.store(s.v[0], tid);
   }
@@ -452,8 +460,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const int buf = it & 1;
     const int key0 = tr.tile(it) * kTile;
     if (it + 1 < ntiles) {
-      tk.load(kbase, rs, tr.tile(it + 1) * kTile, Sk, tid);
-      tv.load(vbase, rs, tr.tile(it + 1) * kTile, Sk, tid);
+      tk.load(kbase, rs, tr.tile(it + 1) * kTile, Sk);
+      tv.load(vbase, rs, tr.tile(it + 1) * kTile, Sk);
     }
     f32x16 st[2], dp[2];
 #pragma unroll
@@ -483,7 +491,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
         float pr = exp2_fast(__builtin_fmaf(st[kb][i], sl2, -lse2));
         if (need_mask) {
           const int j = key0 + 32 * kb + 16 * hh + i;
-          const bool ok = row < Sq && j < Sk && key_visible(j, p, causal, w1, w2);
+          const bool ok = (row < Sq) & (j < Sk) & key_visible(j, p, causal, w1, w2);
           pr = ok ? pr : 0.f;
         }
         dsv[i] = pr * (dp[kb][i] - di_r);
@@ -551,9 +559,9 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
   auto* dk = static_cast<__bf16*>(a.dk);
   auto* dv = static_cast<__bf16*>(a.dv);
   const dim3 pgrid(nblk, a.Hq, a.B);
-  const dim3 kgrid((a.Sk + 127) / 128, a.Hkv, a.B);
+  const dim3 kgrid(a.Hkv, a.B, (a.Sk + 127) / 128);
   const int R = 32 * (4 / hpw);
-  const dim3 qgrid((a.Sq + R - 1) / R, a.Hkv * (g / hpw), a.B);
+  const dim3 qgrid(a.Hkv * (g / hpw), a.B, (a.Sq + R - 1) / R);
   if (a.D == 64) {
     bwd_preprocess_kernel<64><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di, part,
                                                               a.Sq, a.Hq);

@@ -55,6 +55,16 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end return 0
+// without a branch.  Word 3 is the gfx9-family default (32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 __device__ __forceinline__ float wave_max_xor(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, 64));
 }
@@ -67,10 +77,11 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask) {
 // ---------------------------------------------------------------------------
 
 // Key j visible to a query at absolute position p (bottom-right causal).
+// Written without short-circuit operators so it compiles to selects.
 __device__ __forceinline__ bool key_visible(int j, int p, int causal, int w1, int w2) {
-  bool ok = !causal || j <= p;
-  if (w2 > 0) ok = ok && (j < w1 || j > p - w2);
-  return ok;
+  const bool c_ok = (causal == 0) | (j <= p);
+  const bool w_ok = (w2 <= 0) | (j < w1) | (j > p - w2);
+  return c_ok & w_ok;
 }
 
 // Number of selected tokens of a sequence of length L.

@@ -49,25 +49,41 @@ struct KVRegs {
   static constexpr int NTG = 32 / TPL;    // lanes sharing one d-chunk
   uint4 kr[2][KS];
   uint4 vr[TPL];
+  uint32_t vvalid;  // bit t: V row t holds a selected token
 
-  __device__ __forceinline__ void load(const int* slot, int base, const __bf16* kbase,
+  // Loads the K rows (score MFMA operand) and V rows (for the transposed LDS
+  // tile) of step tokens base .. base+31.  The instruction stream is the same
+  // for every step: a token without a slot (past the chunk, or a step past the
+  // end when valid == false) reads row 0 of the cache, its K score is masked
+  // and its V row is replaced by zeros when the tile is staged (not here, so
+  // that no register with a load in flight is overwritten).
+  __device__ __forceinline__ void load(const int* slot, int base, bool valid, const __bf16* kbase,
                                        const __bf16* vbase, size_t rs, int lane) {
     const int kg = lane >> 4, r = lane & 15;
+    const int tg = lane % NTG, c = lane / NTG;
+    int ks[2], vs[TPL];
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       // MFMA row r of token group G holds token 8*(r/4) + 4*G + r%4 of the step
       const int sl = slot[base + 8 * (r >> 2) + 4 * G + (r & 3)];
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        kr[G][s] = sl >= 0 ? *reinterpret_cast<const uint4*>(kbase + (size_t)sl * rs + 32 * s + 8 * kg)
-                           : make_uint4(0, 0, 0, 0);
+      ks[G] = valid ? sl : -1;
     }
-    const int tg = lane % NTG, c = lane / NTG;
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
       const int sl = slot[base + TPL * tg + t];
-      vr[t] = sl >= 0 ? *reinterpret_cast<const uint4*>(vbase + (size_t)sl * rs + 8 * c)
-                      : make_uint4(0, 0, 0, 0);
+      vs[t] = valid ? sl : -1;
+    }
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      const __bf16* row = kbase + (size_t)max(ks[G], 0) * rs + 8 * kg;
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) kr[G][s2] = *reinterpret_cast<const uint4*>(row + 32 * s2);
+    }
+    vvalid = 0;
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      vr[t] = *reinterpret_cast<const uint4*>(vbase + (size_t)max(vs[t], 0) * rs + 8 * c);
+      vvalid |= (vs[t] >= 0 ? 1u : 0u) << t;
     }
   }
 };
@@ -75,6 +91,11 @@ struct KVRegs {
 __device__ __forceinline__ uint32_t half16(const uint4& x, int e) {
   const uint32_t w = e < 2 ? x.x : (e < 4 ? x.y : (e < 6 ? x.z : x.w));
   return (w >> (16 * (e & 1))) & 0xffffu;
+}
+// element e of V row t of a step, zero when the row holds no selected token
+template <int D>
+__device__ __forceinline__ uint32_t vhalf(const KVRegs<D>& r, int t, int e) {
+  return ((r.vvalid >> t) & 1u) ? half16(r.vr[t], e) : 0u;
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -90,7 +111,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
     int Hq, int Hkv, int hgroups, int page_shift, int max_pages, float sl2, int w1, int w2,
     int chunk, int max_splits) {
   __shared__ DecLds<D> s;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int kg = lane >> 4, hl = lane & 15;
   const int split = blockIdx.x, b = blockIdx.z;
   const int kvh = blockIdx.y / hgroups, hgi = blockIdx.y % hgroups;
@@ -122,6 +144,71 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
 
   constexpr int TPL = KVRegs<D>::TPL, NTG = KVRegs<D>::NTG;
   __bf16* vt = s.u.vt[wave];
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // One 32-token step of this wave: scores, online softmax, V^T staging, P.V.
+  auto step = [&](const KVRegs<D>& cur, int base, int nsub) {
+    f32x4 sc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+      for (int s2 = 0; s2 < D / 32; ++s2)
+        sc[G] = mfma16(__builtin_bit_cast(bf16x8, cur.kr[G][s2]), qf[s2], sc[G]);
+    float x[8];
+#pragma unroll
+    for (int G = 0; G < 2; ++G)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        x[4 * G + j] = (base + 8 * kg + 4 * G + j < nsub) ? sc[G][j] : kNegInf;
+    float mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    mx = wave_max_xor(mx, 16);
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m, mx * sl2);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = exp2_fast(m - m_use);
+    m = m_new;
+    float p[8], rsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = exp2_fast(__builtin_fmaf(x[e], sl2, -m_use));
+      rsum += p[e];
+    }
+    l = l * alpha + rsum;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
+    const bf16x8 pf = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+
+    // V^T staging: row d = 8*c + e, tokens TPL*tg .. +TPL-1
+    {
+      const int tg = lane % NTG, c = lane / NTG;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16* dst = vt + (8 * c + e) * kVTS + TPL * tg;
+        if constexpr (TPL == 4) {
+          uint2 w;
+          w.x = vhalf(cur, 0, e) | (vhalf(cur, 1, e) << 16);
+          w.y = vhalf(cur, 2, e) | (vhalf(cur, 3, e) << 16);
+          *reinterpret_cast<uint2*>(dst) = w;
+        } else {
+          uint4 w;
+          w.x = vhalf(cur, 0, e) | (vhalf(cur, 1, e) << 16);
+          w.y = vhalf(cur, 2, e) | (vhalf(cur, 3, e) << 16);
+          w.z = vhalf(cur, 4, e) | (vhalf(cur, 5, e) << 16);
+          w.w = vhalf(cur, 6, e) | (vhalf(cur, 7, e) << 16);
+          *reinterpret_cast<uint4*>(dst) = w;
+        }
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + (16 * db + hl) * kVTS + 8 * kg);
+      acc[db] = mfma16(vf, pf, acc[db]);
+    }
+    wave_lds_sync();
+  };
 
   for (int sub0 = u0; sub0 < u1; sub0 += kSub) {
     const int nsub = min(kSub, u1 - sub0);
@@ -129,75 +216,19 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
       s.slot[x] = x < nsub ? slot_of(bt_row, token_of(sub0 + x, L, w1, w2), page_shift) : -1;
     __syncthreads();
     const int nsteps = (nsub + 31) >> 5;
-    KVRegs<D> cur, nxt;
+    // two register sets in turn: the loads of the next step stay in flight
+    // while the current one is computed
+    KVRegs<D> ra, rb;
     int st = wave;
-    if (st < nsteps) cur.load(s.slot, 32 * st, kbase, vbase, rs, lane);
-    for (; st < nsteps; st += 4) {
-      const int base = 32 * st;
-      if (st + 4 < nsteps) nxt.load(s.slot, base + 128, kbase, vbase, rs, lane);
-
-      // scores of tokens 8*kg + 4*G + j for head hl
-      f32x4 sc[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-      for (int G = 0; G < 2; ++G)
-#pragma unroll
-        for (int s2 = 0; s2 < D / 32; ++s2)
-          sc[G] = mfma16(__builtin_bit_cast(bf16x8, cur.kr[G][s2]), qf[s2], sc[G]);
-      float x[8];
-#pragma unroll
-      for (int G = 0; G < 2; ++G)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          x[4 * G + j] = (base + 8 * kg + 4 * G + j < nsub) ? sc[G][j] : kNegInf;
-      float mx = x[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);
-      const float m_new = fmaxf(m, mx * sl2);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m - m_use);
-      m = m_new;
-      float p[8], rsum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = exp2_fast(__builtin_fmaf(x[e], sl2, -m_use));
-        rsum += p[e];
-      }
-      l = l * alpha + rsum;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
-      const bf16x8 pf = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-
-      // V^T staging: row d = 8*c + e, tokens TPL*tg .. +TPL-1
-      {
-        const int tg = lane % NTG, c = lane / NTG;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          __bf16* dst = vt + (8 * c + e) * kVTS + TPL * tg;
-          if constexpr (TPL == 4) {
-            uint2 w;
-            w.x = half16(cur.vr[0], e) | (half16(cur.vr[1], e) << 16);
-            w.y = half16(cur.vr[2], e) | (half16(cur.vr[3], e) << 16);
-            *reinterpret_cast<uint2*>(dst) = w;
-          } else {
-            uint4 w;
-            w.x = half16(cur.vr[0], e) | (half16(cur.vr[1], e) << 16);
-            w.y = half16(cur.vr[2], e) | (half16(cur.vr[3], e) << 16);
-            w.z = half16(cur.vr[4], e) | (half16(cur.vr[5], e) << 16);
-            w.w = half16(cur.vr[6], e) | (half16(cur.vr[7], e) << 16);
-            *reinterpret_cast<uint4*>(dst) = w;
-          }
-        }
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + (16 * db + hl) * kVTS + 8 * kg);
-        acc[db] = mfma16(vf, pf, acc[db]);
-      }
-      wave_lds_sync();
-      cur = nxt;
+    ra.load(s.slot, 32 * min(st, nsteps - 1), st < nsteps, kbase, vbase, rs, lane);
+    while (st < nsteps) {
+      rb.load(s.slot, 32 * min(st + 4, nsteps - 1), st + 4 < nsteps, kbase, vbase, rs, lane);
+      step(ra, 32 * st, nsub);
+      st += 4;
+      if (st >= nsteps) break;
+      ra.load(s.slot, 32 * min(st + 4, nsteps - 1), st + 4 < nsteps, kbase, vbase, rs, lane);
+      step(rb, 32 * st, nsub);
+      st += 4;
     }
     __syncthreads();
   }

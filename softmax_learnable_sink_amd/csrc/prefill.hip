@@ -50,28 +50,37 @@ struct TileRegs {
   static constexpr int VN = (kBN / 2) * CH / kThreads;    // (key pair, chunk) per thread
   uint4 kr[KN];
   uint4 vr[VN][2];
+  uint32_t koff[KN];     // byte offsets inside a tile (loop invariant)
+  uint32_t voff[VN][2];
 
-  __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, size_t rs,
-                                       int key0, int Sk, int tid) {
+  __device__ __forceinline__ void init(size_t rs, int tid) {
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
       const int idx = tid + i * kThreads;
-      const int j = key0 + idx / CH;
-      const int c = idx % CH;
-      kr[i] = j < Sk ? *reinterpret_cast<const uint4*>(kbase + (size_t)j * rs + c * 8)
-                     : make_uint4(0, 0, 0, 0);
+      koff[i] = (uint32_t)(((size_t)(idx / CH) * rs + (idx % CH) * 8) * 2);
     }
 #pragma unroll
     for (int i = 0; i < VN; ++i) {
       // consecutive lanes take consecutive key pairs of one chunk
       const int idx = tid + i * kThreads;
-      const int pr = idx % (kBN / 2);
-      const int c = idx / (kBN / 2);
-      const int j = key0 + 2 * pr;
-      vr[i][0] = j < Sk ? *reinterpret_cast<const uint4*>(vbase + (size_t)j * rs + c * 8)
-                        : make_uint4(0, 0, 0, 0);
-      vr[i][1] = j + 1 < Sk ? *reinterpret_cast<const uint4*>(vbase + (size_t)(j + 1) * rs + c * 8)
-                            : make_uint4(0, 0, 0, 0);
+      const int pr = idx % (kBN / 2), c = idx / (kBN / 2);
+      voff[i][0] = (uint32_t)(((size_t)(2 * pr) * rs + c * 8) * 2);
+      voff[i][1] = (uint32_t)(((size_t)(2 * pr + 1) * rs + c * 8) * 2);
+    }
+  }
+
+  // Keys key0 .. key0+63 of one KV head; rows at or past Sk read as zero.
+  __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, size_t rs,
+                                       int key0, int Sk) {
+    const uint32_t bytes = (uint32_t)((size_t)(Sk - key0) * rs * 2);
+    const auto kr_ = make_rsrc(kbase + (size_t)key0 * rs, bytes);
+    const auto vr_ = make_rsrc(vbase + (size_t)key0 * rs, bytes);
+#pragma unroll
+    for (int i = 0; i < KN; ++i) kr[i] = buf_load16(kr_, koff[i]);
+#pragma unroll
+    for (int i = 0; i < VN; ++i) {
+      vr[i][0] = buf_load16(vr_, voff[i][0]);
+      vr[i][1] = buf_load16(vr_, voff[i][1]);
     }
   }
 
@@ -146,13 +155,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const int l32 = lane & 31;
 
   const int g = Hq / Hkv;
-  const int groups = g / hpw;  // workgroups per KV head along y
-  const int kvh = blockIdx.y / groups;
-  const int h = kvh * g + (blockIdx.y % groups) * hpw + (wave % hpw);
+  const int groups = g / hpw;  // workgroups per KV head
+  // grid: (head groups, B, row tiles) with the row tile slowest and reversed,
+  // so the tiles with the most keys under a causal mask start first
+  const int kvh = blockIdx.x / groups;
+  const int h = kvh * g + (blockIdx.x % groups) * hpw + (wave % hpw);
   const int rb = wave / hpw;   // row block of this wave inside the workgroup
   const int R = RW * (4 / hpw);
-  const int tile_idx = gridDim.x - 1 - blockIdx.x;  // heaviest causal tiles first
-  const int b = blockIdx.z;
+  const int tile_idx = gridDim.z - 1 - blockIdx.z;
+  const int b = blockIdx.y;
   const int row0 = tile_idx * R;
   const int wrow0 = row0 + rb * RW;
   const int off = Sk - Sq;  // bottom-right alignment
@@ -192,9 +203,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const TileRange tr = tile_range(Sk, p_min, p_max, causal, w1, w2);
   const int ntiles = tr.count();
 
+  // Q and the sink are loaded; start the tile loop with no VMEM load pending so
+  // that the compiler's wait tracking does not hold the first MFMA of every
+  // tile on the prefetch of the next one.
+  __builtin_amdgcn_s_waitcnt(0);
   TileRegs<D> regs;
+  regs.init(rs, tid);
   if (ntiles > 0) {
-    regs.load(kbase, vbase, rs, tr.tile(0) * kBN, Sk, tid);
+    regs.load(kbase, vbase, rs, tr.tile(0) * kBN, Sk);
     regs.store(s, 0, tid);
   }
   __syncthreads();
@@ -202,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     const int key0 = tr.tile(it) * kBN;
-    if (it + 1 < ntiles) regs.load(kbase, vbase, rs, tr.tile(it + 1) * kBN, Sk, tid);
+    if (it + 1 < ntiles) regs.load(kbase, vbase, rs, tr.tile(it + 1) * kBN, Sk);
 
     // ---- S^T = K Q^T : 2 key blocks x QB query blocks of 32x32
     f32x16 st[2][QB];
@@ -233,7 +249,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int j = key0 + 32 * kb + 16 * hh + i;
-            if (!(j < Sk && key_visible(j, p, causal, w1, w2))) st[kb][qb][i] = kNegInf;
+            const bool vis = (j < Sk) & key_visible(j, p, causal, w1, w2);
+            st[kb][qb][i] = vis ? st[kb][qb][i] : kNegInf;
           }
       }
     }
@@ -396,13 +413,13 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   auto* o = static_cast<__bf16*>(a.o);
   if (a.D == 64) {
     const int R = 64 * (4 / hpw);
-    const dim3 grid((a.Sq + R - 1) / R, a.Hkv * (g / hpw), a.B);
+    const dim3 grid(a.Hkv * (g / hpw), a.B, (a.Sq + R - 1) / R);
     prefill_bf16_kernel<64, 2><<<grid, block, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.Sq, a.Sk,
                                                            a.Hq, a.Hkv, hpw, sl2, a.causal, a.w1,
                                                            a.w2);
   } else {
     const int R = 32 * (4 / hpw);
-    const dim3 grid((a.Sq + R - 1) / R, a.Hkv * (g / hpw), a.B);
+    const dim3 grid(a.Hkv * (g / hpw), a.B, (a.Sq + R - 1) / R);
     prefill_bf16_kernel<128, 1><<<grid, block, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.Sq,
                                                             a.Sk, a.Hq, a.Hkv, hpw, sl2, a.causal,
                                                             a.w1, a.w2);
