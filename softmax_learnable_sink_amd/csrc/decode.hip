@@ -26,20 +26,14 @@ namespace attn_sink {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSub = 1024;  // selected tokens whose slots are staged in LDS at once
 constexpr int kVTS = 40;    // V^T staging row stride: 32 tokens + 16 B padding
 
-template <int D>
+constexpr int kSub = 2048;  // selected tokens whose slots are staged in LDS at once
+
+template <int D, int NW>
 struct DecLds {
-  int slot[kSub];
-  union {
-    __bf16 vt[4][D * kVTS];
-    struct {
-      float m[4][16];
-      float l[4][16];
-      float o[4][16][D];
-    } red;
-  } u;
+  int slot[kSub];           // slot of each selected token of the current block
+  __bf16 vt[NW][D * kVTS];  // per-wave V^T staging tiles
 };
 
 template <int D>
@@ -51,28 +45,22 @@ struct KVRegs {
   uint4 vr[TPL];
   uint32_t vvalid;  // bit t: V row t holds a selected token
 
-  // Loads the K rows (score MFMA operand) and V rows (for the transposed LDS
-  // tile) of step tokens base .. base+31.  The instruction stream is the same
-  // for every step: a token without a slot (past the chunk, or a step past the
-  // end when valid == false) reads row 0 of the cache, its K score is masked
-  // and its V row is replaced by zeros when the tile is staged (not here, so
-  // that no register with a load in flight is overwritten).
-  __device__ __forceinline__ void load(const int* slot, int base, bool valid, const __bf16* kbase,
+  // K rows (score MFMA operand) and V rows (for the transposed LDS tile) of
+  // step tokens base .. base+31, slots taken from the LDS slot table (-1 = no
+  // token).  A token without a slot reads row 0 of the cache; its K score is
+  // masked and its V row is replaced by zeros when the tile is staged (not
+  // here, so that no register with a load in flight is overwritten).
+  __device__ __forceinline__ void load(const int* slot, int base, const __bf16* kbase,
                                        const __bf16* vbase, size_t rs, int lane) {
     const int kg = lane >> 4, r = lane & 15;
     const int tg = lane % NTG, c = lane / NTG;
     int ks[2], vs[TPL];
 #pragma unroll
-    for (int G = 0; G < 2; ++G) {
+    for (int G = 0; G < 2; ++G)
       // MFMA row r of token group G holds token 8*(r/4) + 4*G + r%4 of the step
-      const int sl = slot[base + 8 * (r >> 2) + 4 * G + (r & 3)];
-      ks[G] = valid ? sl : -1;
-    }
+      ks[G] = slot[base + 8 * (r >> 2) + 4 * G + (r & 3)];
 #pragma unroll
-    for (int t = 0; t < TPL; ++t) {
-      const int sl = slot[base + TPL * tg + t];
-      vs[t] = valid ? sl : -1;
-    }
+    for (int t = 0; t < TPL; ++t) vs[t] = slot[base + TPL * tg + t];
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       const __bf16* row = kbase + (size_t)max(ks[G], 0) * rs + 8 * kg;
@@ -104,18 +92,25 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(
+// Grid (ceil(units / NW), splits, B), NW waves per workgroup.  A unit is one
+// KV head and up to 16 of its query heads; wave w owns unit blockIdx.x*NW + w
+// and walks every token of the workgroup's chunk, so the NW waves of a
+// workgroup read adjacent heads' slices of the same token rows together and
+// share one slot table.  Each wave writes its own partials.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seqlens, float* __restrict__ part,
     int Hq, int Hkv, int hgroups, int page_shift, int max_pages, float sl2, int w1, int w2,
     int chunk, int max_splits) {
-  __shared__ DecLds<D> s;
+  __shared__ DecLds<D, NW> s;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int kg = lane >> 4, hl = lane & 15;
-  const int split = blockIdx.x, b = blockIdx.z;
-  const int kvh = blockIdx.y / hgroups, hgi = blockIdx.y % hgroups;
+  const int split = blockIdx.y, b = blockIdx.z;
+  const int unit = blockIdx.x * NW + wave;
+  const bool active = unit < Hkv * hgroups;
+  const int kvh = active ? unit / hgroups : 0, hgi = active ? unit % hgroups : 0;
   const int g = Hq / Hkv;
   const int g_eff = min(16, g - 16 * hgi);
   const int h0 = kvh * g + 16 * hgi;
@@ -133,9 +128,9 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
   bf16x8 qf[D / 32];
 #pragma unroll
   for (int s2 = 0; s2 < D / 32; ++s2)
-    qf[s2] = hl < g_eff ? *reinterpret_cast<const bf16x8*>(q + ((size_t)b * Hq + h0 + hl) * D +
-                                                           32 * s2 + 8 * kg)
-                        : bf16x8{};
+    qf[s2] = (active && hl < g_eff)
+                 ? *reinterpret_cast<const bf16x8*>(q + ((size_t)b * Hq + h0 + hl) * D + 32 * s2 + 8 * kg)
+                 : bf16x8{};
 
   float m = kNegInf, l = 0.f;
   f32x4 acc[D / 16];
@@ -143,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
   for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{};
 
   constexpr int TPL = KVRegs<D>::TPL, NTG = KVRegs<D>::NTG;
-  __bf16* vt = s.u.vt[wave];
+  __bf16* vt = s.vt[wave];
   __builtin_amdgcn_s_waitcnt(0);
 
   // One 32-token step of this wave: scores, online softmax, V^T staging, P.V.
@@ -212,57 +207,44 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
 
   for (int sub0 = u0; sub0 < u1; sub0 += kSub) {
     const int nsub = min(kSub, u1 - sub0);
-    for (int x = tid; x < kSub; x += kThreads)
+    const int nsteps = (nsub + 31) >> 5;
+    // slot table of this block, padded with -1 up to an even number of steps
+    const int npad = min(kSub, 64 * ((nsteps + 1) >> 1));
+    for (int x = tid; x < npad; x += 64 * NW)
       s.slot[x] = x < nsub ? slot_of(bt_row, token_of(sub0 + x, L, w1, w2), page_shift) : -1;
     __syncthreads();
-    const int nsteps = (nsub + 31) >> 5;
-    // two register sets in turn: the loads of the next step stay in flight
-    // while the current one is computed
-    KVRegs<D> ra, rb;
-    int st = wave;
-    ra.load(s.slot, 32 * min(st, nsteps - 1), st < nsteps, kbase, vbase, rs, lane);
-    while (st < nsteps) {
-      rb.load(s.slot, 32 * min(st + 4, nsteps - 1), st + 4 < nsteps, kbase, vbase, rs, lane);
-      step(ra, 32 * st, nsub);
-      st += 4;
-      if (st >= nsteps) break;
-      ra.load(s.slot, 32 * min(st + 4, nsteps - 1), st + 4 < nsteps, kbase, vbase, rs, lane);
-      step(rb, 32 * st, nsub);
-      st += 4;
+    if (active) {
+      // Two register sets in turn, two steps per iteration with no exit in
+      // between (so the compiler cannot sink the prefetch below a branch); an
+      // odd last step runs on padding slots and is fully masked.
+      // sched_barrier keeps each prefetch issued ahead of the step it overlaps
+      KVRegs<D> ra, rb;
+      ra.load(s.slot, 0, kbase, vbase, rs, lane);
+      for (int st = 0; st < nsteps; st += 2) {
+        rb.load(s.slot, 32 * (st + 1), kbase, vbase, rs, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        step(ra, 32 * st, nsub);
+        ra.load(s.slot, 32 * min(st + 2, ((npad >> 5) - 1)), kbase, vbase, rs, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        step(rb, 32 * (st + 1), nsub);
+      }
     }
     __syncthreads();
   }
+  if (!active) return;
 
-  // ---- merge the 4 waves (each holds head hl, d = 16*db + 4*kg + j)
+  // ---- partial (acc, m, l) of this wave's heads: lane (kg, hl) holds head hl,
+  // d = 16*db + 4*kg + j
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (kg == 0) {
-    s.u.red.m[wave][hl] = m;
-    s.u.red.l[wave][hl] = l;
-  }
+  if (hl < g_eff) {
+    float* dst = part + (((size_t)b * Hq + h0 + hl) * max_splits + split) * (D + 2);
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s.u.red.o[wave][hl][16 * db + 4 * kg + j] = acc[db][j];
-  __syncthreads();
-  for (int x2 = tid; x2 < 16 * D; x2 += kThreads) {
-    const int hh = x2 / D, d = x2 % D;
-    if (hh >= g_eff) break;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s.u.red.m[w][hh]);
-    float od = 0.f, lw = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = exp2_fast(s.u.red.m[w][hh] - M);
-      od += f * s.u.red.o[w][hh][d];
-      lw += f * s.u.red.l[w][hh];
-    }
-    float* dst = part + (((size_t)b * Hq + h0 + hh) * max_splits + split) * (D + 2);
-    dst[d] = od;
-    if (d == 0) {
-      dst[D] = M;
-      dst[D + 1] = lw;
+    for (int db = 0; db < D / 16; ++db)
+      *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * kg) = acc[db];
+    if (kg == 0) {
+      dst[D] = m;
+      dst[D + 1] = l;
     }
   }
 }
@@ -380,22 +362,26 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pag
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   const int g = a.Hq / a.Hkv;
   const int hgroups = (g + 15) / 16;
+  const int units = a.Hkv * hgroups;
   const int page_shift = log2_exact(a.page_size);
   const float sl2 = a.scale * kLog2e;
   const auto* q = static_cast<const __bf16*>(a.q);
   const auto* kc = static_cast<const __bf16*>(a.k_cache);
   const auto* vc = static_cast<const __bf16*>(a.v_cache);
   auto* o = static_cast<__bf16*>(a.o);
-  const dim3 grid(a.max_splits, a.Hkv * hgroups, a.B);
   const dim3 cgrid((a.B * a.Hq + 3) / 4);
   if (a.D == 64) {
-    decode_partial_kernel<64><<<grid, kThreads, 0, stream>>>(
+    constexpr int NW = 4;
+    const dim3 grid((units + NW - 1) / NW, a.max_splits, a.B);
+    decode_partial_kernel<64, NW><<<grid, 64 * NW, 0, stream>>>(
         q, kc, vc, a.block_table, a.seqlens, a.partials, a.Hq, a.Hkv, hgroups, page_shift,
         a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits);
     decode_combine_kernel<64><<<cgrid, kThreads, 0, stream>>>(
         a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits);
   } else {
-    decode_partial_kernel<128><<<grid, kThreads, 0, stream>>>(
+    constexpr int NW = 4;
+    const dim3 grid((units + NW - 1) / NW, a.max_splits, a.B);
+    decode_partial_kernel<128, NW><<<grid, 64 * NW, 0, stream>>>(
         q, kc, vc, a.block_table, a.seqlens, a.partials, a.Hq, a.Hkv, hgroups, page_shift,
         a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits);
     decode_combine_kernel<128><<<cgrid, kThreads, 0, stream>>>(
