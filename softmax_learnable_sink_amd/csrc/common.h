@@ -65,6 +65,20 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// max(x, x of lane ^ 32) without an LDS round trip.  v_permlane32_swap swaps
+// the upper half of its first operand with the lower half of its second; fed
+// two copies of x it leaves, per lane, x and its partner's x (in some order).
+// Written as one asm block: the compiler's own folding of the builtin's two
+// results is not reliable when both operands hold the same value.  The s_nops
+// give the permlane the wait states it needs around the VALU copy.
+__device__ __forceinline__ float max_xor32(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b;
+  asm("v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(a), "=&v"(b));
+  return __builtin_bit_cast(float, a);
+}
+
 __device__ __forceinline__ float wave_max_xor(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, 64));
 }

@@ -237,7 +237,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       }
     }
 
-    // ---- mask (only on tiles that straddle a boundary)
+    // ---- mask (only on tiles that straddle a boundary).  Per lane and key
+    // block, element i (key j = base + i) is visible iff i <= hi (causal bound
+    // and j < Sk) and, with a window, i < a (first window) or i > b (last).
     const bool need_mask = (key0 + kBN > Sk) || (causal && key0 + kBN - 1 > p_min) ||
                            (w2 > 0 && key0 + kBN - 1 >= w1 && key0 <= p_max - w2);
     if (need_mask) {
@@ -245,13 +247,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       for (int qb = 0; qb < QB; ++qb) {
         const int p = off + wrow0 + 32 * qb + l32;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+          const int base = key0 + 32 * kb + 16 * hh;
+          const int hi = min(causal ? p - base : 15, Sk - 1 - base);
+          if (w2 > 0) {
+            const int a = w1 - base, bnd = p - w2 - base;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = key0 + 32 * kb + 16 * hh + i;
-            const bool vis = (j < Sk) & key_visible(j, p, causal, w1, w2);
-            st[kb][qb][i] = vis ? st[kb][qb][i] : kNegInf;
+            for (int i = 0; i < 16; ++i) {
+              const bool vis = (i <= hi) & ((i < a) | (i > bnd));
+              st[kb][qb][i] = vis ? st[kb][qb][i] : kNegInf;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st[kb][qb][i] = i <= hi ? st[kb][qb][i] : kNegInf;
           }
+        }
       }
     }
 
@@ -264,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb][qb][i]);
-      mx = wave_max_xor(mx, 32);
+      mx = max_xor32(mx);
       const float m_new = fmaxf(m[qb], mx * sl2);
       const float m_use = m_new == kNegInf ? 0.f : m_new;
       const float alpha = exp2_fast(m[qb] - m_use);
@@ -279,8 +289,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
           rsum += p;
         }
       l[qb] = l[qb] * alpha + rsum;
+      // alpha == 1 exactly when no row of this block's max grew
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db][qb] *= alpha;
+        for (int db = 0; db < D / 32; ++db) acc[db][qb] *= alpha;
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
