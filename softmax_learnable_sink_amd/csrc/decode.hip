@@ -224,7 +224,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
         rb.load(s.slot, 32 * (st + 1), kbase, vbase, rs, lane);
         __builtin_amdgcn_sched_barrier(0);
         step(ra, 32 * st, nsub);
-        ra.load(s.slot, 32 * min(st + 2, ((npad >> 5) - 1)), kbase, vbase, rs, lane);
+        ra.load(s.slot, 32 * min(st + 2, npad / 32 - 1), kbase, vbase, rs, lane);
         __builtin_amdgcn_sched_barrier(0);
         step(rb, 32 * (st + 1), nsub);
       }
@@ -266,28 +266,48 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
   const float* base = part + (size_t)bh * max_splits * (D + 2);
   const float sig2 = sink ? sink[h] * kLog2e : kNegInf;
 
+  // pass 1: lane k reads chunk k's (m, l); the max and the weighted sum of l
+  // are wave reductions, so no load waits on another
   float M = sig2;
   for (int k = lane; k < nsp; k += 64) M = fmaxf(M, base[(size_t)k * (D + 2) + D]);
 #pragma unroll
   for (int x = 32; x >= 1; x >>= 1) M = wave_max_xor(M, x);
+  const float Mu = M == kNegInf ? 0.f : M;  // nothing visible and no sink
+  float z = 0.f;
+  for (int k = lane; k < nsp; k += 64) {
+    const float* pk = base + (size_t)k * (D + 2);
+    z += exp2_fast(pk[D] - Mu) * pk[D + 1];
+  }
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) z += __shfl_xor(z, x, 64);
 
+  // pass 2: lane = d; chunks in groups of 8 with all loads issued first
   constexpr int DPL = D / 64;
   float od[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) od[i] = 0.f;
-  float z = 0.f;
-  for (int k = 0; k < nsp; ++k) {
-    const float* pk = base + (size_t)k * (D + 2);
-    const float f = exp2_fast(pk[D] - M);
-    z += f * pk[D + 1];
+  for (int k0 = 0; k0 < nsp; k0 += 8) {
+    float mk[8], ak[8][DPL];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) od[i] += f * pk[lane + 64 * i];
+    for (int j = 0; j < 8; ++j) {
+      const int k = min(k0 + j, nsp - 1);
+      const float* pk = base + (size_t)k * (D + 2);
+      mk[j] = k0 + j < nsp ? pk[D] : kNegInf;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) ak[j][i] = pk[lane + 64 * i];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = exp2_fast(mk[j] - Mu);  // 0 for chunks past the end
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) od[i] += f * ak[j][i];
+    }
   }
-  if (sig2 != kNegInf) z += exp2_fast(sig2 - M);
+  if (sig2 != kNegInf) z += exp2_fast(sig2 - Mu);
   const float inv = z > 0.f ? 1.f / z : 0.f;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) o[(size_t)bh * D + lane + 64 * i] = (__bf16)(od[i] * inv);
-  if (lse && lane == 0) lse[bh] = z > 0.f ? (M + log2_fast(z)) * kLn2 : kNegInf;
+  if (lse && lane == 0) lse[bh] = z > 0.f ? (Mu + log2_fast(z)) * kLn2 : kNegInf;
 }
 
 __global__ void select_slots_kernel(const int32_t* __restrict__ bt,
@@ -348,8 +368,15 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pag
     chunk = (max_sel + num_splits - 1) / num_splits;
     chunk = (chunk + 31) / 32 * 32;
   } else {
-    chunk = 1024;
-    while (chunk > 128 && units * ((max_sel + chunk - 1) / chunk) < 2048) chunk /= 2;
+    // Long chunks amortise each workgroup's start (slot table, first loads);
+    // shorter ones only when long ones leave too few waves in flight.  The
+    // starting lengths (1024 tokens at D = 64, 2048 at D = 128) are measured
+    // optima on the paged and the windowed decode workloads.
+    chunk = D == 64 ? 1024 : 2048;
+    if (units * ((max_sel + chunk - 1) / chunk) < 1024) {
+      chunk = 1024;
+      while (chunk > 128 && units * ((max_sel + chunk - 1) / chunk) < 2048) chunk /= 2;
+    }
   }
   if (chunk < 32) chunk = 32;
   p.chunk = (int)chunk;
