@@ -39,27 +39,79 @@ def causal_pairs(B, Hq, Sq, Sk):
     return B * Hq * per_head
 
 
-def kernel_source_hash():
+KERNEL_SOURCES = {  # sources each measured kernel is compiled from
+    "prefill": ("prefill.hip", "common.h", "launch.h"),
+    "decode": ("decode.hip", "common.h", "launch.h"),
+}
+
+
+def kernel_source_hash(which):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "softmax_learnable_sink_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[which]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_hash):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources (else None)."""
+TRAFFIC_KERNELS = {  # key in hbm_traffic.json -> (kernel-name substring, source set)
+    "prefill_bf16_kernel": ("prefill_bf16_kernelILi64ELi2", "prefill"),
+    "decode_partial_kernel": ("decode_partial_kernelILi64", "decode"),
+    "decode_combine_kernel": ("decode_combine_kernelILi64", "decode"),
+    "decode_partial_kernel_d128": ("decode_partial_kernelILi128", "decode"),
+}
+
+
+def write_traffic(fetch_csv, write_csv, probe_mib):
+    """profiles/hbm_traffic.json from two rocprofv3 counter runs (FETCH_SIZE,
+    then WRITE_SIZE, both in KiB per dispatch) of `bench.py --copy-probe-mib N`.
+    Each counter is scaled by bytes / counter of the plain N MiB device copy in
+    the same run, so the figures are HBM bytes per launch."""
+    import csv
+    probe = probe_mib << 20
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {"source_hash": {k: kernel_source_hash(k) for k in KERNEL_SOURCES},
+           "probe_bytes": probe, "bytes_per_launch": {}, "raw_kib_per_launch": {}}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_kernel(path, counter)
+        copies = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs]
+        ref = max(copies)  # the probe copy is the largest copy of the run
+        out[counter.lower() + "_scale"] = probe / (ref * 1024.0)
+        for key, (sub, _) in TRAFFIC_KERNELS.items():
+            vs = [v for k, v_ in vals.items() if sub in k for v in v_]
+            if vs:
+                kib = sum(vs) / len(vs)
+                out["raw_kib_per_launch"].setdefault(key, {})[counter] = kib
+                b = kib * 1024.0 * out[counter.lower() + "_scale"]
+                out["bytes_per_launch"][key] = out["bytes_per_launch"].get(key, 0) + b
+    for key in out["bytes_per_launch"]:
+        out["bytes_per_launch"][key] = int(out["bytes_per_launch"][key])
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed counter summary, for each kernel
+    whose sources are unchanged since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return {}
-    if data.get("kernel_source_hash") != kernel_hash:
-        return {}
-    return data.get("bytes_per_launch", {})
+    taken = data.get("source_hash", {})
+    return {key: b for key, b in data.get("bytes_per_launch", {}).items()
+            if taken.get(TRAFFIC_KERNELS[key][1]) == kernel_source_hash(TRAFFIC_KERNELS[key][1])}
 
 
 class Workloads:
@@ -84,7 +136,9 @@ class Workloads:
             self.pf["o"] = torch.empty_like(self.pf["q"])
             self.pf["lse"] = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
             pairs = causal_pairs(B, Hq, S, S)
-            self.info["prefill"] = dict(flops=4 * D * pairs, pairs=pairs,
+            # Q, K, V in and O out (bf16), LSE out (fp32), sink in
+            io = 2 * (2 * B * S * Hq * D + 2 * B * S * Hkv * D) + 4 * B * Hq * S + 4 * Hq
+            self.info["prefill"] = dict(flops=4 * D * pairs, pairs=pairs, bytes=io,
                                         shape=f"B{B} S{S} H{Hq}/{Hkv} D{D} causal bf16")
             self.pf_case = c
         for name, spec in (("decode", (64, 64, 8, 64, 1024, 32768, None)),
@@ -204,7 +258,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from the counter_collection.csv of a "
+                         "FETCH_SIZE and a WRITE_SIZE rocprofv3 run made with --copy-probe-mib, "
+                         "then exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib or 1024)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the sink-attention path has no multi-GPU code)", file=sys.stderr)
@@ -256,8 +317,7 @@ def main():
     wall = time.perf_counter() - t0
     ms = {p: sum(a.elapsed_time(b) for a, b in events[p]) / max(1, args.steps) for p in parts}
 
-    khash = kernel_source_hash()
-    traffic = load_traffic(khash)
+    traffic = load_traffic()
     out = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / max(1, args.steps), 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -285,7 +345,7 @@ def main():
         out["roofline"] = {"bound": "mfma", "achieved": pf["tflops"], "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": pf["mfma_frac"],
                            "traffic": tb, "kernel": "prefill_bf16_kernel<64,2>",
-                           "kernel_source_hash": khash}
+                           "algorithmic_bytes": wl.info["prefill"]["bytes"]}
     if "decode" in parts:
         dc = parts_out["decode"]
         out["decode_gbps"] = dc["gbps"]
