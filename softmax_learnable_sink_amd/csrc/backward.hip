@@ -18,6 +18,8 @@
 //   bwd_dq           Q-stationary (the forward's frame): recomputes S and dP
 //                    and accumulates dQ in registers
 //   bwd_dsink_reduce fixed-order sum of the dSink partials
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -181,8 +183,8 @@ struct DkdvLds {
   __bf16 dO[2][kTile * (D + kPad)];
   __bf16 qt[2][D * (kTile + kPad)];
   __bf16 dOt[2][D * (kTile + kPad)];
-  float lse2[2][kTile];
-  float di[2][kTile];
+  alignas(16) float lse2[2][kTile];
+  alignas(16) float di[2][kTile];
 };
 
 template <int D>
@@ -276,45 +278,67 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const bool need_mask = (i0 + kTile > Sq) || (causal && p0 < k1 - 1) ||
                            (w2 > 0 && k1 - 1 >= w1 && p0 + kTile - 1 - w2 >= k0);
 
-    // one 32-row block at a time keeps the live registers low
+    // S and dP of both 32-row blocks first (four independent MFMA chains)
+    f32x16 sa[2], pa[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 sa = f32x16{}, pa = f32x16{};
+      sa[qb] = f32x16{};
+      pa[qb] = f32x16{};
+    }
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
         const int r = (32 * qb + l32) * NS + 16 * ks + 8 * hh;
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&s.q[buf][r]);
         const bf16x8 da = *reinterpret_cast<const bf16x8*>(&s.dO[buf][r]);
-        sa = mfma32(qa, kf[ks], sa);
-        pa = mfma32(da, vf[ks], pa);
+        sa[qb] = mfma32(qa, kf[ks], sa[qb]);
+        pa[qb] = mfma32(da, vf[ks], pa[qb]);
       }
-      const int rbase = 32 * qb + 16 * hh;
-      float pv[16], dsv[16];
+
+    // P = 2^(S sl2 - LSE log2 e), dS = P (dP - Di), rounded to bf16 operands.
+    // Lane (hh, l32): key l32, rows 32*qb + 16*hh + i.  The mask is applied
+    // on one of two straight-line paths chosen once per tile.
+    bf16x8 pb[2][2], sb[2][2];
+    auto softmax_grad = [&](auto masked) {
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(&s.lse2[buf][rbase + 4 * c4]);
-        const f32x4 d2 = *reinterpret_cast<const f32x4*>(&s.di[buf][rbase + 4 * c4]);
+      for (int qb = 0; qb < 2; ++qb) {
+        const int rbase = 32 * qb + 16 * hh;
+        float pv[16], dsv[16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * c4 + e;
-          float p = exp2_fast(__builtin_fmaf(sa[i], sl2, -a[e]));
-          if (need_mask) {
-            const int row = i0 + rbase + i;
-            const bool ok = (row < Sq) & (key < Sk) & key_visible(key, off + row, causal, w1, w2);
-            p = ok ? p : 0.f;
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&s.lse2[buf][rbase + 4 * c4]);
+          const f32x4 d2 = *reinterpret_cast<const f32x4*>(&s.di[buf][rbase + 4 * c4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * c4 + e;
+            float p = exp2_fast(__builtin_fmaf(sa[qb][i], sl2, -a[e]));
+            if constexpr (decltype(masked)::value) {
+              const int row = i0 + rbase + i;
+              const bool ok = (row < Sq) & (key < Sk) & key_visible(key, off + row, causal, w1, w2);
+              p = ok ? p : 0.f;
+            }
+            pv[i] = p;
+            dsv[i] = p * (pa[qb][i] - d2[e]);
           }
-          pv[i] = p;
-          dsv[i] = p * (pa[i] - d2[e]);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          pb[qb][c] = to_bf16x8(pv[8 * c], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3],
+                                pv[8 * c + 4], pv[8 * c + 5], pv[8 * c + 6], pv[8 * c + 7]);
+          sb[qb][c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
+                                dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
         }
       }
-      bf16x8 pb[2], sb[2];
+    };
+    if (need_mask)
+      softmax_grad(std::true_type{});
+    else
+      softmax_grad(std::false_type{});
+
+    // dV^T += dO^T P, dK^T += Q^T dS
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        pb[c] = to_bf16x8(pv[8 * c], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3], pv[8 * c + 4],
-                          pv[8 * c + 5], pv[8 * c + 6], pv[8 * c + 7]);
-        sb[c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
-                          dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
-      }
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int d = 32 * db + l32;
@@ -323,11 +347,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
           const int col = 32 * qb + 16 * hh + 8 * c;
           const bf16x8 dot = *reinterpret_cast<const bf16x8*>(&s.dOt[buf][d * TS + col]);
           const bf16x8 qt = *reinterpret_cast<const bf16x8*>(&s.qt[buf][d * TS + col]);
-          dva[db] = mfma32(dot, pb[c], dva[db]);
-          dka[db] = mfma32(qt, sb[c], dka[db]);
+          dva[db] = mfma32(dot, pb[qb][c], dva[db]);
+          dka[db] = mfma32(qt, sb[qb][c], dka[db]);
         }
       }
-    }
 
     if (it + 1 < niter) store_iter(buf ^ 1);
     __syncthreads();
