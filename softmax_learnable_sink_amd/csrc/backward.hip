@@ -414,7 +414,7 @@ __device__ __forceinline__ QRange kv_tiles(int Sk, int p_min, int p_max, int cau
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
     __bf16* __restrict__ dq, int Sq, int Sk, int Hq, int Hkv, int hpw, float scale, float sl2,
@@ -505,25 +505,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(
     const bool need_mask = (key0 + kTile > Sk) || (causal && key0 + kTile - 1 > p_min) ||
                            (w2 > 0 && key0 + kTile - 1 >= w1 && key0 <= p_max - w2) ||
                            (row0 + R > Sq);
+    // dS^T = P^T (dP^T - Di); the mask is applied on one of two straight-line
+    // paths chosen once per tile
     bf16x8 sb[2][2];
+    auto grad_scores = [&](auto masked) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float dsv[16];
+      for (int kb = 0; kb < 2; ++kb) {
+        float dsv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pr = exp2_fast(__builtin_fmaf(st[kb][i], sl2, -lse2));
-        if (need_mask) {
-          const int j = key0 + 32 * kb + 16 * hh + i;
-          const bool ok = (row < Sq) & (j < Sk) & key_visible(j, p, causal, w1, w2);
-          pr = ok ? pr : 0.f;
+        for (int i = 0; i < 16; ++i) {
+          float pr = exp2_fast(__builtin_fmaf(st[kb][i], sl2, -lse2));
+          if constexpr (decltype(masked)::value) {
+            const int j = key0 + 32 * kb + 16 * hh + i;
+            const bool ok = (row < Sq) & (j < Sk) & key_visible(j, p, causal, w1, w2);
+            pr = ok ? pr : 0.f;
+          }
+          dsv[i] = pr * (dp[kb][i] - di_r);
         }
-        dsv[i] = pr * (dp[kb][i] - di_r);
-      }
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        sb[kb][c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
-                              dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
-    }
+        for (int c = 0; c < 2; ++c)
+          sb[kb][c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
+                                dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
+      }
+    };
+    if (need_mask)
+      grad_scores(std::true_type{});
+    else
+      grad_scores(std::false_type{});
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int d = 32 * db + l32;
