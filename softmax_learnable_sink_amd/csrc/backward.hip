@@ -417,22 +417,20 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
-    __bf16* __restrict__ dq, int Sq, int Sk, int Hq, int Hkv, int hpw, float scale, float sl2,
-    int causal, int w1, int w2) {
+    __bf16* __restrict__ dq, int B, int Sq, int Sk, int Hq, int Hkv, int hpw, float scale,
+    float sl2, int causal, int w1, int w2) {
   __shared__ DqLds<D> s;
   constexpr int NS = D + kPad, TS = kTile + kPad;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, l32 = lane & 31;
   const int g = Hq / Hkv;
   const int groups = g / hpw;
-  // grid: (head groups, B, row tiles) with the row tile slowest and reversed,
-  // so the tiles with the most keys under a causal mask start first
-  const int kvh = blockIdx.x / groups;
-  const int h = kvh * g + (blockIdx.x % groups) * hpw + (wave % hpw);
-  const int rb = wave / hpw;
   const int R = 32 * (4 / hpw);
-  const int b = blockIdx.y;
-  const int row0 = (gridDim.z - 1 - blockIdx.z) * R;
+  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R);
+  const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
+  const int h = kvh * g + wi.grp * hpw + (wave % hpw);
+  const int rb = wave / hpw;
+  const int row0 = wi.tile * R;
   const int row = row0 + rb * 32 + l32;
   const int off = Sk - Sq;
   const int p = off + row;
@@ -592,25 +590,25 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
   const dim3 pgrid(nblk, a.Hq, a.B);
   const dim3 kgrid(a.Hkv, a.B, (a.Sk + 127) / 128);
   const int R = 32 * (4 / hpw);
-  const dim3 qgrid(a.Hkv * (g / hpw), a.B, (a.Sq + R - 1) / R);
+  const dim3 qgrid(a.B * a.Hkv * (g / hpw) * ((a.Sq + R - 1) / R));
   if (a.D == 64) {
     bwd_preprocess_kernel<64><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di, part,
                                                               a.Sq, a.Hq);
     bwd_dkdv_kernel<64><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dk, dv, a.Sq,
                                                         a.Sk, a.Hq, a.Hkv, a.scale, sl2, a.causal,
                                                         a.w1, a.w2);
-    bwd_dq_kernel<64><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, a.Sq, a.Sk,
-                                                      a.Hq, a.Hkv, hpw, a.scale, sl2, a.causal,
-                                                      a.w1, a.w2);
+    bwd_dq_kernel<64><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, a.B, a.Sq,
+                                                      a.Sk, a.Hq, a.Hkv, hpw, a.scale, sl2,
+                                                      a.causal, a.w1, a.w2);
   } else {
     bwd_preprocess_kernel<128><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di, part,
                                                                a.Sq, a.Hq);
     bwd_dkdv_kernel<128><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dk, dv, a.Sq,
                                                          a.Sk, a.Hq, a.Hkv, a.scale, sl2,
                                                          a.causal, a.w1, a.w2);
-    bwd_dq_kernel<128><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, a.Sq, a.Sk,
-                                                       a.Hq, a.Hkv, hpw, a.scale, sl2, a.causal,
-                                                       a.w1, a.w2);
+    bwd_dq_kernel<128><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, a.B, a.Sq,
+                                                       a.Sk, a.Hq, a.Hkv, hpw, a.scale, sl2,
+                                                       a.causal, a.w1, a.w2);
   }
   if (a.sink && a.dsink)
     bwd_dsink_reduce_kernel<<<(a.Hq + 63) / 64, 64, 0, stream>>>(part, a.dsink, a.B, a.Hq, nblk);

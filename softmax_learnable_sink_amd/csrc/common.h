@@ -83,6 +83,32 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, 64));
 }
 
+// Workgroup -> (batch x KV head pair, head group, row tile).  The row tile
+// runs backwards so that the tiles with the most keys under a causal mask
+// start first.  Workgroups are handed to the 8 XCDs round robin by id; when
+// the pair count is a multiple of 8, each XCD gets its own pairs and walks
+// them one after another (all row tiles and head groups of a pair together),
+// so the K/V a pair's workgroups share stays in that XCD's L2.
+struct WorkItem {
+  int pair, grp, tile;
+};
+__device__ __forceinline__ WorkItem work_item(int w, int npairs, int groups, int ntiles) {
+  constexpr int kXcds = 8;
+  int pair, grp, z;
+  if (npairs % kXcds == 0) {
+    const int local = w / kXcds, per_pair = groups * ntiles;
+    pair = (w % kXcds) * (npairs / kXcds) + local / per_pair;
+    z = (local % per_pair) / groups;
+    grp = local % groups;
+  } else {
+    const int col = w % (npairs * groups);
+    pair = col / groups;
+    grp = col % groups;
+    z = w / (npairs * groups);
+  }
+  return WorkItem{pair, grp, ntiles - 1 - z};
+}
+
 // ---------------------------------------------------------------------------
 // Visibility and the first/last-window selection (sglang PR #12504 "To
 // implement attention-sink": keep the first W1 and the last W2 tokens of each

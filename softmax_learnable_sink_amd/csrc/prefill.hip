@@ -144,7 +144,7 @@ __device__ __forceinline__ TileRange tile_range(int Sk, int p_min, int p_max, in
 template <int D, int QB>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int Sq,
+    const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int B, int Sq,
     int Sk, int Hq, int Hkv, int hpw, float sl2, int causal, int w1, int w2) {
   __shared__ Lds<D> s;
   constexpr int RW = 32 * QB;  // query rows per wave
@@ -156,14 +156,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 
   const int g = Hq / Hkv;
   const int groups = g / hpw;  // workgroups per KV head
-  // grid: (head groups, B, row tiles) with the row tile slowest and reversed,
-  // so the tiles with the most keys under a causal mask start first
-  const int kvh = blockIdx.x / groups;
-  const int h = kvh * g + (blockIdx.x % groups) * hpw + (wave % hpw);
-  const int rb = wave / hpw;   // row block of this wave inside the workgroup
   const int R = RW * (4 / hpw);
-  const int tile_idx = gridDim.z - 1 - blockIdx.z;
-  const int b = blockIdx.y;
+  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R);
+  const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
+  const int h = kvh * g + wi.grp * hpw + (wave % hpw);
+  const int rb = wave / hpw;   // row block of this wave inside the workgroup
+  const int tile_idx = wi.tile;
   const int row0 = tile_idx * R;
   const int wrow0 = row0 + rb * RW;
   const int off = Sk - Sq;  // bottom-right alignment
@@ -424,18 +422,19 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   const auto* k = static_cast<const __bf16*>(a.k);
   const auto* v = static_cast<const __bf16*>(a.v);
   auto* o = static_cast<__bf16*>(a.o);
+  const int cols = a.B * a.Hkv * (g / hpw);
   if (a.D == 64) {
     const int R = 64 * (4 / hpw);
-    const dim3 grid(a.Hkv * (g / hpw), a.B, (a.Sq + R - 1) / R);
-    prefill_bf16_kernel<64, 2><<<grid, block, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.Sq, a.Sk,
-                                                           a.Hq, a.Hkv, hpw, sl2, a.causal, a.w1,
-                                                           a.w2);
+    const dim3 grid(cols * ((a.Sq + R - 1) / R));
+    prefill_bf16_kernel<64, 2><<<grid, block, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.B, a.Sq,
+                                                           a.Sk, a.Hq, a.Hkv, hpw, sl2, a.causal,
+                                                           a.w1, a.w2);
   } else {
     const int R = 32 * (4 / hpw);
-    const dim3 grid(a.Hkv * (g / hpw), a.B, (a.Sq + R - 1) / R);
-    prefill_bf16_kernel<128, 1><<<grid, block, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.Sq,
-                                                            a.Sk, a.Hq, a.Hkv, hpw, sl2, a.causal,
-                                                            a.w1, a.w2);
+    const dim3 grid(cols * ((a.Sq + R - 1) / R));
+    prefill_bf16_kernel<128, 1><<<grid, block, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.B,
+                                                            a.Sq, a.Sk, a.Hq, a.Hkv, hpw, sl2,
+                                                            a.causal, a.w1, a.w2);
   }
   return hipGetLastError();
 }
