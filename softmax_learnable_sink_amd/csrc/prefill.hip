@@ -30,86 +30,87 @@ constexpr int kThreads = 256;  // 4 waves of 64
 // keys 16h .. 16h+15 of the block, in order, into accumulator half h.
 __device__ __forceinline__ int k_lds_row(int j) { return ((j & 15) >> 2) * 8 + (j >> 4) * 4 + (j & 3); }
 
-// V is stored transposed, [d][key], rows padded by 16 bytes: the transposed
-// writes of one wave cover 32 consecutive key pairs of one row, and the
-// 16-byte reads of 8 consecutive rows start 4 banks apart.
-__device__ __forceinline__ int vt_col(int pair) { return 2 * pair; }
-
 template <int D>
 struct Lds {
-  static constexpr int KS = D + 8;  // K row stride (elements), 16 B of padding
-  static constexpr int VS = kBN + 8; // V^T row stride (elements), 16 B of padding
+  static constexpr int KS = D + 8;   // K row stride (elements), 16 B of padding
+  static constexpr int VS = D + 8;   // V row stride (elements), 16 B of padding
   __bf16 k[2][kBN * KS];
-  __bf16 vt[2][D * VS];
+  __bf16 v[2][kBN * VS];             // natural [key][d]; read transposed (ds_read_b64_tr_b16)
 };
 
 template <int D>
 struct TileRegs {
+  static constexpr int NT = kThreads;
   static constexpr int CH = D / 8;                        // 16-byte chunks per row
-  static constexpr int KN = kBN * CH / kThreads;          // K chunks per thread
-  static constexpr int VN = (kBN / 2) * CH / kThreads;    // (key pair, chunk) per thread
+  static constexpr int KN = kBN * CH / NT;                // K (and V) chunks per thread
   uint4 kr[KN];
-  uint4 vr[VN][2];
-  uint32_t koff[KN];     // byte offsets inside a tile (loop invariant)
-  uint32_t voff[VN][2];
+  uint4 vr[KN];
+  uint32_t off[KN];      // byte offsets inside a tile (loop invariant)
 
   __device__ __forceinline__ void init(size_t rs, int tid) {
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
-      const int idx = tid + i * kThreads;
-      koff[i] = (uint32_t)(((size_t)(idx / CH) * rs + (idx % CH) * 8) * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < VN; ++i) {
-      // consecutive lanes take consecutive key pairs of one chunk
-      const int idx = tid + i * kThreads;
-      const int pr = idx % (kBN / 2), c = idx / (kBN / 2);
-      voff[i][0] = (uint32_t)(((size_t)(2 * pr) * rs + c * 8) * 2);
-      voff[i][1] = (uint32_t)(((size_t)(2 * pr + 1) * rs + c * 8) * 2);
+      const int idx = tid + i * NT;
+      off[i] = (uint32_t)(((size_t)(idx / CH) * rs + (idx % CH) * 8) * 2);
     }
   }
 
   // Keys key0 .. key0+63 of one KV head; rows at or past Sk read as zero.
+  __device__ __forceinline__ void load_k(const __bf16* kbase, size_t rs, int key0, int Sk) {
+    const auto r = make_rsrc(kbase + (size_t)key0 * rs, (uint32_t)((size_t)(Sk - key0) * rs * 2));
+#pragma unroll
+    for (int i = 0; i < KN; ++i) kr[i] = buf_load16(r, off[i]);
+  }
+  __device__ __forceinline__ void load_v(const __bf16* vbase, size_t rs, int key0, int Sk) {
+    const auto r = make_rsrc(vbase + (size_t)key0 * rs, (uint32_t)((size_t)(Sk - key0) * rs * 2));
+#pragma unroll
+    for (int i = 0; i < KN; ++i) vr[i] = buf_load16(r, off[i]);
+  }
   __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, size_t rs,
                                        int key0, int Sk) {
-    const uint32_t bytes = (uint32_t)((size_t)(Sk - key0) * rs * 2);
-    const auto kr_ = make_rsrc(kbase + (size_t)key0 * rs, bytes);
-    const auto vr_ = make_rsrc(vbase + (size_t)key0 * rs, bytes);
-#pragma unroll
-    for (int i = 0; i < KN; ++i) kr[i] = buf_load16(kr_, koff[i]);
-#pragma unroll
-    for (int i = 0; i < VN; ++i) {
-      vr[i][0] = buf_load16(vr_, voff[i][0]);
-      vr[i][1] = buf_load16(vr_, voff[i][1]);
-    }
+    load_k(kbase, rs, key0, Sk);
+    load_v(vbase, rs, key0, Sk);
   }
 
-  __device__ __forceinline__ void store(Lds<D>& s, int buf, int tid) {
+  __device__ __forceinline__ void store_k(__bf16* dst, int tid) const {
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
-      const int idx = tid + i * kThreads;
-      const int key = idx / CH;
-      const int c = idx % CH;
+      const int idx = tid + i * NT, key = idx / CH, c = idx % CH;
       const int row = (key & ~31) + k_lds_row(key & 31);
-      *reinterpret_cast<uint4*>(&s.k[buf][row * Lds<D>::KS + c * 8]) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VN; ++i) {
-      const int idx = tid + i * kThreads;
-      const int pr = idx % (kBN / 2);
-      const int c = idx / (kBN / 2);
-      const uint32_t a[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
-      const uint32_t b[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const int d = c * 8 + e;
-        *reinterpret_cast<uint32_t*>(&s.vt[buf][d * Lds<D>::VS + vt_col(pr)]) = lo | (hi << 16);
-      }
+      *reinterpret_cast<uint4*>(dst + row * Lds<D>::KS + c * 8) = kr[i];
     }
   }
+  __device__ __forceinline__ void store_v(__bf16* dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int idx = tid + i * NT, key = idx / CH, c = idx % CH;
+      *reinterpret_cast<uint4*>(dst + key * Lds<D>::VS + c * 8) = vr[i];
+    }
+  }
+  __device__ __forceinline__ void store(Lds<D>& s, int buf, int tid) const {
+    store_k(s.k[buf], tid);
+    store_v(s.v[buf], tid);
+  }
 };
+
+// A operand of O^T += V^T P^T for d block db and the 16 keys of k-step (kb, c):
+// lane l gets d = 32*db + l%32 and keys 32*kb + 16*(l/32) + 8*c .. +7, read
+// from the natural V tile with two transpose loads.  ds_read_b64_tr_b16 hands
+// lane i of each 16-lane group element i%4 of the 4-element vectors that lanes
+// 4j + i/4 (j = 0..3) of the group addressed, in order of j; so lane s of a
+// group addresses row (base + 4h + s/4), columns (dbase + 4*(s%4)) .. +3.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+template <int D>
+__device__ __forceinline__ bf16x8 vt_frag(const __bf16* vtile, int db, int kb, int c, int lane) {
+  const int sl = lane & 15, gg = (lane >> 4) & 1, hh = lane >> 5;
+  const int row = 32 * kb + 16 * hh + 8 * c + (sl >> 2);
+  const int col = 32 * db + 16 * gg + 4 * (sl & 3);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const __bf16* p0 = vtile + row * Lds<D>::VS + col;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * Lds<D>::VS));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 // Tile schedule of one workgroup: tiles [0, n1) then [b_start, b_start + n2).
 struct TileRange {
@@ -141,85 +142,53 @@ __device__ __forceinline__ TileRange tile_range(int Sk, int p_min, int p_max, in
   return r;
 }
 
+// Where a wave's query rows sit (absolute positions, bottom-right causal).
+struct RowGeom {
+  int Sk, causal, w1, w2;
+  int p_min, p_max;  // first / last absolute position of the workgroup's rows
+  int p_lane;        // absolute position of this lane's row in query block 0
+};
+
+// The running state of one wave: 32*QB query rows of one head, Q^T fragments,
+// running max / sum per row (one row per lane) and the O^T accumulators.  The
+// tile steps below are shared by the 4-wave and the 8-wave kernels, so both
+// compute the same arithmetic in the same order.
 template <int D, int QB>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int B, int Sq,
-    int Sk, int Hq, int Hkv, int hpw, float sl2, int causal, int w1, int w2) {
-  __shared__ Lds<D> s;
-  constexpr int RW = 32 * QB;  // query rows per wave
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int hh = lane >> 5;
-  const int l32 = lane & 31;
-
-  const int g = Hq / Hkv;
-  const int groups = g / hpw;  // workgroups per KV head
-  const int R = RW * (4 / hpw);
-  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R);
-  const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
-  const int h = kvh * g + wi.grp * hpw + (wave % hpw);
-  const int rb = wave / hpw;   // row block of this wave inside the workgroup
-  const int tile_idx = wi.tile;
-  const int row0 = tile_idx * R;
-  const int wrow0 = row0 + rb * RW;
-  const int off = Sk - Sq;  // bottom-right alignment
-  const int p_min = off + row0;
-  const int p_max = off + min(Sq, row0 + R) - 1;
-
-  // Q^T fragments (B operand): query row wrow0 + 32*qb + l32, d = 16*ks + 8*hh ..
+struct WaveRows {
   bf16x8 qf[QB][D / 16];
+  float m[QB], l[QB];
+  f32x16 acc[D / 32][QB];
+  float sig2;
+
+  __device__ __forceinline__ void init(const __bf16* q, const float* sink, int b, int Sq, int Hq,
+                                       int h, int wrow0, int hh, int l32) {
+    // Q^T fragments (B operand): query row wrow0 + 32*qb + l32, d = 16*ks + 8*hh ..
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = wrow0 + 32 * qb + l32;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = wrow0 + 32 * qb + l32;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      if (row < Sq) {
-        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(
-            q + (((size_t)b * Sq + row) * Hq + h) * D + 16 * ks + 8 * hh);
-      } else {
-        qf[qb][ks] = bf16x8{};
+      for (int ks = 0; ks < D / 16; ++ks) {
+        if (row < Sq) {
+          qf[qb][ks] = *reinterpret_cast<const bf16x8*>(
+              q + (((size_t)b * Sq + row) * Hq + h) * D + 16 * ks + 8 * hh);
+        } else {
+          qf[qb][ks] = bf16x8{};
+        }
       }
+    }
+    sig2 = sink ? sink[h] * kLog2e : kNegInf;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      m[qb] = sig2;
+      l[qb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db][qb] = f32x16{};
     }
   }
 
-  const float sig2 = sink ? sink[h] * kLog2e : kNegInf;
-  float m[QB], l[QB];
-  f32x16 acc[D / 32][QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = sig2;
-    l[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db][qb] = f32x16{};
-  }
-
-  const size_t rs = (size_t)Hkv * D;
-  const __bf16* kbase = k + ((size_t)b * Sk * Hkv + kvh) * D;
-  const __bf16* vbase = v + ((size_t)b * Sk * Hkv + kvh) * D;
-  const TileRange tr = tile_range(Sk, p_min, p_max, causal, w1, w2);
-  const int ntiles = tr.count();
-
-  // Q and the sink are loaded; start the tile loop with no VMEM load pending so
-  // that the compiler's wait tracking does not hold the first MFMA of every
-  // tile on the prefetch of the next one.
-  __builtin_amdgcn_s_waitcnt(0);
-  TileRegs<D> regs;
-  regs.init(rs, tid);
-  if (ntiles > 0) {
-    regs.load(kbase, vbase, rs, tr.tile(0) * kBN, Sk);
-    regs.store(s, 0, tid);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int key0 = tr.tile(it) * kBN;
-    if (it + 1 < ntiles) regs.load(kbase, vbase, rs, tr.tile(it + 1) * kBN, Sk);
-
-    // ---- S^T = K Q^T : 2 key blocks x QB query blocks of 32x32
-    f32x16 st[2][QB];
+  // S^T = K Q^T over one 64-key tile: 2 key blocks x QB query blocks of 32x32.
+  __device__ __forceinline__ void scores(const __bf16* kl, f32x16 (&st)[2][QB], int l32,
+                                         int hh) const {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -229,27 +198,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            &s.k[buf][(32 * kb + l32) * Lds<D>::KS + 16 * ks + 8 * hh]);
+            kl + (32 * kb + l32) * Lds<D>::KS + 16 * ks + 8 * hh);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) st[kb][qb] = mfma32(kf, qf[qb][ks], st[kb][qb]);
       }
     }
+  }
 
-    // ---- mask (only on tiles that straddle a boundary).  Per lane and key
-    // block, element i (key j = base + i) is visible iff i <= hi (causal bound
-    // and j < Sk) and, with a window, i < a (first window) or i > b (last).
-    const bool need_mask = (key0 + kBN > Sk) || (causal && key0 + kBN - 1 > p_min) ||
-                           (w2 > 0 && key0 + kBN - 1 >= w1 && key0 <= p_max - w2);
+  // Mask (only on tiles that straddle a boundary), online softmax in base 2 with
+  // the exact running max of the tile, P rounded to bf16 for P V.
+  __device__ __forceinline__ void softmax(f32x16 (&st)[2][QB], bf16x8 (&pf)[2][QB][2], int key0,
+                                          const RowGeom& g, float sl2, int hh) {
+    // Per lane and key block, element i (key j = base + i) is visible iff
+    // i <= hi (causal bound and j < Sk) and, with a window, i < a (first
+    // window) or i > bnd (last window).
+    const bool need_mask = (key0 + kBN > g.Sk) || (g.causal && key0 + kBN - 1 > g.p_min) ||
+                           (g.w2 > 0 && key0 + kBN - 1 >= g.w1 && key0 <= g.p_max - g.w2);
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int p = off + wrow0 + 32 * qb + l32;
+        const int p = g.p_lane + 32 * qb;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int base = key0 + 32 * kb + 16 * hh;
-          const int hi = min(causal ? p - base : 15, Sk - 1 - base);
-          if (w2 > 0) {
-            const int a = w1 - base, bnd = p - w2 - base;
+          const int hi = min(g.causal ? p - base : 15, g.Sk - 1 - base);
+          if (g.w2 > 0) {
+            const int a = g.w1 - base, bnd = p - g.w2 - base;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const bool vis = (i <= hi) & ((i < a) | (i > bnd));
@@ -262,9 +236,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         }
       }
     }
-
-    // ---- online softmax (base 2), P in bf16
-    bf16x8 pf[2][QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = kNegInf;
@@ -301,47 +272,111 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
                                     x[8 * c + 4], x[8 * c + 5], x[8 * c + 6], x[8 * c + 7]);
         }
     }
+  }
 
-    // ---- O^T += V^T P^T : k-steps of 16 keys (key block kb, half c)
+  // O^T += V^T P^T: k-steps of 16 keys (key block kb, half c).
+  __device__ __forceinline__ void pv(const __bf16* vl, const bf16x8 (&pf)[2][QB][2], int lane) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int d = 32 * db + l32;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int kb = t >> 1, c = t & 1;
-        const int pair = 16 * kb + 8 * hh + 4 * c;
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-            &s.vt[buf][d * Lds<D>::VS + vt_col(pair)]);
+        const bf16x8 vf = vt_frag<D>(vl, db, kb, c, lane);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[db][qb] = mfma32(vf, pf[kb][qb][c], acc[db][qb]);
       }
     }
+  }
 
+  // Fold the sink into the denominator once, normalise, store O and LSE.
+  __device__ __forceinline__ void finish(__bf16* o, float* lse, int b, int Sq, int Hq, int h,
+                                         int wrow0, int hh, int l32) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = wrow0 + 32 * qb + l32;
+      float lt = l[qb] + __shfl_xor(l[qb], 32, 64);
+      if (sig2 != kNegInf) lt += exp2_fast(sig2 - m[qb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if (row < Sq) {
+        __bf16* orow = o + (((size_t)b * Sq + row) * Hq + h) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x16& x = acc[db][qb];
+            *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * a + 4 * hh) =
+                to_bf16x4(x[4 * a] * inv, x[4 * a + 1] * inv, x[4 * a + 2] * inv,
+                          x[4 * a + 3] * inv);
+          }
+        if (lse && hh == 0)
+          lse[((size_t)b * Hq + h) * Sq + row] =
+              lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : kNegInf;
+      }
+    }
+  }
+};
+
+// 4 waves: 4 query heads of one GQA group (or 4 row blocks) over the same rows.
+template <int D, int QB>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int B, int Sq,
+    int Sk, int Hq, int Hkv, int hpw, float sl2, int causal, int w1, int w2) {
+  __shared__ Lds<D> s;
+  constexpr int RW = 32 * QB;  // query rows per wave
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int g = Hq / Hkv;
+  const int groups = g / hpw;  // workgroups per KV head
+  const int R = RW * (4 / hpw);
+  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R);
+  const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
+  const int h = kvh * g + wi.grp * hpw + (wave % hpw);
+  const int rb = wave / hpw;   // row block of this wave inside the workgroup
+  const int row0 = wi.tile * R;
+  const int wrow0 = row0 + rb * RW;
+  const int off = Sk - Sq;  // bottom-right alignment
+  const RowGeom geom{Sk, causal, w1, w2, off + row0, off + min(Sq, row0 + R) - 1,
+                     off + wrow0 + l32};
+
+  WaveRows<D, QB> wr;
+  wr.init(q, sink, b, Sq, Hq, h, wrow0, hh, l32);
+
+  const size_t rs = (size_t)Hkv * D;
+  const __bf16* kbase = k + ((size_t)b * Sk * Hkv + kvh) * D;
+  const __bf16* vbase = v + ((size_t)b * Sk * Hkv + kvh) * D;
+  const TileRange tr = tile_range(Sk, geom.p_min, geom.p_max, causal, w1, w2);
+  const int ntiles = tr.count();
+
+  // Q and the sink are loaded; start the tile loop with no VMEM load pending so
+  // that the compiler's wait tracking does not hold the first MFMA of every
+  // tile on the prefetch of the next one.
+  __builtin_amdgcn_s_waitcnt(0);
+  TileRegs<D> regs;
+  regs.init(rs, tid);
+  if (ntiles > 0) {
+    regs.load(kbase, vbase, rs, tr.tile(0) * kBN, Sk);
+    regs.store(s, 0, tid);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int key0 = tr.tile(it) * kBN;
+    if (it + 1 < ntiles) regs.load(kbase, vbase, rs, tr.tile(it + 1) * kBN, Sk);
+    f32x16 st[2][QB];
+    bf16x8 pf[2][QB][2];
+    wr.scores(s.k[buf], st, l32, hh);
+    wr.softmax(st, pf, key0, geom, sl2, hh);
+    wr.pv(s.v[buf], pf, lane);
     if (it + 1 < ntiles) regs.store(s, buf ^ 1, tid);
     __syncthreads();
   }
-
-  // ---- epilogue: fold the sink into the denominator once, normalise, store
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = wrow0 + 32 * qb + l32;
-    float lt = l[qb] + __shfl_xor(l[qb], 32, 64);
-    if (sig2 != kNegInf) lt += exp2_fast(sig2 - m[qb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (row < Sq) {
-      __bf16* orow = o + (((size_t)b * Sq + row) * Hq + h) * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const f32x16& x = acc[db][qb];
-          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * a + 4 * hh) =
-              to_bf16x4(x[4 * a] * inv, x[4 * a + 1] * inv, x[4 * a + 2] * inv, x[4 * a + 3] * inv);
-        }
-      if (lse && hh == 0)
-        lse[((size_t)b * Hq + h) * Sq + row] = lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : kNegInf;
-    }
-  }
+  wr.finish(o, lse, b, Sq, Hq, h, wrow0, hh, l32);
 }
 
 // ---------------------------------------------------------------------------

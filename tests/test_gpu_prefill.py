@@ -57,6 +57,15 @@ def test_config1_fp32_tiny():
     (1, 300, 300, 4, 1, 128, True, (5, 37)),  # window, D=128
     (1, 1, 1, 4, 4, 64, True, None),         # single token
     (1, 5, 0, 4, 2, 64, False, None),        # no keys at all
+    # group size a multiple of 8: two 4-head workgroups per KV head
+    (1, 300, 300, 16, 2, 64, True, None),    # g=8, ragged tail
+    (2, 190, 260, 8, 1, 64, False, None),    # g=8, non-causal, Sq < Sk
+    (1, 100, 60, 8, 1, 64, True, None),      # g=8, Sq > Sk: first rows see no key
+    (1, 400, 400, 16, 2, 64, True, (70, 100)),  # g=8, first/last window
+    (1, 333, 333, 8, 1, 64, True, (0, 64)),  # g=8, sliding window
+    (1, 1, 1, 8, 1, 64, True, None),         # g=8, single token
+    (1, 5, 0, 8, 1, 64, False, None),        # g=8, no keys at all
+    (1, 130, 130, 32, 2, 64, True, None),    # g=16: two 8-head workgroups per KV head
 ])
 @pytest.mark.parametrize("use_sink", [True, False])
 def test_prefill_bf16_matches_oracle(B, Sq, Sk, Hq, Hkv, D, causal, window, use_sink):
