@@ -38,50 +38,26 @@ __device__ __forceinline__ uint32_t pick16(const uint4& x, int e) {
   return (w >> (16 * (e & 1))) & 0xffffu;
 }
 
-// 64 rows x D tile of a [.., rows, heads, D] tensor: each thread loads one
-// (row pair, 16-byte chunk) item per 256 items and writes it both in natural
-// layout (rows permuted within 32-blocks, see lds_row) and transposed.  Loads
-// go through a buffer resource per tile, so rows past the end read as zero.
+// A operand (32 d x 16 rows) of an MFMA that contracts over tile rows, read
+// from a natural-layout tile (rows permuted within 32-blocks, see lds_row):
+// lane l gets d = 32*db + l%32 and logical rows r0 + 16*(l/32) .. +7.
+// ds_read_b64_tr_b16 hands lane i of each 16-lane group element i%4 of the
+// 4-element vectors that lanes 4j + i/4 (j = 0..3) of the group addressed, in
+// order of j; so lane s of a group addresses logical row (base + 4h + s/4),
+// columns (dbase + 4*(s%4)) .. +3, for the two loads h = 0, 1.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 template <int D>
-struct PairTile {
-  static constexpr int CH = D / 8;
-  static constexpr int N = (kTile / 2) * CH / kThreads;
-  uint4 r[N][2];
-  uint32_t off[N][2];
-  __device__ __forceinline__ void init(size_t rs, int tid) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = tid + i * kThreads;
-      const int pr = idx % (kTile / 2), c = idx / (kTile / 2);
-      off[i][0] = (uint32_t)(((size_t)(2 * pr) * rs + 8 * c) * 2);
-      off[i][1] = (uint32_t)(((size_t)(2 * pr + 1) * rs + 8 * c) * 2);
-    }
-  }
-  __device__ __forceinline__ void load(const __bf16* base, size_t rs, int row0, int nrows) {
-    const auto rsrc = make_rsrc(base + (size_t)row0 * rs, (uint32_t)((size_t)(nrows - row0) * rs * 2));
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      r[i][0] = buf_load16(rsrc, off[i][0]);
-      r[i][1] = buf_load16(rsrc, off[i][1]);
-    }
-  }
-  __device__ __forceinline__ void store(__bf16* nat, __bf16* tr, int tid) const {
-    constexpr int NS = D + kPad, TS = kTile + kPad;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = tid + i * kThreads;
-      const int pr = idx % (kTile / 2), c = idx / (kTile / 2);
-      if (nat) {
-        *reinterpret_cast<uint4*>(nat + lds_row(2 * pr) * NS + 8 * c) = r[i][0];
-        *reinterpret_cast<uint4*>(nat + lds_row(2 * pr + 1) * NS + 8 * c) = r[i][1];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint32_t*>(tr + (8 * c + e) * TS + 2 * pr) =
-            pick16(r[i][0], e) | (pick16(r[i][1], e) << 16);
-    }
-  }
-};
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16* nat, int r0, int db, int lane) {
+  constexpr int NS = D + kPad;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const int sl = lane & 15, gg = (lane >> 4) & 1, hh = lane >> 5;
+  const int col = 32 * db + 16 * gg + 4 * (sl & 3);
+  const int ra = r0 + 16 * hh + (sl >> 2);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(nat + lds_row(ra) * NS + col));
+  const i16x4 b =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(nat + lds_row(ra + 4) * NS + col));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 // 64 rows x D tile stored in natural layout only (rows permuted).
 template <int D>
@@ -181,20 +157,18 @@ template <int D>
 struct DkdvLds {
   __bf16 q[2][kTile * (D + kPad)];
   __bf16 dO[2][kTile * (D + kPad)];
-  __bf16 qt[2][D * (kTile + kPad)];
-  __bf16 dOt[2][D * (kTile + kPad)];
   alignas(16) float lse2[2][kTile];
   alignas(16) float di[2][kTile];
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Sq, int Sk, int Hq, int Hkv, float scale,
     float sl2, int causal, int w1, int w2) {
   __shared__ DkdvLds<D> s;
-  constexpr int NS = D + kPad, TS = kTile + kPad;
+  constexpr int NS = D + kPad;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, l32 = lane & 31;
   // grid: (Hkv, B, key blocks) with the key block slowest, so the key blocks
@@ -236,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const int niter = nq * g;
 
   const size_t rs = (size_t)Hq * D;
-  PairTile<D> tq, tdo;
+  RowTile<D> tq, tdo;
   tq.init(rs, tid);
   tdo.init(rs, tid);
   float lse_r = 0.f, di_r = 0.f;
@@ -255,8 +229,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
                                          make_rsrc(di + x, nb), (tid & 63) * 4, 0, 0));
   };
   auto store_iter = [&](int buf) {
-    tq.store(s.q[buf], s.qt[buf], tid);
-    tdo.store(s.dO[buf], s.dOt[buf], tid);
+    tq.store(s.q[buf], tid);
+    tdo.store(s.dO[buf], tid);
     if (tid < kTile) {
       s.lse2[buf][tid] = lse_r * kLog2e;
       s.di[buf][tid] = di_r;
@@ -336,17 +310,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     else
       softmax_grad(std::false_type{});
 
-    // dV^T += dO^T P, dK^T += Q^T dS
+    // dV^T += dO^T P, dK^T += Q^T dS (A operands read transposed from the
+    // natural tiles; k-step (qb, c) covers rows 32*qb + 16*hh + 8*c .. +7)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int d = 32 * db + l32;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const int col = 32 * qb + 16 * hh + 8 * c;
-          const bf16x8 dot = *reinterpret_cast<const bf16x8*>(&s.dOt[buf][d * TS + col]);
-          const bf16x8 qt = *reinterpret_cast<const bf16x8*>(&s.qt[buf][d * TS + col]);
+          const bf16x8 dot = tr_frag<D>(s.dO[buf], 32 * qb + 8 * c, db, lane);
+          const bf16x8 qt = tr_frag<D>(s.q[buf], 32 * qb + 8 * c, db, lane);
           dva[db] = mfma32(dot, pb[qb][c], dva[db]);
           dka[db] = mfma32(qt, sb[qb][c], dka[db]);
         }
@@ -383,7 +356,6 @@ template <int D>
 struct DqLds {
   __bf16 k[2][kTile * (D + kPad)];
   __bf16 v[2][kTile * (D + kPad)];
-  __bf16 kt[2][D * (kTile + kPad)];
 };
 
 struct QRange {
@@ -414,13 +386,13 @@ __device__ __forceinline__ QRange kv_tiles(int Sk, int p_min, int p_max, int cau
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
     __bf16* __restrict__ dq, int B, int Sq, int Sk, int Hq, int Hkv, int hpw, float scale,
     float sl2, int causal, int w1, int w2) {
   __shared__ DqLds<D> s;
-  constexpr int NS = D + kPad, TS = kTile + kPad;
+  constexpr int NS = D + kPad;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, l32 = lane & 31;
   const int g = Hq / Hkv;
@@ -464,15 +436,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const size_t rs = (size_t)Hkv * D;
   const __bf16* kbase = k + ((size_t)b * Sk * Hkv + kvh) * D;
   const __bf16* vbase = v + ((size_t)b * Sk * Hkv + kvh) * D;
-  PairTile<D> tk;
-  RowTile<D> tv;
+  RowTile<D> tk, tv;
   tk.init(rs, tid);
   tv.init(rs, tid);
   __builtin_amdgcn_s_waitcnt(0);
   if (ntiles > 0) {
     tk.load(kbase, rs, tr.tile(0) * kTile, Sk);
     tv.load(vbase, rs, tr.tile(0) * kTile, Sk);
-    tk.store(s.k[0], s.kt[0], tid);
+    tk.store(s.k[0], tid);
     tv.store(s.v[0], tid);
   }
   __syncthreads();
@@ -532,17 +503,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       grad_scores(std::false_type{});
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int d = 32 * db + l32;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int kb = t >> 1, c = t & 1;
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-            &s.kt[buf][d * TS + 32 * kb + 16 * hh + 8 * c]);
+        const bf16x8 ka = tr_frag<D>(s.k[buf], 32 * kb + 8 * c, db, lane);
         dqa[db] = mfma32(ka, sb[kb][c], dqa[db]);
       }
     }
     if (it + 1 < ntiles) {
-      tk.store(s.k[buf ^ 1], s.kt[buf ^ 1], tid);
+      tk.store(s.k[buf ^ 1], tid);
       tv.store(s.v[buf ^ 1], tid);
     }
     __syncthreads();
