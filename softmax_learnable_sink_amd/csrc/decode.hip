@@ -26,14 +26,16 @@ namespace attn_sink {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVTS = 40;    // V^T staging row stride: 32 tokens + 16 B padding
 
 constexpr int kSub = 2048;  // selected tokens whose slots are staged in LDS at once
 
+template <int D>
+constexpr int vrow() { return D + 8; }  // V staging row stride: D + 16 B padding
+
 template <int D, int NW>
 struct DecLds {
-  int slot[kSub];           // slot of each selected token of the current block
-  __bf16 vt[NW][D * kVTS];  // per-wave V^T staging tiles
+  int slot[kSub];               // slot of each selected token of the current block
+  __bf16 v[NW][32 * vrow<D>()]; // per-wave V staging tiles, natural [token][d]
 };
 
 template <int D>
@@ -76,14 +78,21 @@ struct KVRegs {
   }
 };
 
-__device__ __forceinline__ uint32_t half16(const uint4& x, int e) {
-  const uint32_t w = e < 2 ? x.x : (e < 4 ? x.y : (e < 6 ? x.z : x.w));
-  return (w >> (16 * (e & 1))) & 0xffffu;
-}
-// element e of V row t of a step, zero when the row holds no selected token
+// A operand (16 d x 32 tokens) of O^T += V^T P^T read from the natural V tile:
+// lane l gets d = 16*db + l%16 and tokens 8*(l/16) .. +7.  ds_read_b64_tr_b16
+// hands lane i of each 16-lane group element i%4 of the 4-element vectors that
+// lanes 4j + i/4 (j = 0..3) of the group addressed, in order of j; so lane s of
+// group G addresses token 8G + 4h + s/4, columns 16*db + 4*(s%4) .. +3, for
+// the two loads h = 0, 1.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 template <int D>
-__device__ __forceinline__ uint32_t vhalf(const KVRegs<D>& r, int t, int e) {
-  return ((r.vvalid >> t) & 1u) ? half16(r.vr[t], e) : 0u;
+__device__ __forceinline__ bf16x8 vt_frag16(const __bf16* vtile, int db, int lane) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const int sl = lane & 15, G = lane >> 4;
+  const __bf16* p0 = vtile + (8 * G + (sl >> 2)) * vrow<D>() + 16 * db + 4 * (sl & 3);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * vrow<D>()));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -138,7 +147,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
   for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{};
 
   constexpr int TPL = KVRegs<D>::TPL, NTG = KVRegs<D>::NTG;
-  __bf16* vt = s.vt[wave];
+  __bf16* vt = s.v[wave];
   __builtin_amdgcn_s_waitcnt(0);
 
   // One 32-token step of this wave: scores, online softmax, V^T staging, P.V.
@@ -175,33 +184,21 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
     for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
     const bf16x8 pf = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
 
-    // V^T staging: row d = 8*c + e, tokens TPL*tg .. +TPL-1
+    // V staging, natural rows: token TPL*tg + t, d-chunk c; rows without a
+    // selected token are written as zeros
     {
       const int tg = lane % NTG, c = lane / NTG;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16* dst = vt + (8 * c + e) * kVTS + TPL * tg;
-        if constexpr (TPL == 4) {
-          uint2 w;
-          w.x = vhalf(cur, 0, e) | (vhalf(cur, 1, e) << 16);
-          w.y = vhalf(cur, 2, e) | (vhalf(cur, 3, e) << 16);
-          *reinterpret_cast<uint2*>(dst) = w;
-        } else {
-          uint4 w;
-          w.x = vhalf(cur, 0, e) | (vhalf(cur, 1, e) << 16);
-          w.y = vhalf(cur, 2, e) | (vhalf(cur, 3, e) << 16);
-          w.z = vhalf(cur, 4, e) | (vhalf(cur, 5, e) << 16);
-          w.w = vhalf(cur, 6, e) | (vhalf(cur, 7, e) << 16);
-          *reinterpret_cast<uint4*>(dst) = w;
-        }
+      for (int t = 0; t < TPL; ++t) {
+        const bool ok = (cur.vvalid >> t) & 1u;
+        const uint4 x = cur.vr[t];
+        *reinterpret_cast<uint4*>(vt + (TPL * tg + t) * vrow<D>() + 8 * c) =
+            uint4{ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u};
       }
     }
     wave_lds_sync();
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + (16 * db + hl) * kVTS + 8 * kg);
-      acc[db] = mfma16(vf, pf, acc[db]);
-    }
+    for (int db = 0; db < D / 16; ++db) acc[db] = mfma16(vt_frag16<D>(vt, db, lane), pf, acc[db]);
     wave_lds_sync();
   };
 
