@@ -148,7 +148,6 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
 
   constexpr int TPL = KVRegs<D>::TPL, NTG = KVRegs<D>::NTG;
   __bf16* vt = s.v[wave];
-  __builtin_amdgcn_s_waitcnt(0);
 
   // One 32-token step of this wave: scores, online softmax, V^T staging, P.V.
   auto step = [&](const KVRegs<D>& cur, int base, int nsub) {
@@ -205,11 +204,29 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
   for (int sub0 = u0; sub0 < u1; sub0 += kSub) {
     const int nsub = min(kSub, u1 - sub0);
     const int nsteps = (nsub + 31) >> 5;
-    // slot table of this block, padded with -1 up to an even number of steps
+    // slot table of this block, padded with -1 up to an even number of steps;
+    // every block-table load of a thread is issued before its first LDS write,
+    // so the table costs one memory latency (overlapping the Q loads)
     const int npad = min(kSub, 64 * ((nsteps + 1) >> 1));
-    for (int x = tid; x < npad; x += 64 * NW)
-      s.slot[x] = x < nsub ? slot_of(bt_row, token_of(sub0 + x, L, w1, w2), page_shift) : -1;
+    constexpr int kPer = kSub / (64 * NW);
+    int sv[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)  // index clamped to a selected token
+      sv[i] = slot_of(bt_row, token_of(sub0 + min(tid + i * 64 * NW, nsub - 1), L, w1, w2),
+                      page_shift);
+    // keep the loads unconditional and issued together (otherwise the compiler
+    // sinks each one into the branch that uses it and waits for it there)
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(sv[i]));
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int x = tid + i * 64 * NW;
+      if (x < npad) s.slot[x] = x < nsub ? sv[i] : -1;
+    }
     __syncthreads();
+    // start the step loop with no VMEM load pending, so that the compiler's
+    // wait tracking does not hold a step's MFMAs on the next step's prefetch
+    __builtin_amdgcn_s_waitcnt(0);
     if (active) {
       // Two register sets in turn, two steps per iteration with no exit in
       // between (so the compiler cannot sink the prefetch below a branch); an
