@@ -92,7 +92,9 @@ const char* attn_sink_last_error(void);
  * Requirements: B, Sq, Hq, Hkv >= 1; Sk >= 0; Hq % Hkv == 0; D in {64, 128};
  * softmax_scale finite and > 0; a window needs causal = 1, window_first >= 0
  * and window_last >= 1.  A row that sees no key gets O = 0 and LSE = sink
- * (or -inf without a sink).
+ * (or -inf without a sink).  Size limits (ATTN_SINK_ERR_UNSUPPORTED past
+ * them): B <= 65535, B*Sq*Hq and B*Sk*Hkv < 2^31, and for bf16 one batch's K
+ * (or V) slice Sk*Hkv*D*2 bytes <= 4 GiB - 1.
  */
 int attn_sink_fwd_prefill(const void* q, const void* k, const void* v, const float* sink,
                           void* o, float* lse, int B, int Sq, int Sk, int Hq, int Hkv, int D,
@@ -118,7 +120,9 @@ int attn_sink_fwd_prefill(const void* q, const void* k, const void* v, const flo
  *   workspace    device scratch of at least attn_sink_decode_workspace_bytes()
  *                bytes for the same arguments; contents need no initialisation.
  * Requirements: D in {64, 128}; page_size a power of two in [1, 256];
- * Hq % Hkv == 0; max_pages_per_seq >= 1; num_pages >= 1.
+ * Hq % Hkv == 0; max_pages_per_seq >= 1; num_pages >= 1.  Size limits
+ * (ATTN_SINK_ERR_UNSUPPORTED past them): B and the number of splits <= 65535,
+ * num_pages*page_size and max_pages_per_seq*page_size < 2^31.
  * With a window only the selected tokens are read from the cache.
  */
 int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -145,6 +149,9 @@ size_t attn_sink_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int page_
  * dSink_h = -sum_{b,i} exp(sink_h - LSE_i) * <dO_i, O_i>, reduced in fp32 in
  * a fixed order.
  * workspace: at least attn_sink_bwd_workspace_bytes() bytes.
+ * Size limits (ATTN_SINK_ERR_UNSUPPORTED past them): B and ceil(Sk/128)
+ * <= 65535, B*Sq*Hq and B*Sk*Hkv < 2^31, one batch's K/V slice
+ * (Sk*Hkv*D*2 bytes) and Q/dO slice (Sq*Hq*D*2 bytes) <= 4 GiB - 1.
  */
 int attn_sink_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, const float* sink, void* dq, void* dk, void* dv,

@@ -74,6 +74,11 @@ int check_scale(float scale) {
 
 bool fits_int32(long long x) { return x >= 0 && x <= INT_MAX; }
 
+// Largest grid extent in y and z, and the largest byte range one 32-bit buffer
+// resource addresses (the kernels address a batch's K/V or Q/dO slice through one).
+constexpr long long kMaxGridYZ = 65535;
+constexpr long long kMaxSlice = 0xffffffffLL;
+
 }  // namespace
 
 extern "C" {
@@ -104,6 +109,10 @@ int attn_sink_fwd_prefill(const void* q, const void* k, const void* v, const flo
           "sink and lse must be 4-byte aligned");
   REQUIRE(fits_int32((long long)B * Sq * Hq) && fits_int32((long long)B * Sk * Hkv),
           ATTN_SINK_ERR_UNSUPPORTED, "too many rows for 32-bit row indices");
+  REQUIRE(B <= kMaxGridYZ, ATTN_SINK_ERR_UNSUPPORTED, "B must be <= %lld (got %d)", kMaxGridYZ,
+          B);
+  REQUIRE(dtype != ATTN_SINK_BF16 || (long long)Sk * Hkv * D * 2 <= kMaxSlice,
+          ATTN_SINK_ERR_UNSUPPORTED, "one batch's K or V slice exceeds 4 GiB");
   PrefillArgs a{q, k, v, sink, o, lse, B, Sq, Sk, Hq, Hkv, D, softmax_scale, causal,
                 window_first, window_last};
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -159,6 +168,8 @@ int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v
           ATTN_SINK_ERR_INVALID_ARG, "block_table, seqlens_k, sink and lse must be 4-byte aligned");
   const DecodePlan plan = plan_decode(B, Hq, Hkv, D, page_size, max_pages_per_seq, window_first,
                                       window_last, num_splits);
+  REQUIRE(B <= kMaxGridYZ && plan.max_splits <= kMaxGridYZ, ATTN_SINK_ERR_UNSUPPORTED,
+          "B (%d) and the split count (%d) must each be <= %lld", B, plan.max_splits, kMaxGridYZ);
   REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
           "a 16-byte aligned workspace of %zu bytes is required", plan.workspace_bytes);
   REQUIRE(workspace_bytes >= plan.workspace_bytes, ATTN_SINK_ERR_WORKSPACE,
@@ -201,6 +212,10 @@ int attn_sink_bwd(const void* q, const void* k, const void* v, const void* o, co
           "lse, sink and dsink must be 4-byte aligned");
   REQUIRE(fits_int32((long long)B * Sq * Hq) && fits_int32((long long)B * Sk * Hkv),
           ATTN_SINK_ERR_UNSUPPORTED, "too many rows for 32-bit row indices");
+  REQUIRE(B <= kMaxGridYZ && (Sk + 127) / 128 <= kMaxGridYZ, ATTN_SINK_ERR_UNSUPPORTED,
+          "B (%d) and ceil(Sk / 128) (%d) must each be <= %lld", B, (Sk + 127) / 128, kMaxGridYZ);
+  REQUIRE((long long)Sk * Hkv * D * 2 <= kMaxSlice && (long long)Sq * Hq * D * 2 <= kMaxSlice,
+          ATTN_SINK_ERR_UNSUPPORTED, "one batch's K/V or Q/dO slice exceeds 4 GiB");
   const size_t need = backward_workspace_bytes(B, Sq, Sk, Hq, Hkv, D);
   REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
           "a 16-byte aligned workspace of %zu bytes is required", need);

@@ -75,6 +75,8 @@ def _prefill(lib, **kw):
     (dict(causal=2), binding.ERR_INVALID_ARG, "causal"),
     (dict(dtype=7), binding.ERR_UNSUPPORTED, "dtype"),
     (dict(q=P_ODD), binding.ERR_INVALID_ARG, "aligned"),
+    (dict(B=70000, Sq=1, Sk=1), binding.ERR_UNSUPPORTED, "B must be <="),
+    (dict(Sk=1 << 22, Hkv=8, Hq=8, D=128), binding.ERR_UNSUPPORTED, "4 GiB"),
 ])
 def test_prefill_rejects(lib, kw, status, msg):
     assert _prefill(lib, **kw) == status
@@ -105,6 +107,7 @@ def _decode(lib, **kw):
     (dict(sl=None), binding.ERR_INVALID_ARG, "must not be NULL"),
     (dict(dtype=binding.F32), binding.ERR_UNSUPPORTED, "bf16"),
     (dict(w1=3, w2=-1), binding.ERR_INVALID_ARG, "window"),
+    (dict(B=70000, wsb=1 << 40), binding.ERR_UNSUPPORTED, "must each be <="),
 ])
 def test_decode_rejects(lib, kw, status, msg):
     assert _decode(lib, **kw) == status
@@ -143,6 +146,8 @@ def _bwd(lib, **kw):
     (dict(Sk=0), binding.ERR_INVALID_ARG, "Sk >= 1"),
     (dict(D=256), binding.ERR_UNSUPPORTED, "64 or 128"),
     (dict(w1=2, w2=3, causal=0), binding.ERR_UNSUPPORTED, "causal"),
+    (dict(B=70000, Sq=1, Sk=1, wsb=1 << 40), binding.ERR_UNSUPPORTED, "must each be <="),
+    (dict(Sq=1 << 22, Hq=8, Hkv=8, D=128, wsb=1 << 40), binding.ERR_UNSUPPORTED, "4 GiB"),
 ])
 def test_bwd_rejects(lib, kw, status, msg):
     assert _bwd(lib, **kw) == status
