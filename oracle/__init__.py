@@ -16,5 +16,6 @@ from .sink_attention import (  # noqa: F401
     select_slots,
     gather_kv,
     decode_paged,
+    extend_paged,
     backward,
 )

@@ -35,7 +35,11 @@ Readings where the pages are silent (each also listed in the design doc):
     j < W1 or j > p - W2 (with j <= p); this reproduces both branches of the
     page's selection code for every length;
   * GQA: query head h reads KV head h // (Hq / Hkv);
-  * a row that sees no key and has no sink gets O = 0, LSE = -inf.
+  * a row that sees no key and has no sink gets O = 0, LSE = -inf;
+  * extend (chunked prefill): a sequence's new tokens are the last nq of its
+    L cached tokens, so new token i sits at position L - nq + i and sees keys
+    by the prefill rule above, the window included (the pages define the
+    window for decode only; the per-query rule is its prefill form).
 
 Parity status: every function below is pinned by tests that do not retype
 its formula (closed forms, library special cases, brute force, finite
@@ -238,6 +242,37 @@ def decode_paged(q, k_cache, v_cache, block_table, seqlens, sink, scale, window=
                          causal=False, window=None)
         o[b] = ob[0, 0]
         lse[b] = lb[0, :, 0]
+    return o, lse
+
+
+def extend_paged(q, cu_seqlens_q, k_cache, v_cache, block_table, seqlens, sink, scale,
+                 window=None):
+    """Chunked prefill (extend): packed new queries against a paged KV cache.
+
+    The extend path receives the same sink as decode ([trtllm] Summary of
+    Changes), and the variable-length functions take it too ([FA-sink]
+    Description).  Sequence b's queries are rows cu_seqlens_q[b] ..
+    cu_seqlens_q[b+1]-1 of q [total_q, Hq, D].  They are the last nq_b tokens
+    of a context of L_b = seqlens[b] tokens whose K/V (theirs included) are
+    already in the cache, so query i of b sits at position L_b - nq_b + i and
+    sees keys by the prefill rule: bottom-right causal and, with a window, the
+    first W1 and last W2 positions relative to itself.
+    Returns (o [total_q, Hq, D], lse [Hq, total_q]).
+    """
+    q = _f64(q)
+    total, Hq, D = q.shape
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ks, vs = gather_kv(k_cache, v_cache, block_table, seqlens, k_cache.shape[1], None)
+    o = np.zeros((total, Hq, D))
+    lse = np.full((Hq, total), NEG_INF)
+    for b in range(len(ks)):
+        a, e = int(cu[b]), int(cu[b + 1])
+        if e == a:
+            continue
+        ob, lb = prefill(q[a:e][None], ks[b][None], vs[b][None], sink, scale, causal=True,
+                         window=window)
+        o[a:e] = ob[0]
+        lse[:, a:e] = lb[0]
     return o, lse
 
 
