@@ -102,6 +102,38 @@ int attn_sink_fwd_prefill(const void* q, const void* k, const void* v, const flo
                           int dtype, void* hip_stream);
 
 /*
+ * Chunked prefill (extend) against a paged KV cache.  Sequence b's nq_b new
+ * query tokens are rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q; they are
+ * the last nq_b of its L_b = seqlens_k[b] tokens, whose K/V (theirs included)
+ * are already in the cache.  Row i of sequence b sits at position
+ * L_b - nq_b + i and sees key j iff j <= that position and, with a window,
+ * j < window_first or j > position - window_last (flash-attention PR #1819,
+ * Description: the variable-length functions take the sink; sglang PR #8825,
+ * Summary of Changes: so does the extend path).
+ *   q            [total_q, Hq, D] bf16, packed
+ *   k_cache,
+ *   v_cache      [num_pages, page_size, Hkv, D] bf16
+ *   block_table  [B, max_pages_per_seq] int32, as for the paged decode
+ *   cu_seqlens_q [B+1] int32 device: 0 = cu[0] <= cu[1] <= ... <= cu[B] = total_q
+ *   seqlens_k    [B] int32 device, L_b (at most max_pages_per_seq * page_size)
+ *   sink         [Hq] fp32 or NULL
+ *   o            [total_q, Hq, D] bf16                -- output
+ *   lse          [Hq, total_q] fp32 or NULL           -- output
+ *   max_seqlen_q host-side upper bound of every nq_b
+ * Rows placed before the context (position < 0, when nq_b > L_b) see no key:
+ * O = 0 and LSE = sink (or -inf).  Requirements: D in {64, 128}; page_size a
+ * power of two in [1, 256]; Hq % Hkv == 0; bf16.  The device arrays are not
+ * checked: cu_seqlens_q and seqlens_k must hold the stated ranges.
+ */
+int attn_sink_fwd_extend_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* cu_seqlens_q,
+                               const int32_t* seqlens_k, const float* sink, void* o, float* lse,
+                               int B, int total_q, int max_seqlen_q, int Hq, int Hkv, int D,
+                               int page_size, int max_pages_per_seq, int num_pages,
+                               float softmax_scale, int window_first, int window_last, int dtype,
+                               void* hip_stream);
+
+/*
  * Forward paged decode: one new query token per sequence, whose K/V is already
  * stored in the cache and counted in seqlens_k.
  *   q            [B, Hq, D] bf16

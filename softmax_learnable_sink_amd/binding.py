@@ -29,6 +29,7 @@ _SIGNATURES = {
     "attn_sink_last_error": ([], ctypes.c_char_p),
     "attn_sink_fwd_prefill": ([_vp, _vp, _vp, _vp, _vp, _vp] + [_i] * 6 + [_f, _i, _i, _i, _i, _vp], _i),
     "attn_sink_fwd_decode_paged": ([_vp] * 8 + [_i] * 7 + [_f, _i, _i, _i, _vp, _sz, _i, _vp], _i),
+    "attn_sink_fwd_extend_paged": ([_vp] * 9 + [_i] * 9 + [_f, _i, _i, _i, _vp], _i),
     "attn_sink_decode_workspace_bytes": ([_i] * 9, _sz),
     "attn_sink_bwd": ([_vp] * 11 + [_i] * 6 + [_f, _i, _i, _i, _vp, _sz, _i, _vp], _i),
     "attn_sink_bwd_workspace_bytes": ([_i] * 6, _sz),
@@ -181,6 +182,45 @@ def attn_sink_fwd_decode_paged(q, k_cache, v_cache, block_table, seqlens_k, sink
         _ptr(out), _ptr(lse), B, Hq, Hkv, D, page_size, max_pages, num_pages, scale, w1, w2,
         num_splits, _ptr(workspace), workspace.numel() * workspace.element_size(), BF16,
         _stream(dev)))
+    return out, lse
+
+
+def attn_sink_fwd_extend_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
+                               max_seqlen_q, sink=None, softmax_scale=None, window=None,
+                               out=None, lse=None, return_lse=True):
+    """O [total_q,Hq,D], LSE [Hq,total_q] for packed new queries q [total_q,Hq,D] (rows of
+    sequence b: cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1) against a paged KV cache holding
+    seqlens_k[b] tokens of sequence b, the new ones last.  max_seqlen_q bounds every
+    sequence's number of new queries (host int)."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _need(seqlens_k, "seqlens_k", torch.int32, dev)
+    total_q, Hq, D = q.shape
+    num_pages, page_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (num_pages, page_size, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [num_pages, page_size, Hkv, D]")
+    B = seqlens_k.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != B or cu_seqlens_q.shape != (B + 1,):
+        raise ValueError("block_table must be [B, max_pages], cu_seqlens_q [B+1], seqlens_k [B]")
+    if sink is not None:
+        _need(sink, "sink", torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    w1, w2 = _window(window)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib().attn_sink_fwd_extend_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cu_seqlens_q),
+        _ptr(seqlens_k), _ptr(sink), _ptr(out), _ptr(lse), B, total_q, int(max_seqlen_q), Hq, Hkv,
+        D, page_size, block_table.shape[1], num_pages, scale, w1, w2, BF16, _stream(dev)))
     return out, lse
 
 

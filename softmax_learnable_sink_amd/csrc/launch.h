@@ -24,6 +24,23 @@ struct PrefillArgs {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
+struct ExtendArgs {
+  const void* q;  // packed [total_q, Hq, D]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seqlens_k;
+  const float* sink;
+  void* o;
+  float* lse;  // [Hq, total_q] or NULL
+  int B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages, num_pages;
+  float scale;
+  int w1, w2;
+};
+
+hipError_t launch_extend_paged_bf16(const ExtendArgs& a, hipStream_t stream);
+
 struct DecodeArgs {
   const void* q;
   const void* k_cache;

@@ -160,7 +160,8 @@ struct WaveRows {
   f32x16 acc[D / 32][QB];
   float sig2;
 
-  __device__ __forceinline__ void init(const __bf16* q, const float* sink, int b, int Sq, int Hq,
+  // qrow0: row 0 of this sequence in a [rows, Hq, D] layout; rows >= Sq are zero.
+  __device__ __forceinline__ void init(const __bf16* qrow0, const float* sink, int Sq, int Hq,
                                        int h, int wrow0, int hh, int l32) {
     // Q^T fragments (B operand): query row wrow0 + 32*qb + l32, d = 16*ks + 8*hh ..
 #pragma unroll
@@ -170,7 +171,7 @@ struct WaveRows {
       for (int ks = 0; ks < D / 16; ++ks) {
         if (row < Sq) {
           qf[qb][ks] = *reinterpret_cast<const bf16x8*>(
-              q + (((size_t)b * Sq + row) * Hq + h) * D + 16 * ks + 8 * hh);
+              qrow0 + ((size_t)row * Hq + h) * D + 16 * ks + 8 * hh);
         } else {
           qf[qb][ks] = bf16x8{};
         }
@@ -289,7 +290,9 @@ struct WaveRows {
   }
 
   // Fold the sink into the denominator once, normalise, store O and LSE.
-  __device__ __forceinline__ void finish(__bf16* o, float* lse, int b, int Sq, int Hq, int h,
+  // orow0: row 0 of this sequence in O [rows, Hq, D]; lse_row0: this head's
+  // LSE of row 0 (rows contiguous), or NULL.
+  __device__ __forceinline__ void finish(__bf16* orow0, float* lse_row0, int Sq, int Hq, int h,
                                          int wrow0, int hh, int l32) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -298,7 +301,7 @@ struct WaveRows {
       if (sig2 != kNegInf) lt += exp2_fast(sig2 - m[qb]);
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       if (row < Sq) {
-        __bf16* orow = o + (((size_t)b * Sq + row) * Hq + h) * D;
+        __bf16* orow = orow0 + ((size_t)row * Hq + h) * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -308,9 +311,8 @@ struct WaveRows {
                 to_bf16x4(x[4 * a] * inv, x[4 * a + 1] * inv, x[4 * a + 2] * inv,
                           x[4 * a + 3] * inv);
           }
-        if (lse && hh == 0)
-          lse[((size_t)b * Hq + h) * Sq + row] =
-              lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : kNegInf;
+        if (lse_row0 && hh == 0)
+          lse_row0[row] = lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : kNegInf;
       }
     }
   }
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
                      off + wrow0 + l32};
 
   WaveRows<D, QB> wr;
-  wr.init(q, sink, b, Sq, Hq, h, wrow0, hh, l32);
+  wr.init(q + (size_t)b * Sq * Hq * D, sink, Sq, Hq, h, wrow0, hh, l32);
 
   const size_t rs = (size_t)Hkv * D;
   const __bf16* kbase = k + ((size_t)b * Sk * Hkv + kvh) * D;
@@ -376,7 +378,137 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     if (it + 1 < ntiles) regs.store(s, buf ^ 1, tid);
     __syncthreads();
   }
-  wr.finish(o, lse, b, Sq, Hq, h, wrow0, hh, l32);
+  wr.finish(o + (size_t)b * Sq * Hq * D, lse ? lse + ((size_t)b * Hq + h) * Sq : nullptr, Sq, Hq,
+            h, wrow0, hh, l32);
+}
+
+// ---------------------------------------------------------------------------
+// Chunked prefill (extend) against a paged KV cache.  Sequence b's nq new
+// queries are rows cu_q[b] .. cu_q[b+1]-1 of a packed [total_q, Hq, D] tensor
+// and the last nq tokens of its L = seqlens[b] cached tokens, so row i sits at
+// position L - nq + i (sglang PR #8825, Summary of Changes: the extend path
+// takes the same sink; flash-attention PR #1819, Description: so do the
+// variable-length functions).  The same 4-wave tile steps as the prefill run
+// on K/V tiles gathered from the cache through the block table.
+// ---------------------------------------------------------------------------
+
+// One 64-key tile of K and V gathered from the paged cache.  Each thread owns
+// KN (row, 16-byte chunk) items; their slots come from block-table entries
+// fetched two tiles ahead.  Keys at or past L read slot 0 and are written to
+// LDS as zero V rows (their scores are masked anyway).
+template <int D>
+struct PagedTile {
+  static constexpr int CH = D / 8;
+  static constexpr int KN = kBN * CH / kThreads;
+  uint4 kr[KN], vr[KN];
+  int page[KN];   // block-table entries of the tile being fetched
+  int slot[KN];   // slots of the tile to load next (-1: past the context)
+
+  __device__ __forceinline__ static int row_of(int tid, int i) { return (tid + i * kThreads) / CH; }
+  __device__ __forceinline__ static int chunk_of(int tid, int i) { return (tid + i * kThreads) % CH; }
+
+  __device__ __forceinline__ void fetch_pages(const int32_t* bt_row, int key0, int L, int shift,
+                                              int tid) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) page[i] = bt_row[min(key0 + row_of(tid, i), L - 1) >> shift];
+  }
+  __device__ __forceinline__ void pages_to_slots(int key0, int L, int shift, int tid) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int key = key0 + row_of(tid, i);
+      slot[i] = key < L ? (page[i] << shift) | (key & ((1 << shift) - 1)) : -1;
+    }
+  }
+  __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, size_t rs,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const size_t off = (size_t)max(slot[i], 0) * rs + chunk_of(tid, i) * 8;
+      kr[i] = *reinterpret_cast<const uint4*>(kbase + off);
+      vr[i] = *reinterpret_cast<const uint4*>(vbase + off);
+    }
+  }
+  __device__ __forceinline__ void store(Lds<D>& s, int buf, int tid) const {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int key = row_of(tid, i), c = chunk_of(tid, i);
+      const int row = (key & ~31) + k_lds_row(key & 31);
+      const bool ok = slot[i] >= 0;
+      *reinterpret_cast<uint4*>(&s.k[buf][row * Lds<D>::KS + c * 8]) = kr[i];
+      *reinterpret_cast<uint4*>(&s.v[buf][key * Lds<D>::VS + c * 8]) =
+          uint4{ok ? vr[i].x : 0u, ok ? vr[i].y : 0u, ok ? vr[i].z : 0u, ok ? vr[i].w : 0u};
+    }
+  }
+};
+
+template <int D, int QB>
+__global__ __launch_bounds__(kThreads, 2) void extend_paged_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ seqlens, const float* __restrict__ sink, __bf16* __restrict__ o,
+    float* __restrict__ lse, int B, int total_q, int max_sq, int Hq, int Hkv, int hpw,
+    int page_shift, int max_pages, float sl2, int w1, int w2) {
+  __shared__ Lds<D> s;
+  constexpr int RW = 32 * QB;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int g = Hq / Hkv;
+  const int groups = g / hpw;
+  const int R = RW * (4 / hpw);
+  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (max_sq + R - 1) / R);
+  const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
+  const int qbase = cu_q[b], nq = cu_q[b + 1] - qbase;
+  const int row0 = wi.tile * R;
+  if (row0 >= nq) return;  // uniform over the workgroup
+  const int h = kvh * g + wi.grp * hpw + (wave % hpw);
+  const int rb = wave / hpw;
+  const int wrow0 = row0 + rb * RW;
+  const int L = seqlens[b];
+  const int off = L - nq;
+  const RowGeom geom{L, 1, w1, w2, off + row0, off + min(nq, row0 + R) - 1, off + wrow0 + l32};
+
+  WaveRows<D, QB> wr;
+  wr.init(q + (size_t)qbase * Hq * D, sink, nq, Hq, h, wrow0, hh, l32);
+
+  const size_t rs = (size_t)Hkv * D;
+  const __bf16* kbase = kc + (size_t)kvh * D;
+  const __bf16* vbase = vc + (size_t)kvh * D;
+  const int32_t* bt_row = bt + (size_t)b * max_pages;
+  const TileRange tr = tile_range(L, geom.p_min, geom.p_max, 1, w1, w2);
+  const int nt = tr.count();
+
+  __builtin_amdgcn_s_waitcnt(0);
+  if (nt > 0) {
+    PagedTile<D> pt;
+    pt.fetch_pages(bt_row, tr.tile(0) * kBN, L, page_shift, tid);
+    pt.pages_to_slots(tr.tile(0) * kBN, L, page_shift, tid);
+    pt.load(kbase, vbase, rs, tid);
+    pt.store(s, 0, tid);
+    if (nt > 1) {
+      pt.fetch_pages(bt_row, tr.tile(1) * kBN, L, page_shift, tid);
+      pt.pages_to_slots(tr.tile(1) * kBN, L, page_shift, tid);
+    }
+    __syncthreads();
+    for (int it = 0; it < nt; ++it) {
+      const int buf = it & 1;
+      if (it + 1 < nt) pt.load(kbase, vbase, rs, tid);
+      if (it + 2 < nt) pt.fetch_pages(bt_row, tr.tile(it + 2) * kBN, L, page_shift, tid);
+      f32x16 st[2][QB];
+      bf16x8 pf[2][QB][2];
+      wr.scores(s.k[buf], st, l32, hh);
+      wr.softmax(st, pf, tr.tile(it) * kBN, geom, sl2, hh);
+      wr.pv(s.v[buf], pf, lane);
+      if (it + 1 < nt) pt.store(s, buf ^ 1, tid);
+      if (it + 2 < nt) pt.pages_to_slots(tr.tile(it + 2) * kBN, L, page_shift, tid);
+      __syncthreads();
+    }
+  }
+  wr.finish(o + (size_t)qbase * Hq * D, lse ? lse + (size_t)h * total_q + qbase : nullptr, nq,
+            Hq, h, wrow0, hh, l32);
 }
 
 // ---------------------------------------------------------------------------
@@ -470,6 +602,33 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     prefill_bf16_kernel<128, 1><<<grid, block, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.B,
                                                             a.Sq, a.Sk, a.Hq, a.Hkv, hpw, sl2,
                                                             a.causal, a.w1, a.w2);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_extend_paged_bf16(const ExtendArgs& a, hipStream_t stream) {
+  const int g = a.Hq / a.Hkv;
+  const int hpw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
+  const float sl2 = a.scale * kLog2e;
+  int shift = 0;
+  while ((1 << shift) < a.page_size) ++shift;
+  const auto* q = static_cast<const __bf16*>(a.q);
+  const auto* kc = static_cast<const __bf16*>(a.k_cache);
+  const auto* vc = static_cast<const __bf16*>(a.v_cache);
+  auto* o = static_cast<__bf16*>(a.o);
+  const int cols = a.B * a.Hkv * (g / hpw);
+  if (a.D == 64) {
+    const int R = 64 * (4 / hpw);
+    const dim3 grid(cols * ((a.max_seqlen_q + R - 1) / R));
+    extend_paged_kernel<64, 2><<<grid, kThreads, 0, stream>>>(
+        q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.sink, o, a.lse, a.B, a.total_q,
+        a.max_seqlen_q, a.Hq, a.Hkv, hpw, shift, a.max_pages, sl2, a.w1, a.w2);
+  } else {
+    const int R = 32 * (4 / hpw);
+    const dim3 grid(cols * ((a.max_seqlen_q + R - 1) / R));
+    extend_paged_kernel<128, 1><<<grid, kThreads, 0, stream>>>(
+        q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.sink, o, a.lse, a.B, a.total_q,
+        a.max_seqlen_q, a.Hq, a.Hkv, hpw, shift, a.max_pages, sl2, a.w1, a.w2);
   }
   return hipGetLastError();
 }

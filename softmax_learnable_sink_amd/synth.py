@@ -144,14 +144,14 @@ def decode_case(B, Hq, Hkv, D, page_size, len_lo, len_hi, dtype=BF16, seed=0,
 
 
 def extend_case(B, Hq, Hkv, D, page_size, q_lo, q_hi, ctx_lo, ctx_hi, dtype=BF16, seed=0,
-                sink=True, q_lens=None, ctx_lens=None):
+                sink=True, q_lens=None, ctx_lens=None, nan_poison=False):
     """Chunked-prefill inputs: packed new queries against a paged cache.
 
     Sequence b has nq_b ~ U[q_lo, q_hi] new tokens (or `q_lens`) on top of
     c_b ~ U[ctx_lo, ctx_hi] cached tokens (or `ctx_lens`); its context length
     is L_b = c_b + nq_b and its cache holds all L_b tokens.  q is packed
-    [total_q, Hq, D] with cu_seqlens_q [B+1]; pages are handed out as in
-    decode_case.
+    [total_q, Hq, D] with cu_seqlens_q [B+1]; pages are handed out (and, with
+    nan_poison, the slots past L_b poisoned) as in decode_case.
     """
     rng = np.random.default_rng((int(seed), 2000))
     if q_lens is None:
@@ -163,7 +163,7 @@ def extend_case(B, Hq, Hkv, D, page_size, q_lo, q_hi, ctx_lo, ctx_hi, dtype=BF16
     cu = np.zeros(B + 1, dtype=np.int32)
     cu[1:] = np.cumsum(q_lens)
     case = decode_case(B, Hq, Hkv, D, page_size, 0, 0, dtype=dtype, seed=seed, sink=sink,
-                       lengths=np.maximum(L, 1))
+                       lengths=np.maximum(L, 1), nan_poison=nan_poison)
     dr = _Draws(seed)
     dr.n = 100  # a tensor number of its own: the packed queries
     case["q"] = dr.normal((int(cu[-1]), Hq, D), dtype)

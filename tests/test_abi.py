@@ -34,6 +34,7 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("attn_sink_fwd_prefill", "attn_sink_fwd_decode_paged", "attn_sink_bwd",
+              "attn_sink_fwd_extend_paged",
               "attn_sink_decode_workspace_bytes", "attn_sink_bwd_workspace_bytes",
               "attn_sink_decode_select_slots", "attn_sink_gather_kv", "attn_sink_last_error",
               "attn_sink_abi_version"):
@@ -125,6 +126,39 @@ def test_decode_workspace_query(lib):
     b = binding.attn_sink_decode_workspace_bytes(4, 8, 2, 64, 16, 64, None, 8)
     assert 0 < a < b
     assert binding.attn_sink_decode_workspace_bytes(4, 8, 2, 96, 16, 64) == 0
+
+
+def _extend(lib, **kw):
+    a = dict(B=2, tq=10, mq=6, Hq=8, Hkv=2, D=64, P=16, maxp=4, npages=8, scale=0.125, w1=-1,
+             w2=-1, dtype=binding.BF16, q=P, cu=P, sl=P, bt=P)
+    a.update(kw)
+    return lib.attn_sink_fwd_extend_paged(a["q"], P, P, a["bt"], a["cu"], a["sl"], None, P, None,
+                                          a["B"], a["tq"], a["mq"], a["Hq"], a["Hkv"], a["D"],
+                                          a["P"], a["maxp"], a["npages"], a["scale"], a["w1"],
+                                          a["w2"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dtype=binding.F32), binding.ERR_UNSUPPORTED, "bf16"),
+    (dict(B=0), binding.ERR_INVALID_ARG, "B >= 1"),
+    (dict(tq=-1), binding.ERR_INVALID_ARG, "total_q >= 0"),
+    (dict(D=96), binding.ERR_UNSUPPORTED, "64 or 128"),
+    (dict(Hq=9), binding.ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(P=24), binding.ERR_UNSUPPORTED, "power of two"),
+    (dict(npages=0), binding.ERR_INVALID_ARG, "num_pages"),
+    (dict(cu=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(q=P_ODD), binding.ERR_INVALID_ARG, "aligned"),
+    (dict(w1=3, w2=0), binding.ERR_INVALID_ARG, "window"),
+    (dict(scale=-1.0), binding.ERR_INVALID_ARG, "softmax_scale"),
+])
+def test_extend_rejects(lib, kw, status, msg):
+    assert _extend(lib, **kw) == status
+    assert msg in binding.last_error()
+
+
+def test_extend_with_no_rows_is_a_no_op(lib):
+    # no new query anywhere: accepted, and nothing is launched (no GPU needed)
+    assert _extend(lib, tq=0, mq=0) == binding.OK
 
 
 def _bwd(lib, **kw):
