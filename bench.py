@@ -5,6 +5,8 @@ One step runs every entry point once over its synthetic workload:
   decode    B64, 64/8 heads, D64, page 16, L ~ U[1024, 32768], sink
   window32  B32, 32/8 heads, D128, page 16, L ~ U[16384, 65536], window 1024+7168, sink
   window1   the same with B1 (latency bound, reported only)
+  extend    chunked prefill: B2 x 4096 new tokens on 4096..12288 cached ones, 64/8 heads,
+            D64, page 16, sink (packed queries against the paged cache)
   train     B2, S8192, 64/8 heads, D64, causal: forward + backward with dSink
 Each entry point is bracketed by HIP events on the stream it is launched on;
 `value` is the prefill throughput in TFLOP/s of algorithmic work (4*D flops per
@@ -29,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill attention TFLOP/s + paged-decode HBM GB/s (% of MI355X roofline)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-PARTS = ("prefill", "decode", "window32", "window1", "train")
+PARTS = ("prefill", "decode", "window32", "window1", "extend", "train")
 
 
 def causal_pairs(B, Hq, Sq, Sk):
@@ -59,6 +61,7 @@ TRAFFIC_KERNELS = {  # key in hbm_traffic.json -> (kernel-name substring, source
     "decode_partial_kernel": ("decode_partial_kernelILi64", "decode"),
     "decode_combine_kernel": ("decode_combine_kernelILi64", "decode"),
     "decode_partial_kernel_d128": ("decode_partial_kernelILi128", "decode"),
+    "extend_paged_kernel": ("extend_paged_kernelILi64ELi2", "prefill"),
 }
 
 
@@ -175,6 +178,26 @@ class Workloads:
             setattr(self, name, d)
             if name == "decode":
                 self.dec_case = c
+        if "extend" in parts:
+            B, Hq, Hkv, D = 2, 64, 8, 64
+            c = synth.extend_case(B, Hq, Hkv, D, 16, 4096, 4096, 4096, 12288, seed=0)
+            e = dict(q=dt(c["q"]), k=dt(c["k_cache"]), v=dt(c["v_cache"]),
+                     bt=i32(c["block_table"]), cu=i32(c["cu_seqlens_q"]), sl=i32(c["seqlens"]),
+                     sink=torch.from_numpy(c["sink"]).to(dev), max_sq=c["max_seqlen_q"])
+            e["o"] = torch.empty_like(e["q"])
+            e["lse"] = torch.empty((Hq, e["q"].shape[0]), dtype=torch.float32, device=dev)
+            nq = np.diff(c["cu_seqlens_q"]).astype(np.int64)
+            L = c["seqlens"].astype(np.int64)
+            pairs = int(Hq * (nq * (L - nq) + nq * (nq + 1) // 2).sum())
+            tq = int(nq.sum())
+            # Q in, O out (bf16), LSE out, K and V of every context token, one
+            # block-table entry per page, cu_seqlens, seqlens, sink
+            io = (2 * 2 * tq * Hq * D + 4 * Hq * tq + int(L.sum()) * Hkv * D * 2 * 2
+                  + 4 * int(((L + 15) // 16).sum()) + 4 * (2 * B + 1) + 4 * Hq)
+            self.info["extend"] = dict(flops=4 * D * pairs, pairs=pairs, bytes=io,
+                                       shape=f"B{B} nq{int(nq[0])} L~U[8192,16384] H{Hq}/{Hkv} "
+                                             f"D{D} P16 causal bf16")
+            self.ext = e
         if "train" in parts:
             B, S, Hq, Hkv, D = 2, 8192, 64, 8, 64
             c = synth.prefill_case(B, S, S, Hq, Hkv, D, seed=0, dout=True)
@@ -207,6 +230,11 @@ class Workloads:
             binding.attn_sink_fwd_decode_paged(d["q"], d["k"], d["v"], d["bt"], d["sl"], d["sink"],
                                                softmax_scale=1 / math.sqrt(D), window=d["window"],
                                                out=d["o"], lse=d["lse"], workspace=d["ws"])
+        elif name == "extend":
+            e = self.ext
+            binding.attn_sink_fwd_extend_paged(e["q"], e["k"], e["v"], e["bt"], e["cu"], e["sl"],
+                                               e["max_sq"], e["sink"], softmax_scale=0.125,
+                                               out=e["o"], lse=e["lse"])
         elif name == "train":
             t = self.tr
             binding.attn_sink_fwd_prefill(t["q"], t["k"], t["v"], t["sink"], causal=True,
@@ -332,7 +360,7 @@ def main():
             gbps = info["bytes"] / (ms[p] * 1e-3) / 1e9
             rec.update(gbps=round(gbps, 2), hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
                        algorithmic_bytes=info["bytes"])
-        if p in ("prefill", "train"):
+        if p in ("prefill", "extend", "train"):
             tf = info["flops"] / (ms[p] * 1e-3) / 1e12
             rec.update(tflops=round(tf, 2), mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4),
                        algorithmic_flops=info["flops"])
