@@ -18,4 +18,6 @@ from .sink_attention import (  # noqa: F401
     decode_paged,
     extend_paged,
     backward,
+    prefill_varlen,
+    backward_varlen,
 )

@@ -40,6 +40,10 @@ Readings where the pages are silent (each also listed in the design doc):
     L cached tokens, so new token i sits at position L - nq + i and sees keys
     by the prefill rule above, the window included (the pages define the
     window for decode only; the per-query rule is its prefill form).
+  * variable-length (packed) forward and backward: each sequence is its own
+    attention problem with its own Sq and Sk (bottom-right causal inside the
+    sequence); no key of one sequence is visible to a query of another; the
+    sink gradient sums over all sequences' rows.
 
 Parity status: every function below is pinned by tests that do not retype
 its formula (closed forms, library special cases, brute force, finite
@@ -325,4 +329,69 @@ def backward(q, k, v, sink, dout, scale, causal=True, window=None, row_block=102
                 L = lse[b, h, :]
                 psink = np.where(np.isfinite(L), np.exp(sig[h] - np.where(np.isfinite(L), L, 0.0)), 0.0)
                 dsink[h] -= np.sum(psink * di[b, h, :])
+    return dq, dk, dv, dsink, o, lse
+
+
+def _cu(cu):
+    cu = np.asarray(cu, dtype=np.int64)
+    assert cu[0] == 0 and np.all(np.diff(cu) >= 0), "cu_seqlens must start at 0 and not decrease"
+    return cu
+
+
+def prefill_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, sink, scale, causal=True, window=None):
+    """Packed variable-length forward ([FA-sink] Description: the variable-
+    length counterparts take the sink too).
+
+    q [total_q, Hq, D], k/v [total_k, Hkv, D].  Sequence b owns query rows
+    cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+    cu_seqlens_k[b+1]-1 and is the prefill problem on those slices alone.
+    Returns (o [total_q, Hq, D], lse [Hq, total_q]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cq, ck = _cu(cu_seqlens_q), _cu(cu_seqlens_k)
+    assert len(cq) == len(ck) and cq[-1] == q.shape[0] and ck[-1] == k.shape[0]
+    total, Hq, D = q.shape
+    o = np.zeros((total, Hq, D))
+    lse = np.full((Hq, total), NEG_INF)
+    for b in range(len(cq) - 1):
+        a, e = int(cq[b]), int(cq[b + 1])
+        if e == a:
+            continue
+        ka, ke = int(ck[b]), int(ck[b + 1])
+        ob, lb = prefill(q[a:e][None], k[ka:ke][None], v[ka:ke][None], sink, scale, causal,
+                         window)
+        o[a:e] = ob[0]
+        lse[:, a:e] = lb[0]
+    return o, lse
+
+
+def backward_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, sink, dout, scale, causal=True,
+                    window=None):
+    """Gradients of L = sum(dout * O) for prefill_varlen ([FA-sink]
+    Description: the backward returns the sink's gradient).
+
+    The sequences share no score, so each sequence's dq, dk, dv are the
+    backward above on its own slices, and dsink is the sum of the
+    per-sequence sink gradients.
+    Returns (dq, dk, dv, dsink, o [total_q, Hq, D], lse [Hq, total_q]).
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cq, ck = _cu(cu_seqlens_q), _cu(cu_seqlens_k)
+    assert len(cq) == len(ck) and cq[-1] == q.shape[0] and ck[-1] == k.shape[0]
+    total, Hq, D = q.shape
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dsink = np.zeros(Hq)
+    o = np.zeros((total, Hq, D))
+    lse = np.full((Hq, total), NEG_INF)
+    for b in range(len(cq) - 1):
+        a, e = int(cq[b]), int(cq[b + 1])
+        ka, ke = int(ck[b]), int(ck[b + 1])
+        if e == a:
+            continue  # no query row: no score, every gradient of the slice is 0
+        r = backward(q[a:e][None], k[ka:ke][None], v[ka:ke][None], sink, dout[a:e][None], scale,
+                     causal, window)
+        dq[a:e], dk[ka:ke], dv[ka:ke] = r[0][0], r[1][0], r[2][0]
+        dsink += r[3]
+        o[a:e] = r[4][0]
+        lse[:, a:e] = r[5][0]
     return dq, dk, dv, dsink, o, lse
