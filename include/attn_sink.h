@@ -134,6 +134,34 @@ int attn_sink_fwd_extend_paged(const void* q, const void* k_cache, const void* v
                                void* hip_stream);
 
 /*
+ * Variable-length (packed) forward.  Sequence b's queries are rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and its keys rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v; it is the prefill problem
+ * on those rows alone (flash-attention PR #1819, Description: the
+ * variable-length functions take the sink).  With nq_b queries and nk_b keys,
+ * causal masking is bottom-right inside the sequence: row i sits at position
+ * nk_b - nq_b + i and sees key j iff j <= that position and, with a window,
+ * j < window_first or j > position - window_last.
+ *   q            [total_q, Hq, D] bf16, packed (q and o may be NULL iff total_q == 0)
+ *   k, v         [total_k, Hkv, D] bf16, packed (NULL allowed iff total_k == 0)
+ *   cu_seqlens_q [B+1] int32 device: 0 = cu[0] <= ... <= cu[B] = total_q
+ *   cu_seqlens_k [B+1] int32 device: 0 = cu[0] <= ... <= cu[B] = total_k
+ *   sink         [Hq] fp32 or NULL
+ *   o            [total_q, Hq, D] bf16                -- output
+ *   lse          [Hq, total_q] fp32 or NULL           -- output
+ *   max_seqlen_q host-side upper bound of every nq_b
+ * A row that sees no key gets O = 0 and LSE = sink (or -inf).  Requirements:
+ * D in {64, 128}; Hq % Hkv == 0; bf16; the window needs causal = 1.  Size
+ * limits: total_q*Hq and total_k*Hkv < 2^31.  The device arrays are not
+ * checked: they must hold the stated ranges.
+ */
+int attn_sink_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, const float* sink, void* o, float* lse,
+                         int B, int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv,
+                         int D, float softmax_scale, int causal, int window_first,
+                         int window_last, int dtype, void* hip_stream);
+
+/*
  * Forward paged decode: one new query token per sequence, whose K/V is already
  * stored in the cache and counted in seqlens_k.
  *   q            [B, Hq, D] bf16
@@ -193,6 +221,39 @@ int attn_sink_bwd(const void* q, const void* k, const void* v, const void* o, co
 
 /* Workspace needed by attn_sink_bwd (0 on invalid arguments). */
 size_t attn_sink_bwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D);
+
+/*
+ * Backward of the variable-length forward (bf16): gradients of sum(dO * O)
+ * for attn_sink_fwd_varlen with the same sequences, mask and scale
+ * (flash-attention PR #1819, Description: the variable-length functions take
+ * the sink and the backward returns its gradient).
+ *   q, o, dout     [total_q, Hq, D]; k, v [total_k, Hkv, D]
+ *   lse            [Hq, total_q] fp32 from the forward (sink included)
+ *   cu_seqlens_q,
+ *   cu_seqlens_k   [B+1] int32 device, as in the forward
+ *   dq             [total_q, Hq, D], dk, dv [total_k, Hkv, D] bf16 -- outputs;
+ *                  keys no query sees get dk = dv = 0
+ *   dsink          [Hq] fp32, required iff sink != NULL: the sum over all
+ *                  sequences' rows, reduced in fp32 in a fixed order -- output
+ *   max_seqlen_q,
+ *   max_seqlen_k   host-side upper bounds of every sequence's nq_b and nk_b
+ * workspace: at least attn_sink_bwd_varlen_workspace_bytes() bytes.
+ * Size limits (ATTN_SINK_ERR_UNSUPPORTED past them): B and
+ * ceil(max_seqlen_k/128) <= 65535, total_q*Hq and total_k*Hkv < 2^31, one
+ * sequence's K/V slice (max_seqlen_k*Hkv*D*2 bytes) and Q/dO slice
+ * (max_seqlen_q*Hq*D*2 bytes) <= 4 GiB - 1.  The device arrays are not
+ * checked: they must hold the stated ranges.
+ */
+int attn_sink_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, const float* sink,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq,
+                         void* dk, void* dv, float* dsink, int B, int total_q, int total_k,
+                         int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int D,
+                         float softmax_scale, int causal, int window_first, int window_last,
+                         void* workspace, size_t workspace_bytes, int dtype, void* hip_stream);
+
+/* Workspace needed by attn_sink_bwd_varlen (0 on invalid arguments). */
+size_t attn_sink_bwd_varlen_workspace_bytes(int B, int total_q, int max_seqlen_q, int Hq);
 
 /*
  * Test / debug exports that run the same device index map as the decode

@@ -30,9 +30,12 @@ _SIGNATURES = {
     "attn_sink_fwd_prefill": ([_vp, _vp, _vp, _vp, _vp, _vp] + [_i] * 6 + [_f, _i, _i, _i, _i, _vp], _i),
     "attn_sink_fwd_decode_paged": ([_vp] * 8 + [_i] * 7 + [_f, _i, _i, _i, _vp, _sz, _i, _vp], _i),
     "attn_sink_fwd_extend_paged": ([_vp] * 9 + [_i] * 9 + [_f, _i, _i, _i, _vp], _i),
+    "attn_sink_fwd_varlen": ([_vp] * 8 + [_i] * 7 + [_f, _i, _i, _i, _i, _vp], _i),
     "attn_sink_decode_workspace_bytes": ([_i] * 9, _sz),
     "attn_sink_bwd": ([_vp] * 11 + [_i] * 6 + [_f, _i, _i, _i, _vp, _sz, _i, _vp], _i),
     "attn_sink_bwd_workspace_bytes": ([_i] * 6, _sz),
+    "attn_sink_bwd_varlen": ([_vp] * 13 + [_i] * 8 + [_f, _i, _i, _i, _vp, _sz, _i, _vp], _i),
+    "attn_sink_bwd_varlen_workspace_bytes": ([_i] * 4, _sz),
     "attn_sink_decode_select_slots": ([_vp, _vp] + [_i] * 5 + [_vp, _vp, _i, _vp], _i),
     "attn_sink_gather_kv": ([_vp] * 4 + [_i] * 7 + [_vp, _vp, _i, _i, _vp], _i),
 }
@@ -224,6 +227,44 @@ def attn_sink_fwd_extend_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, s
     return out, lse
 
 
+def attn_sink_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, sink=None,
+                         causal=True, softmax_scale=None, window=None, out=None, lse=None,
+                         return_lse=True):
+    """O [total_q,Hq,D], LSE [Hq,total_q] for packed sequences: sequence b's queries are rows
+    cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q [total_q,Hq,D] and its keys rows
+    cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k, v [total_k,Hkv,D].  max_seqlen_q bounds
+    every sequence's number of queries (host int)."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, dev)
+    _need(v, "v", torch.bfloat16, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+    total_q, Hq, D = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    if k.shape != (total_k, Hkv, D) or v.shape != k.shape:
+        raise ValueError("k/v must be [total_k, Hkv, D]")
+    B = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B+1]")
+    if sink is not None:
+        _need(sink, "sink", torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    w1, w2 = _window(window)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib().attn_sink_fwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(sink),
+        _ptr(out), _ptr(lse), B, total_q, total_k, int(max_seqlen_q), Hq, Hkv, D, scale,
+        int(bool(causal)), w1, w2, BF16, _stream(dev)))
+    return out, lse
+
+
 def attn_sink_bwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D):
     return lib().attn_sink_bwd_workspace_bytes(B, Sq, Sk, Hq, Hkv, D)
 
@@ -252,6 +293,46 @@ def attn_sink_bwd(q, k, v, o, dout, lse, sink=None, causal=True, softmax_scale=N
     _check(lib().attn_sink_bwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(sink), _ptr(dq), _ptr(dk),
         _ptr(dv), _ptr(dsink), B, Sq, Sk, Hq, Hkv, D, scale, int(bool(causal)), w1, w2,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), BF16, _stream(dev)))
+    return dq, dk, dv, dsink
+
+
+def attn_sink_bwd_varlen_workspace_bytes(B, total_q, max_seqlen_q, Hq):
+    return lib().attn_sink_bwd_varlen_workspace_bytes(B, total_q, max_seqlen_q, Hq)
+
+
+def attn_sink_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                         max_seqlen_k, sink=None, causal=True, softmax_scale=None, window=None,
+                         dq=None, dk=None, dv=None, dsink=None, workspace=None):
+    """(dq, dk, dv, dsink) of sum(dout * O) for attn_sink_fwd_varlen; lse is [Hq, total_q];
+    dsink is None when sink is None."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, name, torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+    total_q, Hq, D = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B+1]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if sink is not None:
+        _need(sink, "sink", torch.float32, dev)
+        if dsink is None:
+            dsink = torch.empty_like(sink)
+    need = lib().attn_sink_bwd_varlen_workspace_bytes(B, total_q, int(max_seqlen_q), Hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    w1, w2 = _window(window)
+    _check(lib().attn_sink_bwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(sink), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsink), B, total_q, total_k,
+        int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, scale, int(bool(causal)), w1, w2,
         _ptr(workspace), workspace.numel() * workspace.element_size(), BF16, _stream(dev)))
     return dq, dk, dv, dsink
 

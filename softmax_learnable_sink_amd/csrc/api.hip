@@ -154,11 +154,46 @@ int attn_sink_fwd_extend_paged(const void* q, const void* k_cache, const void* v
           ATTN_SINK_ERR_INVALID_ARG,
           "block_table, cu_seqlens_q, seqlens_k, sink and lse must be 4-byte aligned");
   if (total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;  // nothing to compute
-  ExtendArgs a{q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, sink, o, lse, B,
-               total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages,
-               softmax_scale, window_first, window_last};
-  return hip_status(launch_extend_paged_bf16(a, static_cast<hipStream_t>(hip_stream)),
+  ExtendArgs a{q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, nullptr, sink, o, lse,
+               B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages_per_seq,
+               softmax_scale, 1, window_first, window_last};
+  return hip_status(launch_extend_bf16(a, static_cast<hipStream_t>(hip_stream)),
                     "attn_sink_fwd_extend_paged launch");
+}
+
+int attn_sink_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, const float* sink, void* o, float* lse,
+                         int B, int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv,
+                         int D, float softmax_scale, int causal, int window_first,
+                         int window_last, int dtype, void* hip_stream) {
+  REQUIRE(dtype == ATTN_SINK_BF16, ATTN_SINK_ERR_UNSUPPORTED,
+          "the variable-length forward supports bf16 only (dtype %d)", dtype);
+  REQUIRE(B >= 1 && total_q >= 0 && total_k >= 0 && max_seqlen_q >= 0,
+          ATTN_SINK_ERR_INVALID_ARG,
+          "need B >= 1, total_q >= 0, total_k >= 0, max_seqlen_q >= 0 (got %d, %d, %d, %d)", B,
+          total_q, total_k, max_seqlen_q);
+  if (int r = check_heads(Hq, Hkv, D)) return r;
+  if (int r = check_scale(softmax_scale)) return r;
+  if (int r = check_window(window_first, window_last)) return r;
+  REQUIRE(causal == 0 || causal == 1, ATTN_SINK_ERR_INVALID_ARG, "causal must be 0 or 1");
+  REQUIRE(window_last < 0 || causal, ATTN_SINK_ERR_UNSUPPORTED,
+          "the first/last window needs causal = 1");
+  REQUIRE(fits_int32((long long)total_q * Hq) && fits_int32((long long)total_k * Hkv),
+          ATTN_SINK_ERR_UNSUPPORTED, "too many rows for 32-bit row indices");
+  REQUIRE(cu_seqlens_q && cu_seqlens_k && (total_q == 0 || (q && o)) &&
+              (total_k == 0 || (k && v)),
+          ATTN_SINK_ERR_INVALID_ARG,
+          "cu_seqlens_q, cu_seqlens_k and the tensors of non-empty sides must not be NULL");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o), ATTN_SINK_ERR_INVALID_ARG,
+          "q, k, v and o must be 16-byte aligned");
+  REQUIRE(aligned4(cu_seqlens_q) && aligned4(cu_seqlens_k) && aligned4(sink) && aligned4(lse),
+          ATTN_SINK_ERR_INVALID_ARG,
+          "cu_seqlens_q, cu_seqlens_k, sink and lse must be 4-byte aligned");
+  if (total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;  // nothing to compute
+  ExtendArgs a{q, k, v, nullptr, cu_seqlens_q, nullptr, cu_seqlens_k, sink, o, lse, B, total_q,
+               max_seqlen_q, Hq, Hkv, D, 1, 0, softmax_scale, causal, window_first, window_last};
+  return hip_status(launch_extend_bf16(a, static_cast<hipStream_t>(hip_stream)),
+                    "attn_sink_fwd_varlen launch");
 }
 
 static int check_decode_common(int B, int Hq, int Hkv, int D, int page_size, int max_pages,
@@ -225,7 +260,12 @@ int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v
 
 size_t attn_sink_bwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D) {
   if (B < 1 || Sq < 1 || Sk < 0 || check_heads(Hq, Hkv, D) != ATTN_SINK_OK) return 0;
-  return backward_workspace_bytes(B, Sq, Sk, Hq, Hkv, D);
+  return backward_workspace_bytes(B, Sq, Hq, (size_t)B * Sq);
+}
+
+size_t attn_sink_bwd_varlen_workspace_bytes(int B, int total_q, int max_seqlen_q, int Hq) {
+  if (B < 1 || total_q < 0 || max_seqlen_q < 0 || Hq < 1) return 0;
+  return backward_workspace_bytes(B, max_seqlen_q, Hq, (size_t)total_q);
 }
 
 int attn_sink_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -257,15 +297,65 @@ int attn_sink_bwd(const void* q, const void* k, const void* v, const void* o, co
           "B (%d) and ceil(Sk / 128) (%d) must each be <= %lld", B, (Sk + 127) / 128, kMaxGridYZ);
   REQUIRE((long long)Sk * Hkv * D * 2 <= kMaxSlice && (long long)Sq * Hq * D * 2 <= kMaxSlice,
           ATTN_SINK_ERR_UNSUPPORTED, "one batch's K/V or Q/dO slice exceeds 4 GiB");
-  const size_t need = backward_workspace_bytes(B, Sq, Sk, Hq, Hkv, D);
+  const size_t need = backward_workspace_bytes(B, Sq, Hq, (size_t)B * Sq);
   REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
           "a 16-byte aligned workspace of %zu bytes is required", need);
   REQUIRE(workspace_bytes >= need, ATTN_SINK_ERR_WORKSPACE,
           "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
-  BackwardArgs a{q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, B, Sq, Sk, Hq, Hkv, D,
-                 softmax_scale, causal, window_first, window_last, workspace};
+  BackwardArgs a{q,  k,  v,      o,  dout, lse, sink, dq, dk, dv, dsink, nullptr, nullptr, B,
+                 Sq, Sk, B * Sq, Hq, Hkv,  D,   softmax_scale, causal, window_first,
+                 window_last, workspace};
   return hip_status(launch_backward_bf16(a, static_cast<hipStream_t>(hip_stream)),
                     "attn_sink_bwd launch");
+}
+
+int attn_sink_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, const float* sink,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* dq,
+                         void* dk, void* dv, float* dsink, int B, int total_q, int total_k,
+                         int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int D,
+                         float softmax_scale, int causal, int window_first, int window_last,
+                         void* workspace, size_t workspace_bytes, int dtype, void* hip_stream) {
+  REQUIRE(dtype == ATTN_SINK_BF16, ATTN_SINK_ERR_UNSUPPORTED,
+          "the backward supports bf16 only (dtype %d)", dtype);
+  REQUIRE(B >= 1 && total_q >= 0 && total_k >= 0 && max_seqlen_q >= 0 && max_seqlen_k >= 0,
+          ATTN_SINK_ERR_INVALID_ARG,
+          "need B >= 1 and total_q, total_k, max_seqlen_q, max_seqlen_k >= 0");
+  if (int r = check_heads(Hq, Hkv, D)) return r;
+  if (int r = check_scale(softmax_scale)) return r;
+  if (int r = check_window(window_first, window_last)) return r;
+  REQUIRE(causal == 0 || causal == 1, ATTN_SINK_ERR_INVALID_ARG, "causal must be 0 or 1");
+  REQUIRE(window_last < 0 || causal, ATTN_SINK_ERR_UNSUPPORTED,
+          "the first/last window needs causal = 1");
+  REQUIRE(cu_seqlens_q && cu_seqlens_k && (total_q == 0 || (q && o && dout && lse && dq)) &&
+              (total_k == 0 || (k && v && dk && dv)),
+          ATTN_SINK_ERR_INVALID_ARG,
+          "cu_seqlens_q, cu_seqlens_k and the tensors of non-empty sides must not be NULL");
+  REQUIRE(!sink || dsink, ATTN_SINK_ERR_INVALID_ARG, "dsink is required when sink is given");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) && aligned16(dout) &&
+              aligned16(dq) && aligned16(dk) && aligned16(dv),
+          ATTN_SINK_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  REQUIRE(aligned4(lse) && aligned4(sink) && aligned4(dsink) && aligned4(cu_seqlens_q) &&
+              aligned4(cu_seqlens_k),
+          ATTN_SINK_ERR_INVALID_ARG, "lse, sink, dsink and cu_seqlens must be 4-byte aligned");
+  REQUIRE(fits_int32((long long)total_q * Hq) && fits_int32((long long)total_k * Hkv),
+          ATTN_SINK_ERR_UNSUPPORTED, "too many rows for 32-bit row indices");
+  REQUIRE(B <= kMaxGridYZ && (max_seqlen_k + 127) / 128 <= kMaxGridYZ, ATTN_SINK_ERR_UNSUPPORTED,
+          "B (%d) and ceil(max_seqlen_k / 128) (%d) must each be <= %lld", B,
+          (max_seqlen_k + 127) / 128, kMaxGridYZ);
+  REQUIRE((long long)max_seqlen_k * Hkv * D * 2 <= kMaxSlice &&
+              (long long)max_seqlen_q * Hq * D * 2 <= kMaxSlice,
+          ATTN_SINK_ERR_UNSUPPORTED, "one sequence's K/V or Q/dO slice exceeds 4 GiB");
+  const size_t need = backward_workspace_bytes(B, max_seqlen_q, Hq, (size_t)total_q);
+  REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
+          "a 16-byte aligned workspace of %zu bytes is required", need);
+  REQUIRE(workspace_bytes >= need, ATTN_SINK_ERR_WORKSPACE,
+          "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  BackwardArgs a{q,  k,  v,  o,  dout, lse, sink, dq, dk, dv, dsink, cu_seqlens_q, cu_seqlens_k,
+                 B,  max_seqlen_q, max_seqlen_k, total_q, Hq, Hkv, D, softmax_scale, causal,
+                 window_first, window_last, workspace};
+  return hip_status(launch_backward_bf16(a, static_cast<hipStream_t>(hip_stream)),
+                    "attn_sink_bwd_varlen launch");
 }
 
 int attn_sink_decode_select_slots(const int32_t* block_table, const int32_t* seqlens_k, int B,

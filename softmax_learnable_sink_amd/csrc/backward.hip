@@ -88,6 +88,22 @@ struct RowTile {
   }
 };
 
+// Rows of sequence b.  A dense batch (cu_q == NULL) has Sq query and Sk key
+// rows per sequence and LSE laid out [B, Hq, Sq]; a packed variable-length
+// batch takes its rows from the cumulative lengths and lays LSE out
+// [Hq, total_q].  Di follows the LSE layout.
+struct SeqRows {
+  int q0, nq;     // first packed query row, query count
+  int k0, nk;     // first packed key row, key count
+  size_t l0, lh;  // LSE / Di index of (head 0, row 0), stride between heads
+};
+__device__ __forceinline__ SeqRows seq_rows(const int32_t* cu_q, const int32_t* cu_k, int b,
+                                            int Sq, int Sk, int Hq, int total_q) {
+  if (!cu_q) return SeqRows{b * Sq, Sq, b * Sk, Sk, (size_t)b * Hq * Sq, (size_t)Sq};
+  const int q0 = cu_q[b], k0 = cu_k[b];
+  return SeqRows{q0, cu_q[b + 1] - q0, k0, cu_k[b + 1] - k0, (size_t)q0, (size_t)total_q};
+}
+
 // ---------------------------------------------------------------------------
 // Di = <dO_i, O_i> and dSink partials.  Grid (ceil(Sq/64), Hq, B); 4 threads
 // per row.
@@ -95,16 +111,17 @@ struct RowTile {
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
     const __bf16* __restrict__ o, const __bf16* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ sink, float* __restrict__ di, float* __restrict__ dsink_part, int Sq,
-    int Hq) {
+    const float* __restrict__ sink, float* __restrict__ di, float* __restrict__ dsink_part,
+    const int32_t* __restrict__ cu_q, int Sq, int Hq, int total_q) {
   constexpr int PER = D / 4;  // elements per thread
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
+  const SeqRows sr = seq_rows(cu_q, cu_q, b, Sq, 0, Hq, total_q);
   const int row = blockIdx.x * 64 + tid / 4;
   const int part = tid % 4;
   float acc = 0.f;
-  if (row < Sq) {
-    const size_t off = (((size_t)b * Sq + row) * Hq + h) * D + part * PER;
+  if (row < sr.nq) {
+    const size_t off = ((size_t)(sr.q0 + row) * Hq + h) * D + part * PER;
 #pragma unroll
     for (int c = 0; c < PER / 8; ++c) {
       const uint4 a = *reinterpret_cast<const uint4*>(o + off + 8 * c);
@@ -117,10 +134,11 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
   acc += __shfl_xor(acc, 1, 64);
   acc += __shfl_xor(acc, 2, 64);
   float contrib = 0.f;
-  if (row < Sq && part == 0) {
-    di[((size_t)b * Hq + h) * Sq + row] = acc;
+  if (row < sr.nq && part == 0) {
+    const size_t x = sr.l0 + h * sr.lh + row;
+    di[x] = acc;
     if (sink) {
-      const float L = lse[((size_t)b * Hq + h) * Sq + row];
+      const float L = lse[x];
       contrib = -exp2_fast((sink[h] - L) * kLog2e) * acc;
     }
   }
@@ -146,7 +164,7 @@ __global__ void bwd_dsink_reduce_kernel(const float* __restrict__ part, float* _
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV.  Grid (Hkv, B, ceil(Sk/128)).  Wave w owns keys k0 + 32w .. +31,
+// dK / dV.  Grid (Hkv, B, ceil(max Sk/128)).  Wave w owns keys k0 + 32w .. +31,
 // held as MFMA B operands (K^T, V^T) in registers.  Per (head, query tile):
 //   S  = Q K^T,  dP = dO V^T        (A = Q, dO from LDS, natural layout)
 //   P = 2^(S*sl2 - LSE*log2e), dS = P (dP - Di)
@@ -165,7 +183,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
-    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Sq, int Sk, int Hq, int Hkv, float scale,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, int Sq, int Sk, int Hq, int Hkv, int total_q, float scale,
     float sl2, int causal, int w1, int w2) {
   __shared__ DkdvLds<D> s;
   constexpr int NS = D + kPad;
@@ -175,17 +194,20 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   // that see the most query rows (the first ones under a causal mask) start first
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int g = Hq / Hkv;
+  const SeqRows sr = seq_rows(cu_q, cu_k, b, Sq, Sk, Hq, total_q);
+  const int nq = sr.nq, nk = sr.nk;
   const int k0 = blockIdx.z * 128;
-  const int k1 = min(Sk, k0 + 128);
+  if (k0 >= nk) return;  // uniform over the workgroup
+  const int k1 = min(nk, k0 + 128);
   const int key = k0 + 32 * wave + l32;
-  const int off = Sk - Sq;
+  const int off = nk - nq;
 
   // K^T / V^T B operands: column key, k = d = 16*ks + 8*hh ..
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    if (key < Sk) {
-      const size_t base = (((size_t)b * Sk + key) * Hkv + kvh) * D + 16 * ks + 8 * hh;
+    if (key < nk) {
+      const size_t base = ((size_t)(sr.k0 + key) * Hkv + kvh) * D + 16 * ks + 8 * hh;
       kf[ks] = *reinterpret_cast<const bf16x8*>(k + base);
       vf[ks] = *reinterpret_cast<const bf16x8*>(v + base);
     } else {
@@ -201,13 +223,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   }
 
   // query rows that can see keys [k0, k1)
-  int i_lo = 0, i_hi = Sq;
+  int i_lo = 0, i_hi = nq;
   if (causal) i_lo = max(0, k0 - off);
-  if (w2 > 0 && k0 >= w1) i_hi = min(Sq, (k1 - 1) + w2 - 1 - off + 1);
+  if (w2 > 0 && k0 >= w1) i_hi = min(nq, (k1 - 1) + w2 - 1 - off + 1);
   const int t_lo = i_lo / kTile;
   const int t_hi = i_hi > i_lo ? (i_hi + kTile - 1) / kTile : t_lo;
-  const int nq = t_hi - t_lo;
-  const int niter = nq * g;
+  const int ntq = t_hi - t_lo;
+  const int niter = ntq * g;
 
   const size_t rs = (size_t)Hq * D;
   RowTile<D> tq, tdo;
@@ -215,14 +237,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   tdo.init(rs, tid);
   float lse_r = 0.f, di_r = 0.f;
   auto load_iter = [&](int it) {
-    const int h = kvh * g + it / nq;
-    const int i0 = (t_lo + it % nq) * kTile;
-    const size_t base = ((size_t)b * Sq * Hq + h) * D;
-    tq.load(q + base, rs, i0, Sq);
-    tdo.load(dout + base, rs, i0, Sq);
-    // per-row LSE and Di of the tile (zero past Sq)
-    const size_t x = ((size_t)b * Hq + h) * Sq + i0;
-    const uint32_t nb = (uint32_t)(Sq - i0) * 4;
+    const int h = kvh * g + it / ntq;
+    const int i0 = (t_lo + it % ntq) * kTile;
+    const size_t base = ((size_t)sr.q0 * Hq + h) * D;
+    tq.load(q + base, rs, i0, nq);
+    tdo.load(dout + base, rs, i0, nq);
+    // per-row LSE and Di of the tile (zero past the last row)
+    const size_t x = sr.l0 + h * sr.lh + i0;
+    const uint32_t nb = (uint32_t)(nq - i0) * 4;
     lse_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                           make_rsrc(lse + x, nb), (tid & 63) * 4, 0, 0));
     di_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -246,10 +268,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 
   for (int it = 0; it < niter; ++it) {
     const int buf = it & 1;
-    const int i0 = (t_lo + it % nq) * kTile;
+    const int i0 = (t_lo + it % ntq) * kTile;
     if (it + 1 < niter) load_iter(it + 1);
     const int p0 = off + i0;
-    const bool need_mask = (i0 + kTile > Sq) || (causal && p0 < k1 - 1) ||
+    const bool need_mask = (i0 + kTile > nq) || (causal && p0 < k1 - 1) ||
                            (w2 > 0 && k1 - 1 >= w1 && p0 + kTile - 1 - w2 >= k0);
 
     // S and dP of both 32-row blocks first (four independent MFMA chains)
@@ -289,7 +311,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             float p = exp2_fast(__builtin_fmaf(sa[qb][i], sl2, -a[e]));
             if constexpr (decltype(masked)::value) {
               const int row = i0 + rbase + i;
-              const bool ok = (row < Sq) & (key < Sk) & key_visible(key, off + row, causal, w1, w2);
+              const bool ok = (row < nq) & (key < nk) & key_visible(key, off + row, causal, w1, w2);
               p = ok ? p : 0.f;
             }
             pv[i] = p;
@@ -329,8 +351,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     __syncthreads();
   }
 
-  if (key < Sk) {
-    const size_t base = (((size_t)b * Sk + key) * Hkv + kvh) * D;
+  if (key < nk) {
+    const size_t base = ((size_t)(sr.k0 + key) * Hkv + kvh) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -389,8 +411,9 @@ template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
-    __bf16* __restrict__ dq, int B, int Sq, int Sk, int Hq, int Hkv, int hpw, float scale,
-    float sl2, int causal, int w1, int w2) {
+    __bf16* __restrict__ dq, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    int B, int Sq, int Sk, int Hq, int Hkv, int total_q, int hpw, float scale, float sl2,
+    int causal, int w1, int w2) {
   __shared__ DqLds<D> s;
   constexpr int NS = D + kPad;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -400,26 +423,29 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(
   const int R = 32 * (4 / hpw);
   const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R);
   const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
+  const SeqRows sr = seq_rows(cu_q, cu_k, b, Sq, Sk, Hq, total_q);
+  const int nq = sr.nq, nk = sr.nk;
+  const int row0 = wi.tile * R;
+  if (row0 >= nq) return;  // uniform over the workgroup
   const int h = kvh * g + wi.grp * hpw + (wave % hpw);
   const int rb = wave / hpw;
-  const int row0 = wi.tile * R;
   const int row = row0 + rb * 32 + l32;
-  const int off = Sk - Sq;
+  const int off = nk - nq;
   const int p = off + row;
   const int p_min = off + row0;
-  const int p_max = off + min(Sq, row0 + R) - 1;
+  const int p_max = off + min(nq, row0 + R) - 1;
 
   bf16x8 qf[D / 16], of[D / 16];
   float lse2 = 0.f, di_r = 0.f;
-  if (row < Sq) {
-    const size_t base = (((size_t)b * Sq + row) * Hq + h) * D + 8 * hh;
+  if (row < nq) {
+    const size_t base = ((size_t)(sr.q0 + row) * Hq + h) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       qf[ks] = *reinterpret_cast<const bf16x8*>(q + base + 16 * ks);
       of[ks] = *reinterpret_cast<const bf16x8*>(dout + base + 16 * ks);
     }
-    lse2 = lse[((size_t)b * Hq + h) * Sq + row] * kLog2e;
-    di_r = di[((size_t)b * Hq + h) * Sq + row];
+    lse2 = lse[sr.l0 + h * sr.lh + row] * kLog2e;
+    di_r = di[sr.l0 + h * sr.lh + row];
   } else {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
@@ -431,18 +457,18 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dqa[db] = f32x16{};
 
-  const QRange tr = kv_tiles(Sk, p_min, p_max, causal, w1, w2);
+  const QRange tr = kv_tiles(nk, p_min, p_max, causal, w1, w2);
   const int ntiles = tr.count();
   const size_t rs = (size_t)Hkv * D;
-  const __bf16* kbase = k + ((size_t)b * Sk * Hkv + kvh) * D;
-  const __bf16* vbase = v + ((size_t)b * Sk * Hkv + kvh) * D;
+  const __bf16* kbase = k + ((size_t)sr.k0 * Hkv + kvh) * D;
+  const __bf16* vbase = v + ((size_t)sr.k0 * Hkv + kvh) * D;
   RowTile<D> tk, tv;
   tk.init(rs, tid);
   tv.init(rs, tid);
   __builtin_amdgcn_s_waitcnt(0);
   if (ntiles > 0) {
-    tk.load(kbase, rs, tr.tile(0) * kTile, Sk);
-    tv.load(vbase, rs, tr.tile(0) * kTile, Sk);
+    tk.load(kbase, rs, tr.tile(0) * kTile, nk);
+    tv.load(vbase, rs, tr.tile(0) * kTile, nk);
     tk.store(s.k[0], tid);
     tv.store(s.v[0], tid);
   }
@@ -452,8 +478,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(
     const int buf = it & 1;
     const int key0 = tr.tile(it) * kTile;
     if (it + 1 < ntiles) {
-      tk.load(kbase, rs, tr.tile(it + 1) * kTile, Sk);
-      tv.load(vbase, rs, tr.tile(it + 1) * kTile, Sk);
+      tk.load(kbase, rs, tr.tile(it + 1) * kTile, nk);
+      tv.load(vbase, rs, tr.tile(it + 1) * kTile, nk);
     }
     f32x16 st[2], dp[2];
 #pragma unroll
@@ -471,9 +497,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(
         st[kb] = mfma32(ka, qf[ks], st[kb]);
         dp[kb] = mfma32(va, of[ks], dp[kb]);
       }
-    const bool need_mask = (key0 + kTile > Sk) || (causal && key0 + kTile - 1 > p_min) ||
+    const bool need_mask = (key0 + kTile > nk) || (causal && key0 + kTile - 1 > p_min) ||
                            (w2 > 0 && key0 + kTile - 1 >= w1 && key0 <= p_max - w2) ||
-                           (row0 + R > Sq);
+                           (row0 + R > nq);
     // dS^T = P^T (dP^T - Di); the mask is applied on one of two straight-line
     // paths chosen once per tile
     bf16x8 sb[2][2];
@@ -486,7 +512,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(
           float pr = exp2_fast(__builtin_fmaf(st[kb][i], sl2, -lse2));
           if constexpr (decltype(masked)::value) {
             const int j = key0 + 32 * kb + 16 * hh + i;
-            const bool ok = (row < Sq) & (j < Sk) & key_visible(j, p, causal, w1, w2);
+            const bool ok = (row < nq) & (j < nk) & key_visible(j, p, causal, w1, w2);
             pr = ok ? pr : 0.f;
           }
           dsv[i] = pr * (dp[kb][i] - di_r);
@@ -517,8 +543,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(
     __syncthreads();
   }
 
-  if (row < Sq) {
-    __bf16* dst = dq + (((size_t)b * Sq + row) * Hq + h) * D;
+  if (row < nq) {
+    __bf16* dst = dq + ((size_t)(sr.q0 + row) * Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -531,23 +557,24 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(
 
 }  // namespace
 
-size_t backward_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D) {
-  (void)Sk;
-  (void)Hkv;
-  (void)D;
-  const size_t nblk = (size_t)(Sq + 63) / 64;
-  const size_t di = (size_t)B * Hq * Sq;
+size_t backward_workspace_bytes(int B, int max_sq, int Hq, size_t rows) {
+  const size_t nblk = (size_t)(max_sq + 63) / 64;
+  const size_t di = (size_t)Hq * rows;
   const size_t part = (size_t)B * Hq * nblk;
   return (di + part) * sizeof(float);
 }
 
+// Dense batches: Sq, Sk are every sequence's lengths and cu arrays are NULL.
+// Packed batches: Sq, Sk are upper bounds of the lengths (they size the grids)
+// and rows come from the cu arrays.  Grids that would be empty are skipped.
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
   const int g = a.Hq / a.Hkv;
   const int hpw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
   const float sl2 = a.scale * kLog2e;
   const int nblk = (a.Sq + 63) / 64;
+  const size_t rows = a.cu_seqlens_q ? (size_t)a.total_q : (size_t)a.B * a.Sq;
   float* di = static_cast<float*>(a.workspace);
-  float* part = di + (size_t)a.B * a.Hq * a.Sq;
+  float* part = di + (size_t)a.Hq * rows;
   const auto* q = static_cast<const __bf16*>(a.q);
   const auto* k = static_cast<const __bf16*>(a.k);
   const auto* v = static_cast<const __bf16*>(a.v);
@@ -556,28 +583,38 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
   auto* dq = static_cast<__bf16*>(a.dq);
   auto* dk = static_cast<__bf16*>(a.dk);
   auto* dv = static_cast<__bf16*>(a.dv);
+  const int32_t* cq = a.cu_seqlens_q;
+  const int32_t* ck = a.cu_seqlens_k;
+  const int tq = a.total_q;
   const dim3 pgrid(nblk, a.Hq, a.B);
   const dim3 kgrid(a.Hkv, a.B, (a.Sk + 127) / 128);
   const int R = 32 * (4 / hpw);
   const dim3 qgrid(a.B * a.Hkv * (g / hpw) * ((a.Sq + R - 1) / R));
+  const bool rows_q = a.Sq > 0, rows_k = a.Sk > 0;
   if (a.D == 64) {
-    bwd_preprocess_kernel<64><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di, part,
-                                                              a.Sq, a.Hq);
-    bwd_dkdv_kernel<64><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dk, dv, a.Sq,
-                                                        a.Sk, a.Hq, a.Hkv, a.scale, sl2, a.causal,
-                                                        a.w1, a.w2);
-    bwd_dq_kernel<64><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, a.B, a.Sq,
-                                                      a.Sk, a.Hq, a.Hkv, hpw, a.scale, sl2,
-                                                      a.causal, a.w1, a.w2);
+    if (rows_q)
+      bwd_preprocess_kernel<64><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di, part,
+                                                                cq, a.Sq, a.Hq, tq);
+    if (rows_k)
+      bwd_dkdv_kernel<64><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dk, dv, cq, ck,
+                                                          a.Sq, a.Sk, a.Hq, a.Hkv, tq, a.scale,
+                                                          sl2, a.causal, a.w1, a.w2);
+    if (rows_q)
+      bwd_dq_kernel<64><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, cq, ck, a.B,
+                                                        a.Sq, a.Sk, a.Hq, a.Hkv, tq, hpw, a.scale,
+                                                        sl2, a.causal, a.w1, a.w2);
   } else {
-    bwd_preprocess_kernel<128><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di, part,
-                                                               a.Sq, a.Hq);
-    bwd_dkdv_kernel<128><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dk, dv, a.Sq,
-                                                         a.Sk, a.Hq, a.Hkv, a.scale, sl2,
-                                                         a.causal, a.w1, a.w2);
-    bwd_dq_kernel<128><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, a.B, a.Sq,
-                                                       a.Sk, a.Hq, a.Hkv, hpw, a.scale, sl2,
-                                                       a.causal, a.w1, a.w2);
+    if (rows_q)
+      bwd_preprocess_kernel<128><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di,
+                                                                 part, cq, a.Sq, a.Hq, tq);
+    if (rows_k)
+      bwd_dkdv_kernel<128><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dk, dv, cq,
+                                                           ck, a.Sq, a.Sk, a.Hq, a.Hkv, tq,
+                                                           a.scale, sl2, a.causal, a.w1, a.w2);
+    if (rows_q)
+      bwd_dq_kernel<128><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, cq, ck,
+                                                         a.B, a.Sq, a.Sk, a.Hq, a.Hkv, tq, hpw,
+                                                         a.scale, sl2, a.causal, a.w1, a.w2);
   }
   if (a.sink && a.dsink)
     bwd_dsink_reduce_kernel<<<(a.Hq + 63) / 64, 64, 0, stream>>>(part, a.dsink, a.B, a.Hq, nblk);

@@ -24,22 +24,26 @@ struct PrefillArgs {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
+// Packed variable-length queries against K/V that are either a paged cache
+// (block_table != NULL; sequence lengths in seqlens_k) or packed
+// variable-length tensors (block_table == NULL; rows cu_seqlens_k[b] ..).
 struct ExtendArgs {
   const void* q;  // packed [total_q, Hq, D]
-  const void* k_cache;
-  const void* v_cache;
+  const void* k;  // [num_pages, page_size, Hkv, D] or [total_k, Hkv, D]
+  const void* v;
   const int32_t* block_table;
   const int32_t* cu_seqlens_q;
   const int32_t* seqlens_k;
+  const int32_t* cu_seqlens_k;
   const float* sink;
   void* o;
   float* lse;  // [Hq, total_q] or NULL
-  int B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages, num_pages;
+  int B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages;
   float scale;
-  int w1, w2;
+  int causal, w1, w2;
 };
 
-hipError_t launch_extend_paged_bf16(const ExtendArgs& a, hipStream_t stream);
+hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
   const void* q;
@@ -89,12 +93,19 @@ struct BackwardArgs {
   void* dk;
   void* dv;
   float* dsink;
-  int B, Sq, Sk, Hq, Hkv, D;
+  // Dense: cu arrays NULL, Sq / Sk the lengths, LSE [B, Hq, Sq].  Packed
+  // variable-length: cu arrays [B+1], Sq / Sk upper bounds of the lengths,
+  // total_q packed query rows, LSE [Hq, total_q].
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int B, Sq, Sk, total_q, Hq, Hkv, D;
   float scale;
   int causal, w1, w2;
   void* workspace;
 };
-size_t backward_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D);
+// Di for `rows` query rows per head plus dSink partials of B sequences of at
+// most max_sq rows.
+size_t backward_workspace_bytes(int B, int max_sq, int Hq, size_t rows);
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream);
 
 }  // namespace attn_sink

@@ -392,10 +392,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 // on K/V tiles gathered from the cache through the block table.
 // ---------------------------------------------------------------------------
 
-// One 64-key tile of K and V gathered from the paged cache.  Each thread owns
-// KN (row, 16-byte chunk) items; their slots come from block-table entries
-// fetched two tiles ahead.  Keys at or past L read slot 0 and are written to
-// LDS as zero V rows (their scores are masked anyway).
+// One 64-key tile of K and V gathered row by row.  Each thread owns KN (row,
+// 16-byte chunk) items.  With a block table the rows are cache slots, from
+// block-table entries fetched two tiles ahead; without one (packed
+// variable-length K/V) key j of the sequence is row kbase + j.  Keys at or
+// past L read row 0 and are written to LDS as zero V rows (their scores are
+// masked anyway).
 template <int D>
 struct PagedTile {
   static constexpr int CH = D / 8;
@@ -409,14 +411,21 @@ struct PagedTile {
 
   __device__ __forceinline__ void fetch_pages(const int32_t* bt_row, int key0, int L, int shift,
                                               int tid) {
+    if (!bt_row) {
+#pragma unroll
+      for (int i = 0; i < KN; ++i) page[i] = 0;
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < KN; ++i) page[i] = bt_row[min(key0 + row_of(tid, i), L - 1) >> shift];
   }
-  __device__ __forceinline__ void pages_to_slots(int key0, int L, int shift, int tid) {
+  __device__ __forceinline__ void pages_to_slots(const int32_t* bt_row, int kbase, int key0, int L,
+                                                 int shift, int tid) {
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
       const int key = key0 + row_of(tid, i);
-      slot[i] = key < L ? (page[i] << shift) | (key & ((1 << shift) - 1)) : -1;
+      const int row = bt_row ? (page[i] << shift) | (key & ((1 << shift) - 1)) : kbase + key;
+      slot[i] = key < L ? row : -1;
     }
   }
   __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, size_t rs,
@@ -441,13 +450,18 @@ struct PagedTile {
   }
 };
 
+// Packed variable-length queries against either a paged cache (bt != NULL:
+// K/V rows are cache slots, L = seqlens[b]) or packed variable-length K/V
+// (bt == NULL: sequence b's keys are rows cu_k[b] .. cu_k[b+1]-1, L = their
+// count).  Row i of sequence b sits at position L - nq + i.
 template <int D, int QB>
-__global__ __launch_bounds__(kThreads, 2) void extend_paged_kernel(
+__global__ __launch_bounds__(kThreads, 2) void extend_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ seqlens, const float* __restrict__ sink, __bf16* __restrict__ o,
-    float* __restrict__ lse, int B, int total_q, int max_sq, int Hq, int Hkv, int hpw,
-    int page_shift, int max_pages, float sl2, int w1, int w2) {
+    const int32_t* __restrict__ seqlens, const int32_t* __restrict__ cu_k,
+    const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int B,
+    int total_q, int max_sq, int Hq, int Hkv, int hpw, int page_shift, int max_pages, float sl2,
+    int causal, int w1, int w2) {
   __shared__ Lds<D> s;
   constexpr int RW = 32 * QB;
   const int tid = threadIdx.x;
@@ -467,35 +481,37 @@ __global__ __launch_bounds__(kThreads, 2) void extend_paged_kernel(
   const int h = kvh * g + wi.grp * hpw + (wave % hpw);
   const int rb = wave / hpw;
   const int wrow0 = row0 + rb * RW;
-  const int L = seqlens[b];
+  const int kbase = bt ? 0 : cu_k[b];
+  const int L = bt ? seqlens[b] : cu_k[b + 1] - kbase;
   const int off = L - nq;
-  const RowGeom geom{L, 1, w1, w2, off + row0, off + min(nq, row0 + R) - 1, off + wrow0 + l32};
+  const RowGeom geom{L, causal, w1, w2, off + row0, off + min(nq, row0 + R) - 1,
+                     off + wrow0 + l32};
 
   WaveRows<D, QB> wr;
   wr.init(q + (size_t)qbase * Hq * D, sink, nq, Hq, h, wrow0, hh, l32);
 
   const size_t rs = (size_t)Hkv * D;
-  const __bf16* kbase = kc + (size_t)kvh * D;
-  const __bf16* vbase = vc + (size_t)kvh * D;
-  const int32_t* bt_row = bt + (size_t)b * max_pages;
-  const TileRange tr = tile_range(L, geom.p_min, geom.p_max, 1, w1, w2);
+  const __bf16* kb_ = kc + (size_t)kvh * D;
+  const __bf16* vb_ = vc + (size_t)kvh * D;
+  const int32_t* bt_row = bt ? bt + (size_t)b * max_pages : nullptr;
+  const TileRange tr = tile_range(L, geom.p_min, geom.p_max, causal, w1, w2);
   const int nt = tr.count();
 
   __builtin_amdgcn_s_waitcnt(0);
   if (nt > 0) {
     PagedTile<D> pt;
     pt.fetch_pages(bt_row, tr.tile(0) * kBN, L, page_shift, tid);
-    pt.pages_to_slots(tr.tile(0) * kBN, L, page_shift, tid);
-    pt.load(kbase, vbase, rs, tid);
+    pt.pages_to_slots(bt_row, kbase, tr.tile(0) * kBN, L, page_shift, tid);
+    pt.load(kb_, vb_, rs, tid);
     pt.store(s, 0, tid);
     if (nt > 1) {
       pt.fetch_pages(bt_row, tr.tile(1) * kBN, L, page_shift, tid);
-      pt.pages_to_slots(tr.tile(1) * kBN, L, page_shift, tid);
+      pt.pages_to_slots(bt_row, kbase, tr.tile(1) * kBN, L, page_shift, tid);
     }
     __syncthreads();
     for (int it = 0; it < nt; ++it) {
       const int buf = it & 1;
-      if (it + 1 < nt) pt.load(kbase, vbase, rs, tid);
+      if (it + 1 < nt) pt.load(kb_, vb_, rs, tid);
       if (it + 2 < nt) pt.fetch_pages(bt_row, tr.tile(it + 2) * kBN, L, page_shift, tid);
       f32x16 st[2][QB];
       bf16x8 pf[2][QB][2];
@@ -503,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 2) void extend_paged_kernel(
       wr.softmax(st, pf, tr.tile(it) * kBN, geom, sl2, hh);
       wr.pv(s.v[buf], pf, lane);
       if (it + 1 < nt) pt.store(s, buf ^ 1, tid);
-      if (it + 2 < nt) pt.pages_to_slots(tr.tile(it + 2) * kBN, L, page_shift, tid);
+      if (it + 2 < nt) pt.pages_to_slots(bt_row, kbase, tr.tile(it + 2) * kBN, L, page_shift, tid);
       __syncthreads();
     }
   }
@@ -606,29 +622,31 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_extend_paged_bf16(const ExtendArgs& a, hipStream_t stream) {
+hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream) {
   const int g = a.Hq / a.Hkv;
   const int hpw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
   const float sl2 = a.scale * kLog2e;
   int shift = 0;
   while ((1 << shift) < a.page_size) ++shift;
   const auto* q = static_cast<const __bf16*>(a.q);
-  const auto* kc = static_cast<const __bf16*>(a.k_cache);
-  const auto* vc = static_cast<const __bf16*>(a.v_cache);
+  const auto* kc = static_cast<const __bf16*>(a.k);
+  const auto* vc = static_cast<const __bf16*>(a.v);
   auto* o = static_cast<__bf16*>(a.o);
   const int cols = a.B * a.Hkv * (g / hpw);
   if (a.D == 64) {
     const int R = 64 * (4 / hpw);
     const dim3 grid(cols * ((a.max_seqlen_q + R - 1) / R));
-    extend_paged_kernel<64, 2><<<grid, kThreads, 0, stream>>>(
-        q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.sink, o, a.lse, a.B, a.total_q,
-        a.max_seqlen_q, a.Hq, a.Hkv, hpw, shift, a.max_pages, sl2, a.w1, a.w2);
+    extend_kernel<64, 2><<<grid, kThreads, 0, stream>>>(
+        q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.cu_seqlens_k, a.sink, o, a.lse,
+        a.B, a.total_q, a.max_seqlen_q, a.Hq, a.Hkv, hpw, shift, a.max_pages, sl2, a.causal, a.w1,
+        a.w2);
   } else {
     const int R = 32 * (4 / hpw);
     const dim3 grid(cols * ((a.max_seqlen_q + R - 1) / R));
-    extend_paged_kernel<128, 1><<<grid, kThreads, 0, stream>>>(
-        q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.sink, o, a.lse, a.B, a.total_q,
-        a.max_seqlen_q, a.Hq, a.Hkv, hpw, shift, a.max_pages, sl2, a.w1, a.w2);
+    extend_kernel<128, 1><<<grid, kThreads, 0, stream>>>(
+        q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.cu_seqlens_k, a.sink, o, a.lse,
+        a.B, a.total_q, a.max_seqlen_q, a.Hq, a.Hkv, hpw, shift, a.max_pages, sl2, a.causal, a.w1,
+        a.w2);
   }
   return hipGetLastError();
 }

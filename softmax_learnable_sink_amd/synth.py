@@ -11,6 +11,7 @@ their exact float values.  fp32 tensors are returned as ``float32``.
 Draw order (fixed, so a seed names one input set):
   prefill:  q, k, v, [dout], sink
   decode:   q, sink, context lengths, page permutation, k pool, v pool
+  varlen:   q, k, v, [dout], sink (packed; lengths from rng((seed, 3000)))
 Each N(0,1) tensor is drawn in blocks of 2^22 elements; block i of the n-th
 tensor of a case comes from numpy.random.default_rng((seed, n, i)), so large
 pools can be drawn by several threads with a result that does not depend on
@@ -94,6 +95,55 @@ def prefill_case(B, Sq, Sk, Hq, Hkv, D, dtype=BF16, seed=0, sink=True, dout=Fals
     if dout:
         case["dout"] = dr.normal((B, Sq, Hq, D), dtype)
     case["sink"] = dr.sink(Hq) if sink else None
+    return case
+
+
+def packed_lengths(total, lo, hi, seed=0):
+    """Sequence lengths ~ U[lo, hi] drawn until they add up to `total` tokens;
+    the last one is cut to fit (so it may be shorter than lo)."""
+    rng = np.random.default_rng((int(seed), 3001))
+    out, left = [], int(total)
+    while left > 0:
+        n = min(int(rng.integers(lo, hi, endpoint=True)), left)
+        out.append(n)
+        left -= n
+    return np.asarray(out, dtype=np.int32)
+
+
+def varlen_case(B, Hq, Hkv, D, q_lo=1, q_hi=1, k_lo=None, k_hi=None, dtype=BF16, seed=0,
+                sink=True, dout=False, q_lens=None, k_lens=None):
+    """Packed variable-length inputs: q [total_q,Hq,D], k/v [total_k,Hkv,D], optional
+    dO [total_q,Hq,D], sink [Hq], cu_seqlens_q / cu_seqlens_k [B+1] int32.
+
+    Sequence b has nq_b ~ U[q_lo, q_hi] queries (or `q_lens`) and nk_b keys:
+    `k_lens` if given, else nk_b = nq_b when k_lo is None (self-attention),
+    else U[k_lo, k_hi].
+    """
+    rng = np.random.default_rng((int(seed), 3000))
+    if q_lens is None:
+        q_lens = rng.integers(q_lo, q_hi, size=B, endpoint=True)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    if k_lens is None:
+        k_lens = q_lens if k_lo is None else rng.integers(k_lo, k_hi, size=B, endpoint=True)
+    k_lens = np.asarray(k_lens, dtype=np.int32)
+    assert len(q_lens) == B and len(k_lens) == B
+    cu_q = np.zeros(B + 1, dtype=np.int32)
+    cu_q[1:] = np.cumsum(q_lens)
+    cu_k = np.zeros(B + 1, dtype=np.int32)
+    cu_k[1:] = np.cumsum(k_lens)
+    dr = _Draws(seed)
+    case = {
+        "dtype": dtype,
+        "q": dr.normal((int(cu_q[-1]), Hq, D), dtype),
+        "k": dr.normal((int(cu_k[-1]), Hkv, D), dtype),
+        "v": dr.normal((int(cu_k[-1]), Hkv, D), dtype),
+    }
+    if dout:
+        case["dout"] = dr.normal((int(cu_q[-1]), Hq, D), dtype)
+    case["sink"] = dr.sink(Hq) if sink else None
+    case.update({"cu_seqlens_q": cu_q, "cu_seqlens_k": cu_k, "q_lens": q_lens, "k_lens": k_lens,
+                 "max_seqlen_q": int(q_lens.max()) if B else 0,
+                 "max_seqlen_k": int(k_lens.max()) if B else 0})
     return case
 
 

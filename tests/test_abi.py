@@ -34,7 +34,8 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("attn_sink_fwd_prefill", "attn_sink_fwd_decode_paged", "attn_sink_bwd",
-              "attn_sink_fwd_extend_paged",
+              "attn_sink_fwd_extend_paged", "attn_sink_fwd_varlen", "attn_sink_bwd_varlen",
+              "attn_sink_bwd_varlen_workspace_bytes",
               "attn_sink_decode_workspace_bytes", "attn_sink_bwd_workspace_bytes",
               "attn_sink_decode_select_slots", "attn_sink_gather_kv", "attn_sink_last_error",
               "attn_sink_abi_version"):
@@ -193,6 +194,74 @@ def test_bwd_workspace_query(lib):
     n = binding.attn_sink_bwd_workspace_bytes(B, S, S, Hq, 8, 64)
     assert n == 4 * (B * Hq * S + B * Hq * (S // 64))
     assert binding.attn_sink_bwd_workspace_bytes(B, S, S, Hq, 7, 64) == 0
+
+
+def _fwd_varlen(lib, **kw):
+    a = dict(B=2, tq=10, tk=12, mq=6, Hq=8, Hkv=2, D=64, scale=0.125, causal=1, w1=-1, w2=-1,
+             dtype=binding.BF16, q=P, k=P, cq=P, ck=P)
+    a.update(kw)
+    return lib.attn_sink_fwd_varlen(a["q"], a["k"], a["k"], a["cq"], a["ck"], None, P, None,
+                                    a["B"], a["tq"], a["tk"], a["mq"], a["Hq"], a["Hkv"], a["D"],
+                                    a["scale"], a["causal"], a["w1"], a["w2"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dtype=binding.F32), binding.ERR_UNSUPPORTED, "bf16"),
+    (dict(B=0), binding.ERR_INVALID_ARG, "B >= 1"),
+    (dict(tk=-1), binding.ERR_INVALID_ARG, "total_k >= 0"),
+    (dict(D=96), binding.ERR_UNSUPPORTED, "64 or 128"),
+    (dict(Hq=9), binding.ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(ck=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(k=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(q=P_ODD), binding.ERR_INVALID_ARG, "aligned"),
+    (dict(causal=2), binding.ERR_INVALID_ARG, "causal"),
+    (dict(w1=1, w2=4, causal=0), binding.ERR_UNSUPPORTED, "causal"),
+    (dict(tq=1 << 28, Hq=16, Hkv=2), binding.ERR_UNSUPPORTED, "32-bit"),
+])
+def test_fwd_varlen_rejects(lib, kw, status, msg):
+    assert _fwd_varlen(lib, **kw) == status
+    assert msg in binding.last_error()
+
+
+def test_fwd_varlen_with_no_rows_is_a_no_op(lib):
+    assert _fwd_varlen(lib, tq=0, mq=0) == binding.OK
+    # no key at all: k and v may be NULL
+    assert _fwd_varlen(lib, tq=0, mq=0, tk=0, k=None) == binding.OK
+
+
+def _bwd_varlen(lib, **kw):
+    a = dict(sink=None, dsink=None, B=2, tq=10, tk=12, mq=6, mk=8, Hq=4, Hkv=2, D=64, scale=0.125,
+             causal=1, w1=-1, w2=-1, ws=P, wsb=1 << 20, dtype=binding.BF16, lse=P, dq=P, cq=P)
+    a.update(kw)
+    return lib.attn_sink_bwd_varlen(P, P, P, P, P, a["lse"], a["sink"], a["cq"], P, a["dq"], P, P,
+                                    a["dsink"], a["B"], a["tq"], a["tk"], a["mq"], a["mk"],
+                                    a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["w1"],
+                                    a["w2"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(sink=P), binding.ERR_INVALID_ARG, "dsink"),
+    (dict(lse=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(cq=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(dtype=binding.F32), binding.ERR_UNSUPPORTED, "bf16"),
+    (dict(wsb=4), binding.ERR_WORKSPACE, "too small"),
+    (dict(ws=None), binding.ERR_WORKSPACE, "workspace"),
+    (dict(mk=-1), binding.ERR_INVALID_ARG, ">= 0"),
+    (dict(D=256), binding.ERR_UNSUPPORTED, "64 or 128"),
+    (dict(w1=2, w2=3, causal=0), binding.ERR_UNSUPPORTED, "causal"),
+    (dict(B=70000, wsb=1 << 40), binding.ERR_UNSUPPORTED, "must each be <="),
+    (dict(mq=1 << 22, Hq=8, Hkv=8, D=128, wsb=1 << 40), binding.ERR_UNSUPPORTED, "4 GiB"),
+])
+def test_bwd_varlen_rejects(lib, kw, status, msg):
+    assert _bwd_varlen(lib, **kw) == status
+    assert msg in binding.last_error()
+
+
+def test_bwd_varlen_workspace_query(lib):
+    B, tq, mq, Hq = 3, 5000, 4096, 16
+    n = binding.attn_sink_bwd_varlen_workspace_bytes(B, tq, mq, Hq)
+    assert n == 4 * (Hq * tq + B * Hq * (mq // 64))
+    assert binding.attn_sink_bwd_varlen_workspace_bytes(0, tq, mq, Hq) == 0
 
 
 def test_select_and_gather_reject(lib):
