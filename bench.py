@@ -8,6 +8,8 @@ One step runs every entry point once over its synthetic workload:
   extend    chunked prefill: B2 x 4096 new tokens on 4096..12288 cached ones, 64/8 heads,
             D64, page 16, sink (packed queries against the paged cache)
   train     B2, S8192, 64/8 heads, D64, causal: forward + backward with dSink
+  varlen    packed training: 16384 tokens in sequences of U[512, 4096] tokens (the last
+            one cut to fit), 64/8 heads, D64, causal: forward + backward with dSink
 Each entry point is bracketed by HIP events on the stream it is launched on;
 `value` is the prefill throughput in TFLOP/s of algorithmic work (4*D flops per
 visible (query, key) pair), `decode_gbps` the paged decode's algorithmic HBM
@@ -31,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill attention TFLOP/s + paged-decode HBM GB/s (% of MI355X roofline)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-PARTS = ("prefill", "decode", "window32", "window1", "extend", "train")
+PARTS = ("prefill", "decode", "window32", "window1", "extend", "train", "varlen")
 
 
 def causal_pairs(B, Hq, Sq, Sk):
@@ -61,7 +63,7 @@ TRAFFIC_KERNELS = {  # key in hbm_traffic.json -> (kernel-name substring, source
     "decode_partial_kernel": ("decode_partial_kernelILi64", "decode"),
     "decode_combine_kernel": ("decode_combine_kernelILi64", "decode"),
     "decode_partial_kernel_d128": ("decode_partial_kernelILi128", "decode"),
-    "extend_paged_kernel": ("extend_paged_kernelILi64ELi2", "prefill"),
+    "extend_kernel": ("extend_kernelILi64ELi2", "prefill"),
 }
 
 
@@ -114,7 +116,8 @@ def load_traffic():
         return {}
     taken = data.get("source_hash", {})
     return {key: b for key, b in data.get("bytes_per_launch", {}).items()
-            if taken.get(TRAFFIC_KERNELS[key][1]) == kernel_source_hash(TRAFFIC_KERNELS[key][1])}
+            if key in TRAFFIC_KERNELS
+            and taken.get(TRAFFIC_KERNELS[key][1]) == kernel_source_hash(TRAFFIC_KERNELS[key][1])}
 
 
 class Workloads:
@@ -217,6 +220,31 @@ class Workloads:
                                       bwd_flops=10 * D * pairs, pairs=pairs,
                                       shape=f"B{B} S{S} H{Hq}/{Hkv} D{D} causal bf16 fwd+bwd")
             self.tr = t
+        if "varlen" in parts:
+            Hq, Hkv, D = 64, 8, 64
+            lens = synth.packed_lengths(16384, 512, 4096, seed=0)
+            B = len(lens)
+            c = synth.varlen_case(B, Hq, Hkv, D, seed=0, dout=True, q_lens=lens)
+            t = dict(q=dt(c["q"]), k=dt(c["k"]), v=dt(c["v"]), do=dt(c["dout"]),
+                     sink=torch.from_numpy(c["sink"]).to(dev), cq=i32(c["cu_seqlens_q"]),
+                     ck=i32(c["cu_seqlens_k"]), mq=c["max_seqlen_q"], mk=c["max_seqlen_k"])
+            tq = t["q"].shape[0]
+            t["o"] = torch.empty_like(t["q"])
+            t["lse"] = torch.empty((Hq, tq), dtype=torch.float32, device=dev)
+            t["dq"] = torch.empty_like(t["q"])
+            t["dk"] = torch.empty_like(t["k"])
+            t["dv"] = torch.empty_like(t["v"])
+            t["dsink"] = torch.empty_like(t["sink"])
+            from softmax_learnable_sink_amd import binding
+            t["ws"] = torch.empty(binding.attn_sink_bwd_varlen_workspace_bytes(B, tq, t["mq"], Hq),
+                                  dtype=torch.uint8, device=dev)
+            L = lens.astype(np.int64)
+            pairs = int(Hq * (L * (L + 1) // 2).sum())
+            self.info["varlen"] = dict(flops=14 * D * pairs, fwd_flops=4 * D * pairs,
+                                       bwd_flops=10 * D * pairs, pairs=pairs,
+                                       shape=f"packed {tq} tokens in {B} sequences "
+                                             f"(U[512,4096]) H{Hq}/{Hkv} D{D} causal bf16 fwd+bwd")
+            self.vl = t
 
     def run(self, name):
         from softmax_learnable_sink_amd import binding
@@ -242,6 +270,14 @@ class Workloads:
             binding.attn_sink_bwd(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], t["sink"],
                                   causal=True, softmax_scale=0.125, dq=t["dq"], dk=t["dk"],
                                   dv=t["dv"], dsink=t["dsink"], workspace=t["ws"])
+        elif name == "varlen":
+            t = self.vl
+            binding.attn_sink_fwd_varlen(t["q"], t["k"], t["v"], t["cq"], t["ck"], t["mq"], t["sink"],
+                                         causal=True, softmax_scale=0.125, out=t["o"], lse=t["lse"])
+            binding.attn_sink_bwd_varlen(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], t["cq"],
+                                         t["ck"], t["mq"], t["mk"], t["sink"], causal=True,
+                                         softmax_scale=0.125, dq=t["dq"], dk=t["dk"], dv=t["dv"],
+                                         dsink=t["dsink"], workspace=t["ws"])
 
 
 def cpu_baseline(wl, budget_s=12.0):
@@ -360,7 +396,7 @@ def main():
             gbps = info["bytes"] / (ms[p] * 1e-3) / 1e9
             rec.update(gbps=round(gbps, 2), hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
                        algorithmic_bytes=info["bytes"])
-        if p in ("prefill", "extend", "train"):
+        if p in ("prefill", "extend", "train", "varlen"):
             tf = info["flops"] / (ms[p] * 1e-3) / 1e12
             rec.update(tflops=round(tf, 2), mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4),
                        algorithmic_flops=info["flops"])

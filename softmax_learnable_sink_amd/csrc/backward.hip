@@ -153,14 +153,24 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
     dsink_part[((size_t)b * Hq + h) * gridDim.x + blockIdx.x] = ((ws[0] + ws[1]) + ws[2]) + ws[3];
 }
 
-__global__ void bwd_dsink_reduce_kernel(const float* __restrict__ part, float* __restrict__ dsink,
-                                        int B, int Hq, int nblk) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= Hq) return;
-  float s = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int k = 0; k < nblk; ++k) s += part[((size_t)b * Hq + h) * nblk + k];
-  dsink[h] = s;
+// dSink_h: one workgroup per head.  Thread t sums partials t, t + 256, ...
+// of the head (over sequences, then row blocks), then the 256 sums are added
+// by a fixed tree: the order depends only on B and nblk, never on timing.
+__global__ __launch_bounds__(kThreads) void bwd_dsink_reduce_kernel(
+    const float* __restrict__ part, float* __restrict__ dsink, int Hq, int B, int nblk) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int n = B * nblk;
+  float acc = 0.f;
+  for (int i = tid; i < n; i += kThreads) {
+    const int b = i / nblk, k = i - b * nblk;
+    acc += part[((size_t)b * Hq + h) * nblk + k];
+  }
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) acc += __shfl_xor(acc, x, 64);
+  __shared__ float ws[kThreads / 64];
+  if ((tid & 63) == 0) ws[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) dsink[h] = (ws[0] + ws[1]) + (ws[2] + ws[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -421,7 +431,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(
   const int g = Hq / Hkv;
   const int groups = g / hpw;
   const int R = 32 * (4 / hpw);
-  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R);
+  const WorkItem wi =
+      work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R, cu_q == nullptr);
   const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
   const SeqRows sr = seq_rows(cu_q, cu_k, b, Sq, Sk, Hq, total_q);
   const int nq = sr.nq, nk = sr.nk;
@@ -617,7 +628,7 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
                                                          a.scale, sl2, a.causal, a.w1, a.w2);
   }
   if (a.sink && a.dsink)
-    bwd_dsink_reduce_kernel<<<(a.Hq + 63) / 64, 64, 0, stream>>>(part, a.dsink, a.B, a.Hq, nblk);
+    bwd_dsink_reduce_kernel<<<a.Hq, kThreads, 0, stream>>>(part, a.dsink, a.Hq, a.B, nblk);
   return hipGetLastError();
 }
 

@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const int g = Hq / Hkv;
   const int groups = g / hpw;  // workgroups per KV head
   const int R = RW * (4 / hpw);
-  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R);
+  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R, true);
   const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
   const int h = kvh * g + wi.grp * hpw + (wave % hpw);
   const int rb = wave / hpw;   // row block of this wave inside the workgroup
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
   const int g = Hq / Hkv;
   const int groups = g / hpw;
   const int R = RW * (4 / hpw);
-  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (max_sq + R - 1) / R);
+  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (max_sq + R - 1) / R, false);
   const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
   const int qbase = cu_q[b], nq = cu_q[b + 1] - qbase;
   const int row0 = wi.tile * R;
