@@ -20,4 +20,5 @@ from .sink_attention import (  # noqa: F401
     backward,
     prefill_varlen,
     backward_varlen,
+    index_paged,
 )

@@ -24,6 +24,12 @@ Sources (web pages; cited by title and section):
              1024+7168) and the maintainer's comment that the last 7168 tokens
              are kept for each sequence.
 
+  [dsa]      "SGLang dsa" (s1mplewind blog), sections "layer0" and "Other
+             Layers": the lightning indexer selects, per query, a list of KV
+             entries (sink-like absolute positions plus relative/local ones);
+             the lists of 128 adjacent queries overlap by about a third of
+             their size; the first 2048 tokens are attended densely.
+
 Readings where the pages are silent (each also listed in the design doc):
   * the sink is in the units of the already-scaled scores (not multiplied by
     the softmax scale), indexed by query head;
@@ -40,6 +46,10 @@ Readings where the pages are silent (each also listed in the design doc):
     L cached tokens, so new token i sits at position L - nq + i and sees keys
     by the prefill rule above, the window included (the pages define the
     window for decode only; the per-query rule is its prefill form).
+  * index-list selection: one list of token positions serves a block of
+    block_q consecutive query rows of a sequence; a row attends to the
+    listed tokens at or before its own position (plus the sink); entries
+    < 0 or >= L are empty slots; a list names each token at most once;
   * variable-length (packed) forward and backward: each sequence is its own
     attention problem with its own Sq and Sk (bottom-right causal inside the
     sequence); no key of one sequence is visible to a query of another; the
@@ -395,3 +405,58 @@ def backward_varlen(q, cu_seqlens_q, k, v, cu_seqlens_k, sink, dout, scale, caus
         o[a:e] = r[4][0]
         lse[:, a:e] = r[5][0]
     return dq, dk, dv, dsink, o, lse
+
+
+def _attend(s, sig, V):
+    """Softmax with the sink over masked logits s [rows, n] (-inf = not
+    visible) and values V [n, D]; the same definition as prefill's."""
+    rowmax = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], NEG_INF)
+    m = np.maximum(sig, rowmax)
+    live = np.isfinite(m)
+    mm = np.where(live, m, 0.0)
+    e = np.where(np.isfinite(s), np.exp(s - mm[:, None]), 0.0)
+    z = np.exp(sig - mm) + e.sum(axis=1)
+    o = np.where(live[:, None], (e @ V) / np.where(live, z, 1.0)[:, None], 0.0)
+    lse = np.where(live, mm + np.log(np.where(live, z, 1.0)), NEG_INF)
+    return o, lse
+
+
+def index_paged(q, cu_seqlens_q, k_cache, v_cache, block_table, seqlens, kv_index, cu_blocks,
+                block_q, sink, scale):
+    """Sink attention over per-query-block KV index lists ([dsa] layer0,
+    Other Layers; the sink as in [trtllm] Summary of Changes).
+
+    Sequence b's new queries are rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+    of q [total_q, Hq, D], the last nq_b of its L_b = seqlens[b] cached tokens
+    (row i at position p = L_b - nq_b + i).  Row i reads list
+    kv_index[cu_blocks[b] + i // block_q] (token positions; entries < 0 or
+    >= L_b are empty) and attends to its tokens t <= p.
+    Returns (o [total_q, Hq, D], lse [Hq, total_q]).
+    """
+    q = _f64(q)
+    total, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    g = Hq // Hkv
+    sig = _sink_vector(sink, Hq)
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    cb = np.asarray(cu_blocks, dtype=np.int64)
+    idx_all = np.asarray(kv_index, dtype=np.int64)
+    ks, vs = gather_kv(k_cache, v_cache, block_table, seqlens, k_cache.shape[1], None)
+    ks, vs = [_f64(x) for x in ks], [_f64(x) for x in vs]
+    o = np.zeros((total, Hq, D))
+    lse = np.full((Hq, total), NEG_INF)
+    for b in range(len(ks)):
+        a, e = int(cu[b]), int(cu[b + 1])
+        nq, L = e - a, len(ks[b])
+        for i0 in range(0, nq, block_q):
+            i1 = min(nq, i0 + block_q)
+            idx = idx_all[cb[b] + i0 // block_q]
+            idx = idx[(idx >= 0) & (idx < L)]
+            pos = L - nq + np.arange(i0, i1)
+            vis = idx[None, :] <= pos[:, None]
+            for h in range(Hq):
+                K = ks[b][idx, h // g, :]
+                V = vs[b][idx, h // g, :]
+                sc = np.where(vis, scale * (q[a + i0:a + i1, h, :] @ K.T), NEG_INF)
+                o[a + i0:a + i1, h, :], lse[h, a + i0:a + i1] = _attend(sc, sig[h], V)
+    return o, lse

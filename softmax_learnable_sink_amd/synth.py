@@ -12,6 +12,7 @@ Draw order (fixed, so a seed names one input set):
   prefill:  q, k, v, [dout], sink
   decode:   q, sink, context lengths, page permutation, k pool, v pool
   varlen:   q, k, v, [dout], sink (packed; lengths from rng((seed, 3000)))
+  index:    the extend case of the same seed, then index lists from rng((seed, 4000))
 Each N(0,1) tensor is drawn in blocks of 2^22 elements; block i of the n-th
 tensor of a case comes from numpy.random.default_rng((seed, n, i)), so large
 pools can be drawn by several threads with a result that does not depend on
@@ -219,4 +220,48 @@ def extend_case(B, Hq, Hkv, D, page_size, q_lo, q_hi, ctx_lo, ctx_hi, dtype=BF16
     case["q"] = dr.normal((int(cu[-1]), Hq, D), dtype)
     case.update({"cu_seqlens_q": cu, "seqlens": L, "q_lens": q_lens,
                  "max_seqlen_q": int(q_lens.max()) if B else 0})
+    return case
+
+
+def index_case(B, Hq, Hkv, D, page_size, q_lo, q_hi, ctx_lo, ctx_hi, block_q, topk, dtype=BF16,
+               seed=0, sink=True, q_lens=None, ctx_lens=None, n_first=64, n_local=512,
+               shuffle=False, pad=0, nan_poison=False):
+    """Chunked-prefill inputs (as extend_case) plus one KV index list per block of
+    block_q query rows of each sequence: kv_index [num_blocks, topk] int32 and
+    cu_blocks [B+1] (sequence b's lists are rows cu_blocks[b] ..).
+
+    For a block whose last row sits at position p1: if p1 + 1 <= topk - pad the
+    list is every token 0..p1; otherwise it is the first n_first tokens, the
+    n_local tokens ending at p1 (at most (topk - pad) / 8 and / 2 of them), and
+    a uniform sample of the tokens between them, topk - pad entries in all.  Lists are ascending (or shuffled) and end
+    in `pad` (or more) entries of -1.
+    """
+    case = extend_case(B, Hq, Hkv, D, page_size, q_lo, q_hi, ctx_lo, ctx_hi, dtype=dtype,
+                       seed=seed, sink=sink, q_lens=q_lens, ctx_lens=ctx_lens,
+                       nan_poison=nan_poison)
+    rng = np.random.default_rng((int(seed), 4000))
+    k_sel = topk - pad
+    nq = case["q_lens"].astype(np.int64)
+    L = case["seqlens"].astype(np.int64)
+    nblk = (nq + block_q - 1) // block_q
+    cu_b = np.zeros(B + 1, dtype=np.int32)
+    cu_b[1:] = np.cumsum(nblk)
+    lists = np.full((int(cu_b[-1]), topk), -1, dtype=np.int32)
+    for b in range(B):
+        for j in range(int(nblk[b])):
+            p1 = int(L[b] - nq[b] + min(nq[b], (j + 1) * block_q) - 1)
+            if p1 + 1 <= k_sel:
+                sel = np.arange(max(p1 + 1, 0))
+            else:
+                nf, nl = min(n_first, k_sel // 8), min(n_local, k_sel // 2)
+                first = np.arange(nf)
+                local = np.arange(p1 + 1 - nl, p1 + 1)
+                mid = np.arange(nf, p1 + 1 - nl)
+                sel = np.concatenate([first, rng.choice(mid, k_sel - nf - nl, replace=False),
+                                      local])
+                sel.sort()
+            if shuffle:
+                sel = rng.permutation(sel)
+            lists[cu_b[b] + j, :len(sel)] = sel
+    case.update({"kv_index": lists, "cu_blocks": cu_b, "block_q": block_q, "topk": topk})
     return case
