@@ -134,6 +134,35 @@ int attn_sink_fwd_extend_paged(const void* q, const void* k_cache, const void* v
                                void* hip_stream);
 
 /*
+ * Attention over KV index lists (chunked prefill against a paged cache).  As
+ * in attn_sink_fwd_extend_paged, sequence b's nq_b new queries are rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and sit at positions
+ * L_b - nq_b + i of its L_b = seqlens_k[b] cached tokens.  The rows of each
+ * block of block_q consecutive queries of a sequence share one list of token
+ * positions (an indexer's selection: the SGLang DSA write-up, sections layer0
+ * and Other Layers, finds the selections of 128 adjacent queries largely
+ * shared); row i attends to the tokens of list kv_index[cu_blocks[b] +
+ * i / block_q] at or before its position, plus the sink.
+ *   kv_index   [num_blocks, topk] int32 device: token positions; entries < 0
+ *              or >= L_b are empty; a list names each token at most once
+ *   cu_blocks  [B+1] int32 device: sequence b's lists are rows cu_blocks[b] ..
+ *              cu_blocks[b] + ceil(nq_b / block_q) - 1
+ *   other arguments as in attn_sink_fwd_extend_paged (lse [Hq, total_q]).
+ * A row whose list holds no visible token gets O = 0 and LSE = sink (or
+ * -inf).  Requirements (ATTN_SINK_ERR_UNSUPPORTED otherwise): bf16; D in {64,
+ * 128}; Hq / Hkv a multiple of 4; block_q a positive multiple of 64;
+ * 1 <= topk <= 2048; page_size a power of two in [1, 256].  The device arrays
+ * are not checked: they must hold the stated ranges.
+ */
+int attn_sink_fwd_index_paged(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* cu_seqlens_q,
+                              const int32_t* seqlens_k, const int32_t* kv_index,
+                              const int32_t* cu_blocks, const float* sink, void* o, float* lse,
+                              int B, int total_q, int max_seqlen_q, int Hq, int Hkv, int D,
+                              int page_size, int max_pages_per_seq, int num_pages, int block_q,
+                              int topk, float softmax_scale, int dtype, void* hip_stream);
+
+/*
  * Variable-length (packed) forward.  Sequence b's queries are rows
  * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and its keys rows
  * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v; it is the prefill problem

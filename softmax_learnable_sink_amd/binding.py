@@ -31,6 +31,7 @@ _SIGNATURES = {
     "attn_sink_fwd_decode_paged": ([_vp] * 8 + [_i] * 7 + [_f, _i, _i, _i, _vp, _sz, _i, _vp], _i),
     "attn_sink_fwd_extend_paged": ([_vp] * 9 + [_i] * 9 + [_f, _i, _i, _i, _vp], _i),
     "attn_sink_fwd_varlen": ([_vp] * 8 + [_i] * 7 + [_f, _i, _i, _i, _i, _vp], _i),
+    "attn_sink_fwd_index_paged": ([_vp] * 11 + [_i] * 11 + [_f, _i, _vp], _i),
     "attn_sink_decode_workspace_bytes": ([_i] * 9, _sz),
     "attn_sink_bwd": ([_vp] * 11 + [_i] * 6 + [_f, _i, _i, _i, _vp, _sz, _i, _vp], _i),
     "attn_sink_bwd_workspace_bytes": ([_i] * 6, _sz),
@@ -224,6 +225,47 @@ def attn_sink_fwd_extend_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, s
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cu_seqlens_q),
         _ptr(seqlens_k), _ptr(sink), _ptr(out), _ptr(lse), B, total_q, int(max_seqlen_q), Hq, Hkv,
         D, page_size, block_table.shape[1], num_pages, scale, w1, w2, BF16, _stream(dev)))
+    return out, lse
+
+
+def attn_sink_fwd_index_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
+                              max_seqlen_q, kv_index, cu_blocks, block_q, sink=None,
+                              softmax_scale=None, out=None, lse=None, return_lse=True):
+    """O [total_q,Hq,D], LSE [Hq,total_q] for packed new queries against a paged KV cache,
+    each block of block_q query rows of a sequence attending to the tokens of one row of
+    kv_index [num_blocks, topk] (sequence b's rows start at cu_blocks[b]) at or before its
+    position."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    for name, t in (("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q),
+                    ("seqlens_k", seqlens_k), ("kv_index", kv_index), ("cu_blocks", cu_blocks)):
+        _need(t, name, torch.int32, dev)
+    total_q, Hq, D = q.shape
+    num_pages, page_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (num_pages, page_size, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [num_pages, page_size, Hkv, D]")
+    B = seqlens_k.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != B or cu_seqlens_q.shape != (B + 1,) \
+            or cu_blocks.shape != (B + 1,) or kv_index.dim() != 2:
+        raise ValueError("block_table must be [B, max_pages], cu_seqlens_q and cu_blocks [B+1], "
+                         "seqlens_k [B], kv_index [num_blocks, topk]")
+    if sink is not None:
+        _need(sink, "sink", torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib().attn_sink_fwd_index_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cu_seqlens_q),
+        _ptr(seqlens_k), _ptr(kv_index), _ptr(cu_blocks), _ptr(sink), _ptr(out), _ptr(lse), B,
+        total_q, int(max_seqlen_q), Hq, Hkv, D, page_size, block_table.shape[1], num_pages,
+        int(block_q), kv_index.shape[1], scale, BF16, _stream(dev)))
     return out, lse
 
 

@@ -161,6 +161,53 @@ int attn_sink_fwd_extend_paged(const void* q, const void* k_cache, const void* v
                     "attn_sink_fwd_extend_paged launch");
 }
 
+int attn_sink_fwd_index_paged(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* cu_seqlens_q,
+                              const int32_t* seqlens_k, const int32_t* kv_index,
+                              const int32_t* cu_blocks, const float* sink, void* o, float* lse,
+                              int B, int total_q, int max_seqlen_q, int Hq, int Hkv, int D,
+                              int page_size, int max_pages_per_seq, int num_pages, int block_q,
+                              int topk, float softmax_scale, int dtype, void* hip_stream) {
+  REQUIRE(dtype == ATTN_SINK_BF16, ATTN_SINK_ERR_UNSUPPORTED,
+          "index-list attention supports bf16 only (dtype %d)", dtype);
+  REQUIRE(B >= 1 && total_q >= 0 && max_seqlen_q >= 0, ATTN_SINK_ERR_INVALID_ARG,
+          "need B >= 1, total_q >= 0, max_seqlen_q >= 0 (got %d, %d, %d)", B, total_q,
+          max_seqlen_q);
+  if (int r = check_heads(Hq, Hkv, D)) return r;
+  REQUIRE((Hq / Hkv) % 4 == 0, ATTN_SINK_ERR_UNSUPPORTED,
+          "index-list attention needs Hq / Hkv to be a multiple of 4 (got %d)", Hq / Hkv);
+  REQUIRE(block_q >= 64 && block_q % 64 == 0, ATTN_SINK_ERR_UNSUPPORTED,
+          "block_q must be a positive multiple of 64 (got %d)", block_q);
+  REQUIRE(topk >= 1 && topk <= 2048, ATTN_SINK_ERR_UNSUPPORTED,
+          "topk must be in [1, 2048] (got %d)", topk);
+  if (int r = check_scale(softmax_scale)) return r;
+  REQUIRE(pow2(page_size) && page_size <= 256, ATTN_SINK_ERR_UNSUPPORTED,
+          "page_size must be a power of two in [1, 256] (got %d)", page_size);
+  REQUIRE(max_pages_per_seq >= 1 && num_pages >= 1, ATTN_SINK_ERR_INVALID_ARG,
+          "max_pages_per_seq and num_pages must be >= 1");
+  REQUIRE(fits_int32((long long)num_pages * page_size) &&
+              fits_int32((long long)max_pages_per_seq * page_size),
+          ATTN_SINK_ERR_UNSUPPORTED, "num_pages or max_pages_per_seq times page_size exceeds 2^31 - 1");
+  REQUIRE(fits_int32((long long)total_q * Hq), ATTN_SINK_ERR_UNSUPPORTED,
+          "too many rows for 32-bit row indices");
+  REQUIRE(q && k_cache && v_cache && block_table && cu_seqlens_q && seqlens_k && kv_index &&
+              cu_blocks && o,
+          ATTN_SINK_ERR_INVALID_ARG,
+          "q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, kv_index, cu_blocks and o "
+          "must not be NULL");
+  REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(o),
+          ATTN_SINK_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
+  REQUIRE(aligned4(block_table) && aligned4(cu_seqlens_q) && aligned4(seqlens_k) &&
+              aligned4(kv_index) && aligned4(cu_blocks) && aligned4(sink) && aligned4(lse),
+          ATTN_SINK_ERR_INVALID_ARG, "int32 and fp32 arrays must be 4-byte aligned");
+  if (total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;  // nothing to compute
+  IndexArgs a{q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, kv_index, cu_blocks,
+              sink, o, lse, B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages_per_seq,
+              block_q, topk, softmax_scale};
+  return hip_status(launch_index_bf16(a, static_cast<hipStream_t>(hip_stream)),
+                    "attn_sink_fwd_index_paged launch");
+}
+
 int attn_sink_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                          const int32_t* cu_seqlens_k, const float* sink, void* o, float* lse,
                          int B, int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv,

@@ -45,6 +45,28 @@ struct ExtendArgs {
 
 hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream);
 
+// Packed new queries against a paged cache; each block of block_q query rows
+// of a sequence attends to the tokens of one list (row cu_blocks[b] + i /
+// block_q of kv_index [*, topk]).  Needs Hq / Hkv % 4 == 0 and block_q a
+// multiple of 64.
+struct IndexArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seqlens_k;
+  const int32_t* kv_index;
+  const int32_t* cu_blocks;
+  const float* sink;
+  void* o;
+  float* lse;  // [Hq, total_q] or NULL
+  int B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages, block_q, topk;
+  float scale;
+};
+
+hipError_t launch_index_bf16(const IndexArgs& a, hipStream_t stream);
+
 struct DecodeArgs {
   const void* q;
   const void* k_cache;

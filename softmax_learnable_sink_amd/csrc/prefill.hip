@@ -16,6 +16,8 @@
 // softmax denominator).
 //
 // fp32 path: a plain VALU kernel, one thread per query row, K/V tiles in LDS.
+#include <climits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -210,6 +212,33 @@ struct WaveRows {
   // the exact running max of the tile, P rounded to bf16 for P V.
   __device__ __forceinline__ void softmax(f32x16 (&st)[2][QB], bf16x8 (&pf)[2][QB][2], int key0,
                                           const RowGeom& g, float sl2, int hh) {
+    mask(st, key0, g, hh);
+    online(st, pf, sl2);
+  }
+
+  // Keys named by a list: element i of key block kb is tile key 32*kb + 16*hh + i,
+  // whose token position is tok[that key] (INT_MAX for an empty entry); it is
+  // visible to the lane's row at position p iff token <= p.
+  __device__ __forceinline__ void mask_tokens(f32x16 (&st)[2][QB], const int* tok, int p_lane,
+                                              int hh) const {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int4 x = *reinterpret_cast<const int4*>(tok + 32 * kb + 16 * hh + 4 * c);
+        const int t[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int p = p_lane + 32 * qb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            st[kb][qb][4 * c + e] = t[e] <= p ? st[kb][qb][4 * c + e] : kNegInf;
+        }
+      }
+  }
+
+  __device__ __forceinline__ void mask(f32x16 (&st)[2][QB], int key0, const RowGeom& g,
+                                       int hh) const {
     // Per lane and key block, element i (key j = base + i) is visible iff
     // i <= hi (causal bound and j < Sk) and, with a window, i < a (first
     // window) or i > bnd (last window).
@@ -237,6 +266,9 @@ struct WaveRows {
         }
       }
     }
+  }
+
+  __device__ __forceinline__ void online(f32x16 (&st)[2][QB], bf16x8 (&pf)[2][QB][2], float sl2) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = kNegInf;
@@ -528,6 +560,141 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Index-list selection: the keys of a block of query rows are the tokens named
+// by one list (positions in the sequence, read through the block table).  The
+// list is staged in LDS once; per 64-entry tile the block-table pages are
+// fetched two tiles ahead and the K/V rows one tile ahead.
+// ---------------------------------------------------------------------------
+constexpr int kMaxList = 2048;  // longest list (LDS-resident, 8 KB)
+
+template <int D>
+struct ListTile {
+  static constexpr int CH = D / 8;
+  static constexpr int KN = kBN * CH / kThreads;
+  uint4 kr[KN], vr[KN];
+  int ps[KN];  // block-table pages, then slots, of the tile two ahead
+
+  __device__ __forceinline__ static int row_of(int tid, int i) { return (tid + i * kThreads) / CH; }
+  __device__ __forceinline__ static int chunk_of(int tid, int i) { return (tid + i * kThreads) % CH; }
+
+  // tok: the tile's 64 tokens (INT_MAX: empty entry)
+  __device__ __forceinline__ void fetch_pages(const int* tok, const int32_t* bt_row, int shift,
+                                              int tid) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int t = tok[row_of(tid, i)];
+      ps[i] = bt_row[(t == INT_MAX ? 0 : t) >> shift];
+    }
+  }
+  __device__ __forceinline__ void pages_to_slots(const int* tok, int shift, int tid) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int t = tok[row_of(tid, i)];
+      ps[i] = t == INT_MAX ? 0 : (ps[i] << shift) | (t & ((1 << shift) - 1));
+    }
+  }
+  __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, size_t rs,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const size_t off = (size_t)ps[i] * rs + chunk_of(tid, i) * 8;
+      kr[i] = *reinterpret_cast<const uint4*>(kbase + off);
+      vr[i] = *reinterpret_cast<const uint4*>(vbase + off);
+    }
+  }
+  // V rows of empty entries are written as zeros (the slot they read is only
+  // a stand-in); their scores are masked.
+  __device__ __forceinline__ void store(Lds<D>& s, int buf, const int* tok, int tid) const {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int key = row_of(tid, i), c = chunk_of(tid, i);
+      const bool ok = tok[key] != INT_MAX;
+      const int row = (key & ~31) + k_lds_row(key & 31);
+      *reinterpret_cast<uint4*>(&s.k[buf][row * Lds<D>::KS + c * 8]) = kr[i];
+      *reinterpret_cast<uint4*>(&s.v[buf][key * Lds<D>::VS + c * 8]) =
+          uint4{ok ? vr[i].x : 0u, ok ? vr[i].y : 0u, ok ? vr[i].z : 0u, ok ? vr[i].w : 0u};
+    }
+  }
+};
+
+// Packed new queries against a paged cache (as extend_kernel); the rows of
+// each block of block_q rows of a sequence attend to the tokens of one list
+// (kv_index row cu_blocks[b] + row / block_q) at or before their positions.
+template <int D, int QB>
+__global__ __launch_bounds__(kThreads, 2) void index_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ seqlens, const int32_t* __restrict__ kv_index,
+    const int32_t* __restrict__ cu_blocks, const float* __restrict__ sink, __bf16* __restrict__ o,
+    float* __restrict__ lse, int B, int total_q, int max_sq, int Hq, int Hkv, int page_shift,
+    int max_pages, int block_q, int topk, float sl2) {
+  __shared__ Lds<D> s;
+  __shared__ __attribute__((aligned(16))) int tokl[kMaxList];
+  constexpr int RW = 32 * QB;  // rows per wave = rows per workgroup (4 heads of a group)
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int g = Hq / Hkv;
+  const WorkItem wi = work_item(blockIdx.x, B * Hkv, g / 4, (max_sq + RW - 1) / RW, false);
+  const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
+  const int qbase = cu_q[b], nq = cu_q[b + 1] - qbase;
+  const int row0 = wi.tile * RW;
+  if (row0 >= nq) return;  // uniform over the workgroup
+  const int h = kvh * g + wi.grp * 4 + wave;
+  const int L = seqlens[b];
+  const int p_lane = L - nq + row0 + l32;
+  const int nt = (topk + kBN - 1) / kBN;
+
+  // the block's list -> LDS, padded to whole tiles; entries outside [0, L) are empty
+  {
+    const int32_t* list = kv_index + (size_t)(cu_blocks[b] + row0 / block_q) * topk;
+    for (int e = tid; e < nt * kBN; e += kThreads) {
+      const int x = e < topk ? list[e] : -1;
+      tokl[e] = ((x >= 0) & (x < L)) ? x : INT_MAX;
+    }
+  }
+
+  WaveRows<D, QB> wr;
+  wr.init(q + (size_t)qbase * Hq * D, sink, nq, Hq, h, row0, hh, l32);
+
+  const size_t rs = (size_t)Hkv * D;
+  const __bf16* kb_ = kc + (size_t)kvh * D;
+  const __bf16* vb_ = vc + (size_t)kvh * D;
+  const int32_t* bt_row = bt + (size_t)b * max_pages;
+
+  __syncthreads();
+  ListTile<D> lt;
+  lt.fetch_pages(tokl, bt_row, page_shift, tid);
+  lt.pages_to_slots(tokl, page_shift, tid);
+  lt.load(kb_, vb_, rs, tid);
+  lt.store(s, 0, tokl, tid);
+  if (nt > 1) {
+    lt.fetch_pages(tokl + kBN, bt_row, page_shift, tid);
+    lt.pages_to_slots(tokl + kBN, page_shift, tid);
+  }
+  __syncthreads();
+  for (int it = 0; it < nt; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < nt) lt.load(kb_, vb_, rs, tid);
+    if (it + 2 < nt) lt.fetch_pages(tokl + (it + 2) * kBN, bt_row, page_shift, tid);
+    f32x16 st[2][QB];
+    bf16x8 pf[2][QB][2];
+    wr.scores(s.k[buf], st, l32, hh);
+    wr.mask_tokens(st, tokl + it * kBN, p_lane, hh);
+    wr.online(st, pf, sl2);
+    wr.pv(s.v[buf], pf, lane);
+    if (it + 1 < nt) lt.store(s, buf ^ 1, tokl + (it + 1) * kBN, tid);
+    if (it + 2 < nt) lt.pages_to_slots(tokl + (it + 2) * kBN, page_shift, tid);
+    __syncthreads();
+  }
+  wr.finish(o + (size_t)qbase * Hq * D, lse ? lse + (size_t)h * total_q + qbase : nullptr, nq,
+            Hq, h, row0, hh, l32);
+}
+
+// ---------------------------------------------------------------------------
 // fp32 VALU path: one thread per query row, 32-key tiles of K and V in LDS.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -647,6 +814,31 @@ hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream) {
         q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.cu_seqlens_k, a.sink, o, a.lse,
         a.B, a.total_q, a.max_seqlen_q, a.Hq, a.Hkv, hpw, shift, a.max_pages, sl2, a.causal, a.w1,
         a.w2);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_index_bf16(const IndexArgs& a, hipStream_t stream) {
+  const float sl2 = a.scale * kLog2e;
+  int shift = 0;
+  while ((1 << shift) < a.page_size) ++shift;
+  const auto* q = static_cast<const __bf16*>(a.q);
+  const auto* kc = static_cast<const __bf16*>(a.k_cache);
+  const auto* vc = static_cast<const __bf16*>(a.v_cache);
+  auto* o = static_cast<__bf16*>(a.o);
+  const int cols = a.B * a.Hkv * (a.Hq / a.Hkv / 4);
+  if (a.D == 64) {
+    const dim3 grid(cols * ((a.max_seqlen_q + 63) / 64));
+    index_kernel<64, 2><<<grid, kThreads, 0, stream>>>(
+        q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.kv_index, a.cu_blocks, a.sink, o,
+        a.lse, a.B, a.total_q, a.max_seqlen_q, a.Hq, a.Hkv, shift, a.max_pages, a.block_q, a.topk,
+        sl2);
+  } else {
+    const dim3 grid(cols * ((a.max_seqlen_q + 31) / 32));
+    index_kernel<128, 1><<<grid, kThreads, 0, stream>>>(
+        q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.kv_index, a.cu_blocks, a.sink, o,
+        a.lse, a.B, a.total_q, a.max_seqlen_q, a.Hq, a.Hkv, shift, a.max_pages, a.block_q, a.topk,
+        sl2);
   }
   return hipGetLastError();
 }

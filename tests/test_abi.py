@@ -35,7 +35,7 @@ def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("attn_sink_fwd_prefill", "attn_sink_fwd_decode_paged", "attn_sink_bwd",
               "attn_sink_fwd_extend_paged", "attn_sink_fwd_varlen", "attn_sink_bwd_varlen",
-              "attn_sink_bwd_varlen_workspace_bytes",
+              "attn_sink_bwd_varlen_workspace_bytes", "attn_sink_fwd_index_paged",
               "attn_sink_decode_workspace_bytes", "attn_sink_bwd_workspace_bytes",
               "attn_sink_decode_select_slots", "attn_sink_gather_kv", "attn_sink_last_error",
               "attn_sink_abi_version"):
@@ -194,6 +194,40 @@ def test_bwd_workspace_query(lib):
     n = binding.attn_sink_bwd_workspace_bytes(B, S, S, Hq, 8, 64)
     assert n == 4 * (B * Hq * S + B * Hq * (S // 64))
     assert binding.attn_sink_bwd_workspace_bytes(B, S, S, Hq, 7, 64) == 0
+
+
+def _index(lib, **kw):
+    a = dict(B=2, tq=10, mq=6, Hq=8, Hkv=2, D=64, P=16, maxp=4, npages=8, bq=64, topk=256,
+             scale=0.125, dtype=binding.BF16, q=P, idx=P, cb=P)
+    a.update(kw)
+    return lib.attn_sink_fwd_index_paged(a["q"], P, P, P, P, P, a["idx"], a["cb"], None, P, None,
+                                         a["B"], a["tq"], a["mq"], a["Hq"], a["Hkv"], a["D"],
+                                         a["P"], a["maxp"], a["npages"], a["bq"], a["topk"],
+                                         a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dtype=binding.F32), binding.ERR_UNSUPPORTED, "bf16"),
+    (dict(B=0), binding.ERR_INVALID_ARG, "B >= 1"),
+    (dict(Hq=6, Hkv=3), binding.ERR_UNSUPPORTED, "multiple of 4"),
+    (dict(bq=96), binding.ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(bq=0), binding.ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(topk=0), binding.ERR_UNSUPPORTED, "topk"),
+    (dict(topk=4096), binding.ERR_UNSUPPORTED, "topk"),
+    (dict(D=96), binding.ERR_UNSUPPORTED, "64 or 128"),
+    (dict(P=12), binding.ERR_UNSUPPORTED, "power of two"),
+    (dict(idx=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(cb=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(q=P_ODD), binding.ERR_INVALID_ARG, "aligned"),
+    (dict(scale=0.0), binding.ERR_INVALID_ARG, "softmax_scale"),
+])
+def test_index_rejects(lib, kw, status, msg):
+    assert _index(lib, **kw) == status
+    assert msg in binding.last_error()
+
+
+def test_index_with_no_rows_is_a_no_op(lib):
+    assert _index(lib, tq=0, mq=0) == binding.OK
 
 
 def _fwd_varlen(lib, **kw):
