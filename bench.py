@@ -10,6 +10,9 @@ One step runs every entry point once over its synthetic workload:
   train     B2, S8192, 64/8 heads, D64, causal: forward + backward with dSink
   varlen    packed training: 16384 tokens in sequences of U[512, 4096] tokens (the last
             one cut to fit), 64/8 heads, D64, causal: forward + backward with dSink
+  index     index-list selection: B2 x 4096 new tokens on 4096 cached ones, 64/8 heads, D64,
+            page 16, one list of 2048 positions per 128 queries (first 64, last 512, uniform
+            middle), sink
 Each entry point is bracketed by HIP events on the stream it is launched on;
 `value` is the prefill throughput in TFLOP/s of algorithmic work (4*D flops per
 visible (query, key) pair), `decode_gbps` the paged decode's algorithmic HBM
@@ -33,7 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill attention TFLOP/s + paged-decode HBM GB/s (% of MI355X roofline)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-PARTS = ("prefill", "decode", "window32", "window1", "extend", "train", "varlen")
+PARTS = ("prefill", "decode", "window32", "window1", "extend", "train", "varlen", "index")
 
 
 def causal_pairs(B, Hq, Sq, Sk):
@@ -64,6 +67,7 @@ TRAFFIC_KERNELS = {  # key in hbm_traffic.json -> (kernel-name substring, source
     "decode_combine_kernel": ("decode_combine_kernelILi64", "decode"),
     "decode_partial_kernel_d128": ("decode_partial_kernelILi128", "decode"),
     "extend_kernel": ("extend_kernelILi64ELi2", "prefill"),
+    "index_kernel": ("index_kernelILi64ELi2", "prefill"),
 }
 
 
@@ -245,6 +249,40 @@ class Workloads:
                                        shape=f"packed {tq} tokens in {B} sequences "
                                              f"(U[512,4096]) H{Hq}/{Hkv} D{D} causal bf16 fwd+bwd")
             self.vl = t
+        if "index" in parts:
+            B, Hq, Hkv, D, bq, topk = 2, 64, 8, 64, 128, 2048
+            c = synth.index_case(B, Hq, Hkv, D, 16, 4096, 4096, 4096, 4096, bq, topk, seed=0)
+            e = dict(q=dt(c["q"]), k=dt(c["k_cache"]), v=dt(c["v_cache"]),
+                     bt=i32(c["block_table"]), cu=i32(c["cu_seqlens_q"]), sl=i32(c["seqlens"]),
+                     idx=i32(c["kv_index"]), cb=i32(c["cu_blocks"]),
+                     sink=torch.from_numpy(c["sink"]).to(dev), max_sq=c["max_seqlen_q"], bq=bq)
+            e["o"] = torch.empty_like(e["q"])
+            e["lse"] = torch.empty((Hq, e["q"].shape[0]), dtype=torch.float32, device=dev)
+            # visible (row, listed token) pairs: tokens of the row's list at or before it
+            pairs = 0
+            for b in range(B):
+                nq, L = int(c["q_lens"][b]), int(c["seqlens"][b])
+                for j in range(int(c["cu_blocks"][b + 1] - c["cu_blocks"][b])):
+                    lst = c["kv_index"][c["cu_blocks"][b] + j]
+                    lst = np.sort(lst[(lst >= 0) & (lst < L)])
+                    pos = L - nq + np.arange(j * bq, min(nq, (j + 1) * bq))
+                    pairs += int(np.searchsorted(lst, pos, side="right").sum())
+            pairs *= Hq
+            # Q in, O out (bf16), LSE out, K and V of every distinct listed token of a
+            # sequence, the lists, one block-table entry per page touched, small arrays
+            kv_rows, pages = 0, 0
+            for b in range(B):
+                lst = c["kv_index"][c["cu_blocks"][b]:c["cu_blocks"][b + 1]]
+                toks = np.unique(lst[(lst >= 0) & (lst < int(c["seqlens"][b]))])
+                kv_rows += len(toks)
+                pages += len(np.unique(toks // 16))
+            tq = int(c["q_lens"].sum())
+            io = (2 * 2 * tq * Hq * D + 4 * Hq * tq + kv_rows * Hkv * D * 2 * 2
+                  + c["kv_index"].size * 4 + 4 * pages + 4 * (3 * B + 2) + 4 * Hq)
+            self.info["index"] = dict(flops=4 * D * pairs, pairs=pairs, bytes=io,
+                                      shape=f"B{B} nq4096 L8192 H{Hq}/{Hkv} D{D} P16 "
+                                            f"list {topk} per {bq} queries causal bf16")
+            self.ix = e
 
     def run(self, name):
         from softmax_learnable_sink_amd import binding
@@ -263,6 +301,11 @@ class Workloads:
             binding.attn_sink_fwd_extend_paged(e["q"], e["k"], e["v"], e["bt"], e["cu"], e["sl"],
                                                e["max_sq"], e["sink"], softmax_scale=0.125,
                                                out=e["o"], lse=e["lse"])
+        elif name == "index":
+            e = self.ix
+            binding.attn_sink_fwd_index_paged(e["q"], e["k"], e["v"], e["bt"], e["cu"], e["sl"],
+                                              e["max_sq"], e["idx"], e["cb"], e["bq"], e["sink"],
+                                              softmax_scale=0.125, out=e["o"], lse=e["lse"])
         elif name == "train":
             t = self.tr
             binding.attn_sink_fwd_prefill(t["q"], t["k"], t["v"], t["sink"], causal=True,
@@ -396,7 +439,7 @@ def main():
             gbps = info["bytes"] / (ms[p] * 1e-3) / 1e9
             rec.update(gbps=round(gbps, 2), hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
                        algorithmic_bytes=info["bytes"])
-        if p in ("prefill", "extend", "train", "varlen"):
+        if p in ("prefill", "extend", "train", "varlen", "index"):
             tf = info["flops"] / (ms[p] * 1e-3) / 1e12
             rec.update(tflops=round(tf, 2), mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4),
                        algorithmic_flops=info["flops"])

@@ -630,6 +630,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_kernel(
     int max_pages, int block_q, int topk, float sl2) {
   __shared__ Lds<D> s;
   __shared__ __attribute__((aligned(16))) int tokl[kMaxList];
+  __shared__ int tmax[kMaxList / kBN];  // largest token of each tile (INT_MAX if one is empty)
   constexpr int RW = 32 * QB;  // rows per wave = rows per workgroup (4 heads of a group)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -648,14 +649,23 @@ __global__ __launch_bounds__(kThreads, 2) void index_kernel(
   const int p_lane = L - nq + row0 + l32;
   const int nt = (topk + kBN - 1) / kBN;
 
-  // the block's list -> LDS, padded to whole tiles; entries outside [0, L) are empty
+  // the block's list -> LDS, padded to whole tiles; entries outside [0, L) are
+  // empty.  Wave w stages tiles w, w + 4, ... and records each tile's largest
+  // token, so tiles whose tokens all precede the workgroup's first row skip
+  // the mask.
   {
     const int32_t* list = kv_index + (size_t)(cu_blocks[b] + row0 / block_q) * topk;
     for (int e = tid; e < nt * kBN; e += kThreads) {
       const int x = e < topk ? list[e] : -1;
-      tokl[e] = ((x >= 0) & (x < L)) ? x : INT_MAX;
+      const int t = ((x >= 0) & (x < L)) ? x : INT_MAX;
+      tokl[e] = t;
+      int mx = t;
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d, 64));
+      if (lane == 0) tmax[e / kBN] = mx;
     }
   }
+  const int p_first = L - nq + row0;
 
   WaveRows<D, QB> wr;
   wr.init(q + (size_t)qbase * Hq * D, sink, nq, Hq, h, row0, hh, l32);
@@ -683,7 +693,8 @@ __global__ __launch_bounds__(kThreads, 2) void index_kernel(
     f32x16 st[2][QB];
     bf16x8 pf[2][QB][2];
     wr.scores(s.k[buf], st, l32, hh);
-    wr.mask_tokens(st, tokl + it * kBN, p_lane, hh);
+    if (__builtin_amdgcn_readfirstlane(tmax[it]) > p_first)
+      wr.mask_tokens(st, tokl + it * kBN, p_lane, hh);
     wr.online(st, pf, sl2);
     wr.pv(s.v[buf], pf, lane);
     if (it + 1 < nt) lt.store(s, buf ^ 1, tokl + (it + 1) * kBN, tid);
