@@ -431,8 +431,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(
   const int g = Hq / Hkv;
   const int groups = g / hpw;
   const int R = 32 * (4 / hpw);
-  const WorkItem wi =
-      work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R, cu_q == nullptr);
+  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R);
   const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
   const SeqRows sr = seq_rows(cu_q, cu_k, b, Sq, Sk, Hq, total_q);
   const int nq = sr.nq, nk = sr.nk;

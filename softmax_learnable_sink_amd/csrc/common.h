@@ -83,25 +83,25 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, 64));
 }
 
-// Workgroup -> (batch x KV head pair, head group, row tile).  The row tile
-// runs backwards so that the tiles with the most keys under a causal mask
-// start first.  Workgroups are handed to the 8 XCDs round robin by id.  With
-// `by_pair` (every pair has the same work) and a pair count that is a
-// multiple of 8, each XCD gets its own pairs and walks them one after another
-// (all row tiles and head groups of a pair together), so the K/V a pair's
-// workgroups share stays in that XCD's L2.  Otherwise (sequences of different
-// lengths, whose pairs differ in work) the order is tile-major over all pairs,
-// which spreads every sequence over all XCDs.
+// Workgroup -> (batch x KV head pair, head group, row tile).  Workgroups are
+// handed to the 8 XCDs round robin by id.  When the pair count is a multiple
+// of 8, XCD x owns pairs x, x + 8, ... and walks them one after another (all
+// row tiles and head groups of a pair together), so the K/V a pair's
+// workgroups share stays in that XCD's L2; with pairs numbered b * Hkv + kvh
+// and Hkv a multiple of 8, every XCD holds one KV head of every sequence, so
+// sequences of different lengths still give every XCD the same work.  Other
+// pair counts are walked tile-major over all pairs.  Within a pair the row
+// tile runs backwards so that the tiles with the most keys under a causal
+// mask start first.
 struct WorkItem {
   int pair, grp, tile;
 };
-__device__ __forceinline__ WorkItem work_item(int w, int npairs, int groups, int ntiles,
-                                              bool by_pair) {
+__device__ __forceinline__ WorkItem work_item(int w, int npairs, int groups, int ntiles) {
   constexpr int kXcds = 8;
   int pair, grp, z;
-  if (by_pair && npairs % kXcds == 0) {
+  if (npairs % kXcds == 0) {
     const int local = w / kXcds, per_pair = groups * ntiles;
-    pair = (w % kXcds) * (npairs / kXcds) + local / per_pair;
+    pair = w % kXcds + kXcds * (local / per_pair);
     z = (local % per_pair) / groups;
     grp = local % groups;
   } else {

@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const int g = Hq / Hkv;
   const int groups = g / hpw;  // workgroups per KV head
   const int R = RW * (4 / hpw);
-  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R, true);
+  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (Sq + R - 1) / R);
   const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
   const int h = kvh * g + wi.grp * hpw + (wave % hpw);
   const int rb = wave / hpw;   // row block of this wave inside the workgroup
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
   const int g = Hq / Hkv;
   const int groups = g / hpw;
   const int R = RW * (4 / hpw);
-  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (max_sq + R - 1) / R, false);
+  const WorkItem wi = work_item(blockIdx.x, B * Hkv, groups, (max_sq + R - 1) / R);
   const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
   const int qbase = cu_q[b], nq = cu_q[b + 1] - qbase;
   const int row0 = wi.tile * R;
@@ -639,7 +639,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_kernel(
   const int l32 = lane & 31;
 
   const int g = Hq / Hkv;
-  const WorkItem wi = work_item(blockIdx.x, B * Hkv, g / 4, (max_sq + RW - 1) / RW, false);
+  const WorkItem wi = work_item(blockIdx.x, B * Hkv, g / 4, (max_sq + RW - 1) / RW);
   const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
   const int qbase = cu_q[b], nq = cu_q[b + 1] - qbase;
   const int row0 = wi.tile * RW;
