@@ -284,29 +284,31 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const bool need_mask = (i0 + kTile > nq) || (causal && p0 < k1 - 1) ||
                            (w2 > 0 && k1 - 1 >= w1 && p0 + kTile - 1 - w2 >= k0);
 
-    // S and dP of both 32-row blocks first (four independent MFMA chains)
-    f32x16 sa[2], pa[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      sa[qb] = f32x16{};
-      pa[qb] = f32x16{};
-    }
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+    // One tile on one of two straight-line paths (mask or not), chosen once per
+    // tile, so that the whole tile is one block for the scheduler: S and dP of
+    // both 32-row blocks first (four independent MFMA chains), then per row
+    // block P = 2^(S sl2 - LSE log2 e), dS = P (dP - Di) (rounded to bf16
+    // operands) and dV^T += dO^T P, dK^T += Q^T dS, so the exps of one row
+    // block can run under the other's MFMAs.  Lane (hh, l32): key l32, rows
+    // 32*qb + 16*hh + i.  The dV/dK A operands are read transposed from the
+    // natural tiles; k-step (qb, c) covers rows 32*qb + 16*hh + 8*c .. +7.
+    auto tile = [&](auto masked) {
+      f32x16 sa[2], pa[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const int r = (32 * qb + l32) * NS + 16 * ks + 8 * hh;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&s.q[buf][r]);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(&s.dO[buf][r]);
-        sa[qb] = mfma32(qa, kf[ks], sa[qb]);
-        pa[qb] = mfma32(da, vf[ks], pa[qb]);
+        sa[qb] = f32x16{};
+        pa[qb] = f32x16{};
       }
-
-    // P = 2^(S sl2 - LSE log2 e), dS = P (dP - Di), rounded to bf16 operands.
-    // Lane (hh, l32): key l32, rows 32*qb + 16*hh + i.  The mask is applied
-    // on one of two straight-line paths chosen once per tile.
-    bf16x8 pb[2][2], sb[2][2];
-    auto softmax_grad = [&](auto masked) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int r = (32 * qb + l32) * NS + 16 * ks + 8 * hh;
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&s.q[buf][r]);
+          const bf16x8 da = *reinterpret_cast<const bf16x8*>(&s.dO[buf][r]);
+          sa[qb] = mfma32(qa, kf[ks], sa[qb]);
+          pa[qb] = mfma32(da, vf[ks], pa[qb]);
+        }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int rbase = 32 * qb + 16 * hh;
@@ -328,34 +330,30 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             dsv[i] = p * (pa[qb][i] - d2[e]);
           }
         }
+        bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          pb[qb][c] = to_bf16x8(pv[8 * c], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3],
-                                pv[8 * c + 4], pv[8 * c + 5], pv[8 * c + 6], pv[8 * c + 7]);
-          sb[qb][c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
-                                dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
+          pb[c] = to_bf16x8(pv[8 * c], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3],
+                            pv[8 * c + 4], pv[8 * c + 5], pv[8 * c + 6], pv[8 * c + 7]);
+          sb[c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
+                            dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const bf16x8 dot = tr_frag<D>(s.dO[buf], 32 * qb + 8 * c, db, lane);
+            const bf16x8 qt = tr_frag<D>(s.q[buf], 32 * qb + 8 * c, db, lane);
+            dva[db] = mfma32(dot, pb[c], dva[db]);
+            dka[db] = mfma32(qt, sb[c], dka[db]);
+          }
         }
       }
     };
     if (need_mask)
-      softmax_grad(std::true_type{});
+      tile(std::true_type{});
     else
-      softmax_grad(std::false_type{});
-
-    // dV^T += dO^T P, dK^T += Q^T dS (A operands read transposed from the
-    // natural tiles; k-step (qb, c) covers rows 32*qb + 16*hh + 8*c .. +7)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const bf16x8 dot = tr_frag<D>(s.dO[buf], 32 * qb + 8 * c, db, lane);
-          const bf16x8 qt = tr_frag<D>(s.q[buf], 32 * qb + 8 * c, db, lane);
-          dva[db] = mfma32(dot, pb[qb][c], dva[db]);
-          dka[db] = mfma32(qt, sb[qb][c], dka[db]);
-        }
-      }
+      tile(std::false_type{});
 
     if (it + 1 < niter) store_iter(buf ^ 1);
     __syncthreads();
