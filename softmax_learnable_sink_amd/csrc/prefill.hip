@@ -208,12 +208,14 @@ struct WaveRows {
     }
   }
 
-  // Mask (only on tiles that straddle a boundary), online softmax in base 2 with
-  // the exact running max of the tile, P rounded to bf16 for P V.
-  __device__ __forceinline__ void softmax(f32x16 (&st)[2][QB], bf16x8 (&pf)[2][QB][2], int key0,
-                                          const RowGeom& g, float sl2, int hh) {
-    mask(st, key0, g, hh);
-    online(st, pf, sl2);
+  // Does the 64-key tile at key0 straddle a mask boundary of these rows?  Only
+  // such tiles are masked.  Callers issue the score MFMAs inside both arms of
+  // the mask branch: with the branch after them, the unmasked arm had to copy
+  // all score registers (24 v_mov_b64 per tile) to where the masked arm left
+  // its results.
+  __device__ __forceinline__ static bool needs_mask(int key0, const RowGeom& g) {
+    return (key0 + kBN > g.Sk) || (g.causal && key0 + kBN - 1 > g.p_min) ||
+           (g.w2 > 0 && key0 + kBN - 1 >= g.w1 && key0 <= g.p_max - g.w2);
   }
 
   // Keys named by a list: element i of key block kb is tile key 32*kb + 16*hh + i,
@@ -242,32 +244,30 @@ struct WaveRows {
     // Per lane and key block, element i (key j = base + i) is visible iff
     // i <= hi (causal bound and j < Sk) and, with a window, i < a (first
     // window) or i > bnd (last window).
-    const bool need_mask = (key0 + kBN > g.Sk) || (g.causal && key0 + kBN - 1 > g.p_min) ||
-                           (g.w2 > 0 && key0 + kBN - 1 >= g.w1 && key0 <= g.p_max - g.w2);
-    if (need_mask) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int p = g.p_lane + 32 * qb;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int p = g.p_lane + 32 * qb;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int base = key0 + 32 * kb + 16 * hh;
-          const int hi = min(g.causal ? p - base : 15, g.Sk - 1 - base);
-          if (g.w2 > 0) {
-            const int a = g.w1 - base, bnd = p - g.w2 - base;
+      for (int kb = 0; kb < 2; ++kb) {
+        const int base = key0 + 32 * kb + 16 * hh;
+        const int hi = min(g.causal ? p - base : 15, g.Sk - 1 - base);
+        if (g.w2 > 0) {
+          const int a = g.w1 - base, bnd = p - g.w2 - base;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const bool vis = (i <= hi) & ((i < a) | (i > bnd));
-              st[kb][qb][i] = vis ? st[kb][qb][i] : kNegInf;
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st[kb][qb][i] = i <= hi ? st[kb][qb][i] : kNegInf;
+          for (int i = 0; i < 16; ++i) {
+            const bool vis = (i <= hi) & ((i < a) | (i > bnd));
+            st[kb][qb][i] = vis ? st[kb][qb][i] : kNegInf;
           }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st[kb][qb][i] = i <= hi ? st[kb][qb][i] : kNegInf;
         }
       }
     }
   }
 
+  // Online softmax in base 2 with the exact running max of the tile, P rounded
+  // to bf16 for P V.
   __device__ __forceinline__ void online(f32x16 (&st)[2][QB], bf16x8 (&pf)[2][QB][2], float sl2) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -404,8 +404,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     if (it + 1 < ntiles) regs.load(kbase, vbase, rs, tr.tile(it + 1) * kBN, Sk);
     f32x16 st[2][QB];
     bf16x8 pf[2][QB][2];
-    wr.scores(s.k[buf], st, l32, hh);
-    wr.softmax(st, pf, key0, geom, sl2, hh);
+    if (WaveRows<D, QB>::needs_mask(key0, geom)) {
+      wr.scores(s.k[buf], st, l32, hh);
+      wr.mask(st, key0, geom, hh);
+    } else {
+      wr.scores(s.k[buf], st, l32, hh);
+    }
+    wr.online(st, pf, sl2);
     wr.pv(s.v[buf], pf, lane);
     if (it + 1 < ntiles) regs.store(s, buf ^ 1, tid);
     __syncthreads();
@@ -545,10 +550,16 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
       const int buf = it & 1;
       if (it + 1 < nt) pt.load(kb_, vb_, rs, tid);
       if (it + 2 < nt) pt.fetch_pages(bt_row, tr.tile(it + 2) * kBN, L, page_shift, tid);
+      const int key0 = tr.tile(it) * kBN;
       f32x16 st[2][QB];
       bf16x8 pf[2][QB][2];
-      wr.scores(s.k[buf], st, l32, hh);
-      wr.softmax(st, pf, tr.tile(it) * kBN, geom, sl2, hh);
+      if (WaveRows<D, QB>::needs_mask(key0, geom)) {
+        wr.scores(s.k[buf], st, l32, hh);
+        wr.mask(st, key0, geom, hh);
+      } else {
+        wr.scores(s.k[buf], st, l32, hh);
+      }
+      wr.online(st, pf, sl2);
       wr.pv(s.v[buf], pf, lane);
       if (it + 1 < nt) pt.store(s, buf ^ 1, tid);
       if (it + 2 < nt) pt.pages_to_slots(bt_row, kbase, tr.tile(it + 2) * kBN, L, page_shift, tid);
@@ -692,9 +703,12 @@ __global__ __launch_bounds__(kThreads, 2) void index_kernel(
     if (it + 2 < nt) lt.fetch_pages(tokl + (it + 2) * kBN, bt_row, page_shift, tid);
     f32x16 st[2][QB];
     bf16x8 pf[2][QB][2];
-    wr.scores(s.k[buf], st, l32, hh);
-    if (__builtin_amdgcn_readfirstlane(tmax[it]) > p_first)
+    if (__builtin_amdgcn_readfirstlane(tmax[it]) > p_first) {
+      wr.scores(s.k[buf], st, l32, hh);
       wr.mask_tokens(st, tokl + it * kBN, p_lane, hh);
+    } else {
+      wr.scores(s.k[buf], st, l32, hh);
+    }
     wr.online(st, pf, sl2);
     wr.pv(s.v[buf], pf, lane);
     if (it + 1 < nt) lt.store(s, buf ^ 1, tokl + (it + 1) * kBN, tid);
