@@ -293,6 +293,8 @@ int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v
                                       window_last, num_splits);
   REQUIRE(B <= kMaxGridYZ && plan.max_splits <= kMaxGridYZ, ATTN_SINK_ERR_UNSUPPORTED,
           "B (%d) and the split count (%d) must each be <= %lld", B, plan.max_splits, kMaxGridYZ);
+  REQUIRE(fits_int32((long long)B * plan.max_splits * ((Hkv * ((Hq / Hkv + 15) / 16) + 3) / 4)),
+          ATTN_SINK_ERR_UNSUPPORTED, "B * splits * KV-head units exceeds 2^31 - 1 workgroups");
   REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
           "a 16-byte aligned workspace of %zu bytes is required", plan.workspace_bytes);
   REQUIRE(workspace_bytes >= plan.workspace_bytes, ATTN_SINK_ERR_WORKSPACE,

@@ -101,29 +101,121 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Grid (ceil(units / NW), splits, B), NW waves per workgroup.  A unit is one
-// KV head and up to 16 of its query heads; wave w owns unit blockIdx.x*NW + w
-// and walks every token of the workgroup's chunk, so the NW waves of a
-// workgroup read adjacent heads' slices of the same token rows together and
-// share one slot table.  Each wave writes its own partials.
+// The partial kernel's grid is sized by the longest possible sequence, so many
+// of its (sequence, split) slots hold no selected token.  Workgroups that exit
+// at once, interleaved with the working ones, cost a third of the read rate
+// (a read probe of this access pattern: 5.8 -> 4.0 TB/s), so workgroup j takes
+// the j-th chunk that does hold tokens, in sequence order, and the workgroups
+// without work all sit at the end of the grid.  Chunk counts per sequence:
+__device__ __forceinline__ int chunks_of(int L, int w1, int w2, int chunk, int max_splits) {
+  return min(max_splits, (n_selected(L, w1, w2) + chunk - 1) / chunk);
+}
+
+// Up to kScanSeqs sequences, every wave finds its workgroup's chunk itself: a
+// wave-wide prefix scan of the chunk counts (all lengths loaded at once).
+constexpr int kScanSeqs = 256;
+__device__ __forceinline__ bool find_chunk(const int32_t* seqlens, int B, int w1, int w2,
+                                           int chunk, int max_splits, int j, int lane, int& b,
+                                           int& split, int& L) {
+  constexpr int R = kScanSeqs / 64;
+  int len[R], ns[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) len[r] = seqlens[min(64 * r + lane, B - 1)];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    ns[r] = 64 * r + lane < B ? chunks_of(len[r], w1, w2, chunk, max_splits) : 0;
+  int rem = j;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int x = ns[r];  // inclusive scan over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    const int tot = __shfl(x, 63, 64);
+    if (rem < tot) {  // uniform over the wave
+      const uint64_t hit = __ballot(x > rem);
+      const int first = __builtin_ctzll(hit);
+      b = 64 * r + first;
+      split = rem - __shfl(x - ns[r], first, 64);
+      L = __shfl(len[r], first, 64);
+      return true;
+    }
+    rem -= tot;
+  }
+  return false;
+}
+
+// More sequences: decode_plan_kernel lists the chunks once (one workgroup
+// scanning the sequences 256 at a time) and workgroup j reads entry j.
+__global__ __launch_bounds__(256) void decode_plan_kernel(const int32_t* __restrict__ seqlens,
+                                                          int B, int w1, int w2, int chunk,
+                                                          int max_splits,
+                                                          int32_t* __restrict__ items,
+                                                          int32_t* __restrict__ count) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int base = 0;
+  for (int b0 = 0; b0 < B; b0 += 256) {
+    const int b = b0 + tid;
+    const int ns = b < B ? chunks_of(seqlens[b], w1, w2, chunk, max_splits) : 0;
+    int x = ns;  // inclusive scan over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int off = base + x - ns;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    for (int t = 0; t < ns; ++t) items[off + t] = b * max_splits + t;
+    base += (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    __syncthreads();  // wsum is rewritten by the next round
+  }
+  if (tid == 0) *count = base;
+}
+
+// 1-D grid of ceil(units / NW) workgroups per chunk slot (B * splits slots),
+// NW waves per workgroup; the chunk of slot j is found as above (`items` NULL:
+// by the scan; else from the list).  A unit is one KV head and up to 16 of its
+// query heads; wave w owns unit (blockIdx.x % ceil(units/NW))*NW + w and walks
+// every token of the workgroup's chunk, so the NW waves of a workgroup read
+// adjacent heads' slices of the same token rows together and share one slot
+// table.  Each wave writes its own partials.
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seqlens, float* __restrict__ part,
-    int Hq, int Hkv, int hgroups, int page_shift, int max_pages, float sl2, int w1, int w2,
-    int chunk, int max_splits) {
+    const int32_t* __restrict__ items, const int32_t* __restrict__ count, int B, int Hq, int Hkv,
+    int hgroups, int page_shift, int max_pages, float sl2, int w1, int w2, int chunk,
+    int max_splits) {
   __shared__ DecLds<D, NW> s;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int kg = lane >> 4, hl = lane & 15;
-  const int split = blockIdx.y, b = blockIdx.z;
-  const int unit = blockIdx.x * NW + wave;
+  const int nxu = (Hkv * hgroups + NW - 1) / NW;
+  const int j = blockIdx.x / nxu;
+  int b, split, L;
+  if (items) {
+    if (j >= *count) return;  // uniform over the workgroup
+    const int item = items[j];
+    split = item % max_splits;
+    b = item / max_splits;
+    L = seqlens[b];
+  } else if (!find_chunk(seqlens, B, w1, w2, chunk, max_splits, j, lane, b, split, L)) {
+    return;  // uniform over the workgroup
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  split = __builtin_amdgcn_readfirstlane(split);
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int unit = (blockIdx.x % nxu) * NW + wave;
   const bool active = unit < Hkv * hgroups;
   const int kvh = active ? unit / hgroups : 0, hgi = active ? unit % hgroups : 0;
   const int g = Hq / Hkv;
   const int g_eff = min(16, g - 16 * hgi);
   const int h0 = kvh * g + 16 * hgi;
-  const int L = seqlens[b];
   const int nsel = n_selected(L, w1, w2);
   const int u0 = split * chunk;
   if (u0 >= nsel) return;  // uniform over the workgroup
@@ -276,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
   if (bh >= B * Hq) return;
   const int b = bh / Hq, h = bh % Hq;
   const int nsel = n_selected(seqlens[b], w1, w2);
-  const int nsp = nsel > 0 ? (nsel + chunk - 1) / chunk : 0;
+  const int nsp = nsel > 0 ? min(max_splits, (nsel + chunk - 1) / chunk) : 0;
   const float* base = part + (size_t)bh * max_splits * (D + 2);
   const float sig2 = sink ? sink[h] * kLog2e : kNegInf;
 
@@ -396,7 +488,9 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pag
   p.chunk = (int)chunk;
   p.max_splits = (int)((max_sel + chunk - 1) / chunk);
   if (p.max_splits < 1) p.max_splits = 1;
-  p.workspace_bytes = (size_t)B * Hq * p.max_splits * (D + 2) * sizeof(float);
+  // partials, then the chunk list and its length
+  p.workspace_bytes = (size_t)B * Hq * p.max_splits * (D + 2) * sizeof(float) +
+                      ((size_t)B * p.max_splits + 1) * sizeof(int32_t);
   return p;
 }
 
@@ -411,20 +505,28 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   const auto* vc = static_cast<const __bf16*>(a.v_cache);
   auto* o = static_cast<__bf16*>(a.o);
   const dim3 cgrid((a.B * a.Hq + 3) / 4);
+  int32_t* items = reinterpret_cast<int32_t*>(a.partials + (size_t)a.B * a.Hq * a.max_splits *
+                                                               (a.D + 2));
+  int32_t* count = items + (size_t)a.B * a.max_splits;
+  if (a.B > kScanSeqs) {
+    decode_plan_kernel<<<1, 256, 0, stream>>>(a.seqlens, a.B, a.w1, a.w2, a.chunk, a.max_splits,
+                                               items, count);
+  } else {
+    items = nullptr;
+    count = nullptr;
+  }
+  constexpr int NW = 4;
+  const dim3 grid(((units + NW - 1) / NW) * a.B * a.max_splits);
   if (a.D == 64) {
-    constexpr int NW = 4;
-    const dim3 grid((units + NW - 1) / NW, a.max_splits, a.B);
     decode_partial_kernel<64, NW><<<grid, 64 * NW, 0, stream>>>(
-        q, kc, vc, a.block_table, a.seqlens, a.partials, a.Hq, a.Hkv, hgroups, page_shift,
-        a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits);
+        q, kc, vc, a.block_table, a.seqlens, a.partials, items, count, a.B, a.Hq, a.Hkv, hgroups,
+        page_shift, a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits);
     decode_combine_kernel<64><<<cgrid, kThreads, 0, stream>>>(
         a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits);
   } else {
-    constexpr int NW = 4;
-    const dim3 grid((units + NW - 1) / NW, a.max_splits, a.B);
     decode_partial_kernel<128, NW><<<grid, 64 * NW, 0, stream>>>(
-        q, kc, vc, a.block_table, a.seqlens, a.partials, a.Hq, a.Hkv, hgroups, page_shift,
-        a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits);
+        q, kc, vc, a.block_table, a.seqlens, a.partials, items, count, a.B, a.Hq, a.Hkv, hgroups,
+        page_shift, a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits);
     decode_combine_kernel<128><<<cgrid, kThreads, 0, stream>>>(
         a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits);
   }

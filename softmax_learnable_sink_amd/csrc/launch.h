@@ -81,7 +81,8 @@ struct DecodeArgs {
   int w1, w2;
   int chunk;       // selected tokens per split
   int max_splits;  // grid extent over splits
-  float* partials; // [B, Hq, max_splits, D + 2] fp32
+  float* partials; // workspace: [B, Hq, max_splits, D + 2] fp32 partials, then the
+                   // chunk list (B * max_splits int32) and its length (int32)
 };
 
 // Split plan shared by the workspace query and the launch.

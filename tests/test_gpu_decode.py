@@ -63,6 +63,8 @@ def _oracle_decode(case, scale, window, batches=None):
     (4, 32, 8, 128, 16, 40, 500, (32, 96)),  # window, lengths around W1+W2
     (3, 8, 2, 64, 16, 120, 2600, (100, 700)),  # window, L > W1+W2 mostly
     (3, 8, 2, 64, 4, 1, 40, (0, 8)),        # pure sliding window, tiny
+    (300, 8, 2, 64, 16, 1, 2500, None),     # > 256 sequences: chunk list built by a kernel
+    (256, 8, 2, 64, 16, 1, 2500, (64, 512)),  # 256 sequences: chunks found by the scan
 ])
 @pytest.mark.parametrize("use_sink", [True, False])
 def test_decode_matches_oracle(B, Hq, Hkv, D, P, lo, hi, window, use_sink):
