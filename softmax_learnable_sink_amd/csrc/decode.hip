@@ -476,9 +476,9 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pag
   } else {
     // Long chunks amortise each workgroup's start (slot table, first loads);
     // shorter ones only when long ones leave too few waves in flight.  The
-    // starting lengths (1024 tokens at D = 64, 2048 at D = 128) are measured
-    // optima on the paged and the windowed decode workloads.
-    chunk = D == 64 ? 1024 : 2048;
+    // starting length of 2048 tokens is the measured optimum on the paged
+    // (D = 64) and the windowed (D = 128) decode workloads.
+    chunk = 2048;
     if (units * ((max_sel + chunk - 1) / chunk) < 1024) {
       chunk = 1024;
       while (chunk > 128 && units * ((max_sel + chunk - 1) / chunk) < 2048) chunk /= 2;

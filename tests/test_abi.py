@@ -120,7 +120,7 @@ def test_decode_workspace_query(lib):
     # 64 sequences of up to 2048 pages of 16 tokens, 64/8 heads, D 64
     n = binding.attn_sink_decode_workspace_bytes(64, 64, 8, 64, 16, 2048)
     # fp32 partials [B, Hq, splits, D + 2], then the chunk list [B * splits] and its length
-    splits = 2048 * 16 // 1024
+    splits = 2048 * 16 // 2048  # 2048-token chunks
     assert n == 64 * 64 * splits * 66 * 4 + (64 * splits + 1) * 4
     # the window caps the selected length, so the workspace shrinks
     assert binding.attn_sink_decode_workspace_bytes(64, 64, 8, 64, 16, 2048, (1024, 7168)) < n
