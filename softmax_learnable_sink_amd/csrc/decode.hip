@@ -107,48 +107,71 @@ __device__ __forceinline__ void wave_lds_sync() {
 // (a read probe of this access pattern: 5.8 -> 4.0 TB/s), so workgroup j takes
 // the j-th chunk that does hold tokens, in sequence order, and the workgroups
 // without work all sit at the end of the grid.  Chunk counts per sequence:
-__device__ __forceinline__ int chunks_of(int L, int w1, int w2, int chunk, int max_splits) {
-  return min(max_splits, (n_selected(L, w1, w2) + chunk - 1) / chunk);
+// Whole chunks of a sequence, and whether a shorter last one follows.  The
+// chunks are taken whole ones first (in sequence order), then the shorter
+// last ones, so that the shortest work runs at the end of the grid.
+__device__ __forceinline__ int full_chunks(int nsel, int chunk, int max_splits) {
+  return min(max_splits, nsel / chunk);
+}
+__device__ __forceinline__ int part_chunk(int nsel, int chunk, int max_splits) {
+  return (nsel / chunk < max_splits && nsel % chunk != 0) ? 1 : 0;
 }
 
-// Up to kScanSeqs sequences, every wave finds its workgroup's chunk itself: a
-// wave-wide prefix scan of the chunk counts (all lengths loaded at once).
+// Wave-wide search: the first of 64 counts c (one per lane) whose inclusive
+// prefix sum exceeds rem.  On a hit, lane `first` holds it and `before` is
+// the sum of the counts ahead of it; otherwise rem drops by the total.
+__device__ __forceinline__ bool wave_find(int c, int& rem, int lane, int& first, int& before) {
+  int x = c;  // inclusive scan over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  const int tot = __shfl(x, 63, 64);
+  if (rem >= tot) {  // uniform over the wave
+    rem -= tot;
+    return false;
+  }
+  first = __builtin_ctzll(__ballot(x > rem));
+  before = __shfl(x - c, first, 64);
+  return true;
+}
+
+// Up to kScanSeqs sequences, every wave finds its workgroup's chunk itself
+// (all lengths loaded at once).
 constexpr int kScanSeqs = 256;
 __device__ __forceinline__ bool find_chunk(const int32_t* seqlens, int B, int w1, int w2,
                                            int chunk, int max_splits, int j, int lane, int& b,
                                            int& split, int& L) {
   constexpr int R = kScanSeqs / 64;
-  int len[R], ns[R];
+  int len[R], nsel[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) len[r] = seqlens[min(64 * r + lane, B - 1)];
 #pragma unroll
+  for (int r = 0; r < R; ++r) nsel[r] = 64 * r + lane < B ? n_selected(len[r], w1, w2) : 0;
+  int rem = j, first, before;
+#pragma unroll
   for (int r = 0; r < R; ++r)
-    ns[r] = 64 * r + lane < B ? chunks_of(len[r], w1, w2, chunk, max_splits) : 0;
-  int rem = j;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    int x = ns[r];  // inclusive scan over the wave
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(x, d, 64);
-      if (lane >= d) x += y;
-    }
-    const int tot = __shfl(x, 63, 64);
-    if (rem < tot) {  // uniform over the wave
-      const uint64_t hit = __ballot(x > rem);
-      const int first = __builtin_ctzll(hit);
+    if (wave_find(full_chunks(nsel[r], chunk, max_splits), rem, lane, first, before)) {
       b = 64 * r + first;
-      split = rem - __shfl(x - ns[r], first, 64);
+      split = rem - before;
       L = __shfl(len[r], first, 64);
       return true;
     }
-    rem -= tot;
-  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (wave_find(part_chunk(nsel[r], chunk, max_splits), rem, lane, first, before)) {
+      b = 64 * r + first;
+      split = full_chunks(__shfl(nsel[r], first, 64), chunk, max_splits);
+      L = __shfl(len[r], first, 64);
+      return true;
+    }
   return false;
 }
 
-// More sequences: decode_plan_kernel lists the chunks once (one workgroup
-// scanning the sequences 256 at a time) and workgroup j reads entry j.
+// More sequences: decode_plan_kernel lists the chunks in the same order once
+// (one workgroup scanning the sequences 256 at a time, whole chunks in a
+// first pass, last ones in a second) and workgroup j reads entry j.
 __global__ __launch_bounds__(256) void decode_plan_kernel(const int32_t* __restrict__ seqlens,
                                                           int B, int w1, int w2, int chunk,
                                                           int max_splits,
@@ -157,23 +180,26 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(const int32_t* __restr
   __shared__ int wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int base = 0;
-  for (int b0 = 0; b0 < B; b0 += 256) {
-    const int b = b0 + tid;
-    const int ns = b < B ? chunks_of(seqlens[b], w1, w2, chunk, max_splits) : 0;
-    int x = ns;  // inclusive scan over the wave
+  for (int pass = 0; pass < 2; ++pass)
+    for (int b0 = 0; b0 < B; b0 += 256) {
+      const int b = b0 + tid;
+      const int nsel = b < B ? n_selected(seqlens[b], w1, w2) : 0;
+      const int nf = full_chunks(nsel, chunk, max_splits);
+      const int ns = pass == 0 ? nf : part_chunk(nsel, chunk, max_splits);
+      int x = ns;  // inclusive scan over the wave
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(x, d, 64);
-      if (lane >= d) x += y;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+      }
+      if (lane == 63) wsum[wave] = x;
+      __syncthreads();
+      int off = base + x - ns;
+      for (int w = 0; w < wave; ++w) off += wsum[w];
+      for (int t = 0; t < ns; ++t) items[off + t] = b * max_splits + (pass == 0 ? t : nf);
+      base += (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+      __syncthreads();  // wsum is rewritten by the next round
     }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    int off = base + x - ns;
-    for (int w = 0; w < wave; ++w) off += wsum[w];
-    for (int t = 0; t < ns; ++t) items[off + t] = b * max_splits + t;
-    base += (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-    __syncthreads();  // wsum is rewritten by the next round
-  }
   if (tid == 0) *count = base;
 }
 
