@@ -19,6 +19,8 @@
 // the decode path receives the per-head sink; flash-attention PR #1819 review
 // thread: decoding with a sink through the KV-cache entry point was reported
 // wrong, so the merge is where the sink must enter, once).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -541,18 +543,34 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
     items = nullptr;
     count = nullptr;
   }
-  constexpr int NW = 4;
-  const dim3 grid(((units + NW - 1) / NW) * a.B * a.max_splits);
-  if (a.D == 64) {
-    decode_partial_kernel<64, NW><<<grid, 64 * NW, 0, stream>>>(
+  // 4 waves per workgroup (4 KV heads of one chunk sharing a slot table),
+  // unless that leaves CUs without a workgroup: then 2, which doubles the
+  // workgroups (the single-sequence window decode: 24 -> 19 us).
+  const long long slots = (long long)a.B * a.max_splits;
+  const bool narrow = ((units + 3) / 4) * slots < 256;
+  auto partial = [&](auto d, auto nw) {
+    constexpr int D = decltype(d)::value, NW = decltype(nw)::value;
+    const dim3 grid((unsigned)(((units + NW - 1) / NW) * slots));
+    decode_partial_kernel<D, NW><<<grid, 64 * NW, 0, stream>>>(
         q, kc, vc, a.block_table, a.seqlens, a.partials, items, count, a.B, a.Hq, a.Hkv, hgroups,
         page_shift, a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits);
+  };
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
+  using W2 = std::integral_constant<int, 2>;
+  using W4 = std::integral_constant<int, 4>;
+  if (a.D == 64) {
+    if (narrow)
+      partial(I64{}, W2{});
+    else
+      partial(I64{}, W4{});
     decode_combine_kernel<64><<<cgrid, kThreads, 0, stream>>>(
         a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits);
   } else {
-    decode_partial_kernel<128, NW><<<grid, 64 * NW, 0, stream>>>(
-        q, kc, vc, a.block_table, a.seqlens, a.partials, items, count, a.B, a.Hq, a.Hkv, hgroups,
-        page_shift, a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits);
+    if (narrow)
+      partial(I128{}, W2{});
+    else
+      partial(I128{}, W4{});
     decode_combine_kernel<128><<<cgrid, kThreads, 0, stream>>>(
         a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits);
   }
