@@ -1,24 +1,25 @@
 // Paged decode with a learnable per-head sink and optional first/last window.
 //
 // Split-K: each sequence's selected tokens are cut into chunks of `chunk`
-// tokens; one workgroup handles one (chunk, KV head, sequence) and computes the
-// scores of all query heads of that KV head (GQA group, up to 16 per
-// workgroup), so every K/V byte is read from HBM once.  Inside a workgroup the
-// 4 waves take interleaved steps of 32 tokens:
+// tokens.  A workgroup takes one chunk and NW (4, or 2 for small grids) KV
+// heads of it; wave w computes the scores of all query heads of its KV head
+// (GQA group, up to 16 per wave), so every K/V byte is read from HBM once:
 //   * the slots of the chunk's tokens are computed once into LDS from the
 //     block table and the window rule (sglang PR #12504 "To implement
 //     attention-sink": first W1 tokens followed by the last W2 tokens of each
-//     sequence, or the whole prefix when it is not longer than W1 + W2);
-//   * S^T (16 tokens x 16 heads) = K Q^T on 16x16x32 bf16 MFMA, K rows loaded
-//     straight from the paged cache;
-//   * a running max / sum per head WITHOUT the sink;
-//   * V is transposed through a wave-private LDS tile and O^T += V^T P^T.
-// The 4 waves merge through LDS and write one partial (acc[D], m, l) per
-// (sequence, head, chunk).  The combine kernel merges the chunks and folds the
-// sink into the denominator exactly once (sglang PR #8825, Summary of Changes:
-// the decode path receives the per-head sink; flash-attention PR #1819 review
-// thread: decoding with a sink through the KV-cache entry point was reported
-// wrong, so the merge is where the sink must enter, once).
+//     sequence, or the whole prefix when it is not longer than W1 + W2) and
+//     shared by the workgroup's waves;
+//   * each wave walks the chunk in steps of 32 tokens: S^T (16 tokens x 16
+//     heads) = K Q^T on 16x16x32 bf16 MFMA with K rows loaded straight from
+//     the paged cache, a running max / sum per head WITHOUT the sink, and
+//     O^T += V^T P^T with V staged in a wave-private LDS tile and read back
+//     transposed;
+//   * each wave writes one partial (acc[D], m, l) per (sequence, head, chunk).
+// The combine kernel merges the chunks and folds the sink into the
+// denominator exactly once (sglang PR #8825, Summary of Changes: the decode
+// path receives the per-head sink; flash-attention PR #1819 review thread:
+// decoding with a sink through the KV-cache entry point was reported wrong,
+// so the merge is where the sink must enter, once).
 #include <type_traits>
 
 #include "common.h"

@@ -15,6 +15,11 @@
 // sglang PR #8825, Summary of Changes: an additional value per head in the
 // softmax denominator).
 //
+// The same per-wave tile steps (WaveRows) also drive extend_kernel (packed
+// variable-length queries against a paged cache or packed K/V, with K/V rows
+// gathered per tile) and index_kernel (each block of query rows against the
+// tokens of one index list).
+//
 // fp32 path: a plain VALU kernel, one thread per query row, K/V tiles in LDS.
 #include <climits>
 
