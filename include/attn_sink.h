@@ -163,6 +163,35 @@ int attn_sink_fwd_index_paged(const void* q, const void* k_cache, const void* v_
                               int topk, float softmax_scale, int dtype, void* hip_stream);
 
 /*
+ * Attention over per-query KV index lists (an indexer's top-k selection per
+ * query token: the SGLang DSA write-up, sections layer0 and Other Layers).
+ * Packed query rows as in attn_sink_fwd_extend_paged (row i of sequence b at
+ * position L_b - nq_b + i of its L_b = seqlens_k[b] cached tokens); packed row
+ * r attends to the tokens of kv_index row r that lie in [0, L_b) and at or
+ * before its position, plus the sink.
+ *   kv_index   [total_q, topk] int32 device: token positions; entries < 0 or
+ *              >= L_b are empty; a list names each token at most once
+ *   o          [total_q, Hq, D] bf16; lse [Hq, total_q] fp32 or NULL -- outputs
+ *   workspace  at least attn_sink_index_rows_workspace_bytes() bytes
+ * Each row reads its own listed K/V rows (the decode path's cost per row, not
+ * the shared-tile cost of attn_sink_fwd_index_paged).  A row whose list holds
+ * no visible token gets O = 0 and LSE = sink (or -inf).  Requirements: bf16;
+ * D in {64, 128}; Hq % Hkv == 0; topk >= 1; page_size a power of two in
+ * [1, 256].  The device arrays are not checked: they must hold the stated
+ * ranges.
+ */
+int attn_sink_fwd_index_rows_paged(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                   const int32_t* seqlens_k, const int32_t* kv_index,
+                                   const float* sink, void* o, float* lse, int B, int total_q,
+                                   int Hq, int Hkv, int D, int page_size, int max_pages_per_seq,
+                                   int num_pages, int topk, float softmax_scale, void* workspace,
+                                   size_t workspace_bytes, int dtype, void* hip_stream);
+
+/* Workspace needed by attn_sink_fwd_index_rows_paged (0 on invalid arguments). */
+size_t attn_sink_index_rows_workspace_bytes(int total_q, int Hq, int Hkv, int D, int topk);
+
+/*
  * Variable-length (packed) forward.  Sequence b's queries are rows
  * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and its keys rows
  * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v; it is the prefill problem

@@ -32,6 +32,8 @@ _SIGNATURES = {
     "attn_sink_fwd_extend_paged": ([_vp] * 9 + [_i] * 9 + [_f, _i, _i, _i, _vp], _i),
     "attn_sink_fwd_varlen": ([_vp] * 8 + [_i] * 7 + [_f, _i, _i, _i, _i, _vp], _i),
     "attn_sink_fwd_index_paged": ([_vp] * 11 + [_i] * 11 + [_f, _i, _vp], _i),
+    "attn_sink_fwd_index_rows_paged": ([_vp] * 10 + [_i] * 9 + [_f, _vp, _sz, _i, _vp], _i),
+    "attn_sink_index_rows_workspace_bytes": ([_i] * 5, _sz),
     "attn_sink_decode_workspace_bytes": ([_i] * 9, _sz),
     "attn_sink_bwd": ([_vp] * 11 + [_i] * 6 + [_f, _i, _i, _i, _vp, _sz, _i, _vp], _i),
     "attn_sink_bwd_workspace_bytes": ([_i] * 6, _sz),
@@ -266,6 +268,54 @@ def attn_sink_fwd_index_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, se
         _ptr(seqlens_k), _ptr(kv_index), _ptr(cu_blocks), _ptr(sink), _ptr(out), _ptr(lse), B,
         total_q, int(max_seqlen_q), Hq, Hkv, D, page_size, block_table.shape[1], num_pages,
         int(block_q), kv_index.shape[1], scale, BF16, _stream(dev)))
+    return out, lse
+
+
+def attn_sink_index_rows_workspace_bytes(total_q, Hq, Hkv, D, topk):
+    return lib().attn_sink_index_rows_workspace_bytes(total_q, Hq, Hkv, D, topk)
+
+
+def attn_sink_fwd_index_rows_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
+                                   kv_index, sink=None, softmax_scale=None, out=None, lse=None,
+                                   workspace=None, return_lse=True):
+    """O [total_q,Hq,D], LSE [Hq,total_q] for packed new queries against a paged KV cache,
+    packed row r attending to the tokens of kv_index [total_q, topk] row r at or before its
+    position."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    for name, t in (("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q),
+                    ("seqlens_k", seqlens_k), ("kv_index", kv_index)):
+        _need(t, name, torch.int32, dev)
+    total_q, Hq, D = q.shape
+    num_pages, page_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (num_pages, page_size, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [num_pages, page_size, Hkv, D]")
+    B = seqlens_k.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != B or cu_seqlens_q.shape != (B + 1,) \
+            or kv_index.dim() != 2 or kv_index.shape[0] != total_q:
+        raise ValueError("block_table must be [B, max_pages], cu_seqlens_q [B+1], seqlens_k [B], "
+                         "kv_index [total_q, topk]")
+    if sink is not None:
+        _need(sink, "sink", torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    topk = kv_index.shape[1]
+    if workspace is None:
+        need = lib().attn_sink_index_rows_workspace_bytes(total_q, Hq, Hkv, D, topk)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib().attn_sink_fwd_index_rows_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cu_seqlens_q),
+        _ptr(seqlens_k), _ptr(kv_index), _ptr(sink), _ptr(out), _ptr(lse), B, total_q, Hq, Hkv,
+        D, page_size, block_table.shape[1], num_pages, topk, scale, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), BF16, _stream(dev)))
     return out, lse
 
 

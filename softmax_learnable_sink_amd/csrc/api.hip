@@ -208,6 +208,59 @@ int attn_sink_fwd_index_paged(const void* q, const void* k_cache, const void* v_
                     "attn_sink_fwd_index_paged launch");
 }
 
+size_t attn_sink_index_rows_workspace_bytes(int total_q, int Hq, int Hkv, int D, int topk) {
+  if (total_q < 0 || topk < 1 || check_heads(Hq, Hkv, D) != ATTN_SINK_OK) return 0;
+  return plan_index_rows(total_q, Hq, Hkv, D, topk).workspace_bytes;
+}
+
+int attn_sink_fwd_index_rows_paged(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                   const int32_t* seqlens_k, const int32_t* kv_index,
+                                   const float* sink, void* o, float* lse, int B, int total_q,
+                                   int Hq, int Hkv, int D, int page_size, int max_pages_per_seq,
+                                   int num_pages, int topk, float softmax_scale, void* workspace,
+                                   size_t workspace_bytes, int dtype, void* hip_stream) {
+  REQUIRE(dtype == ATTN_SINK_BF16, ATTN_SINK_ERR_UNSUPPORTED,
+          "index-list attention supports bf16 only (dtype %d)", dtype);
+  REQUIRE(B >= 1 && total_q >= 0, ATTN_SINK_ERR_INVALID_ARG,
+          "need B >= 1, total_q >= 0 (got %d, %d)", B, total_q);
+  if (int r = check_heads(Hq, Hkv, D)) return r;
+  REQUIRE(topk >= 1, ATTN_SINK_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", topk);
+  if (int r = check_scale(softmax_scale)) return r;
+  REQUIRE(pow2(page_size) && page_size <= 256, ATTN_SINK_ERR_UNSUPPORTED,
+          "page_size must be a power of two in [1, 256] (got %d)", page_size);
+  REQUIRE(max_pages_per_seq >= 1 && num_pages >= 1, ATTN_SINK_ERR_INVALID_ARG,
+          "max_pages_per_seq and num_pages must be >= 1");
+  REQUIRE(fits_int32((long long)num_pages * page_size) &&
+              fits_int32((long long)max_pages_per_seq * page_size),
+          ATTN_SINK_ERR_UNSUPPORTED, "num_pages or max_pages_per_seq times page_size exceeds 2^31 - 1");
+  REQUIRE(fits_int32((long long)total_q * Hq), ATTN_SINK_ERR_UNSUPPORTED,
+          "too many rows for 32-bit row indices");
+  REQUIRE(q && k_cache && v_cache && block_table && cu_seqlens_q && seqlens_k && kv_index && o,
+          ATTN_SINK_ERR_INVALID_ARG,
+          "q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, kv_index and o must not be "
+          "NULL");
+  REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(o),
+          ATTN_SINK_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
+  REQUIRE(aligned4(block_table) && aligned4(cu_seqlens_q) && aligned4(seqlens_k) &&
+              aligned4(kv_index) && aligned4(sink) && aligned4(lse),
+          ATTN_SINK_ERR_INVALID_ARG, "int32 and fp32 arrays must be 4-byte aligned");
+  if (total_q == 0) return ATTN_SINK_OK;  // nothing to compute
+  const DecodePlan plan = plan_index_rows(total_q, Hq, Hkv, D, topk);
+  REQUIRE(fits_int32((long long)total_q * plan.max_splits * ((Hkv * ((Hq / Hkv + 15) / 16) + 1) / 2)),
+          ATTN_SINK_ERR_UNSUPPORTED, "rows * splits * KV-head units exceeds 2^31 - 1 workgroups");
+  REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
+          "a 16-byte aligned workspace of %zu bytes is required", plan.workspace_bytes);
+  REQUIRE(workspace_bytes >= plan.workspace_bytes, ATTN_SINK_ERR_WORKSPACE,
+          "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+          plan.workspace_bytes);
+  IndexRowsArgs a{q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, kv_index, sink, o,
+                  lse, B, total_q, Hq, Hkv, D, page_size, max_pages_per_seq, topk,
+                  softmax_scale, workspace};
+  return hip_status(launch_index_rows_bf16(a, static_cast<hipStream_t>(hip_stream)),
+                    "attn_sink_fwd_index_rows_paged launch");
+}
+
 int attn_sink_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                          const int32_t* cu_seqlens_k, const float* sink, void* o, float* lse,
                          int B, int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv,

@@ -39,6 +39,7 @@ template <int D, int NW>
 struct DecLds {
   int slot[kSub];               // slot of each selected token of the current block
   __bf16 v[NW][32 * vrow<D>()]; // per-wave V staging tiles, natural [token][d]
+  int wsum[NW];                 // per-wave counts (compaction of listed tokens)
 };
 
 template <int D>
@@ -213,21 +214,44 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(const int32_t* __restr
 // every token of the workgroup's chunk, so the NW waves of a workgroup read
 // adjacent heads' slices of the same token rows together and share one slot
 // table.  Each wave writes its own partials.
-template <int D, int NW>
+//
+// LIST: per-query index lists instead of whole sequences.  "Sequence" b is then
+// packed query row b (B rows) of sequence row_seq[b]; its tokens are the
+// entries of kv_index row b (topk of them) that lie in [0, L) and at or before
+// the row's position L - nq + i; each chunk covers `chunk` list entries, every
+// slot of the grid is real, and a chunk's valid entries are compacted into the
+// slot table.
+struct ListArgs {
+  const int32_t* kv_index;  // [B, topk]
+  const int32_t* row_seq;   // [B]: sequence of each packed row
+  const int32_t* cu_q;      // [sequences + 1]
+  int topk;
+};
+
+template <int D, int NW, bool LIST>
 __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seqlens, float* __restrict__ part,
     const int32_t* __restrict__ items, const int32_t* __restrict__ count, int B, int Hq, int Hkv,
     int hgroups, int page_shift, int max_pages, float sl2, int w1, int w2, int chunk,
-    int max_splits) {
+    int max_splits, ListArgs la) {
   __shared__ DecLds<D, NW> s;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int kg = lane >> 4, hl = lane & 15;
   const int nxu = (Hkv * hgroups + NW - 1) / NW;
   const int j = blockIdx.x / nxu;
-  int b, split, L;
-  if (items) {
+  int b, split, L, seq = 0, pos = 0;
+  if constexpr (LIST) {
+    split = j % max_splits;
+    b = j / max_splits;
+    seq = la.row_seq[b];
+    L = seqlens[seq];
+    const int qs = la.cu_q[seq];
+    pos = L - (la.cu_q[seq + 1] - qs) + (b - qs);
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    pos = __builtin_amdgcn_readfirstlane(pos);
+  } else if (items) {
     if (j >= *count) return;  // uniform over the workgroup
     const int item = items[j];
     split = item % max_splits;
@@ -245,11 +269,11 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
   const int g = Hq / Hkv;
   const int g_eff = min(16, g - 16 * hgi);
   const int h0 = kvh * g + 16 * hgi;
-  const int nsel = n_selected(L, w1, w2);
+  const int nsel = LIST ? la.topk : n_selected(L, w1, w2);
   const int u0 = split * chunk;
   if (u0 >= nsel) return;  // uniform over the workgroup
   const int u1 = min(nsel, u0 + chunk);
-  const int32_t* bt_row = bt + (size_t)b * max_pages;
+  const int32_t* bt_row = bt + (size_t)(LIST ? seq : b) * max_pages;
   const size_t rs = (size_t)Hkv * D;
   const __bf16* kbase = kc + (size_t)kvh * D;
   const __bf16* vbase = vc + (size_t)kvh * D;
@@ -323,26 +347,69 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
   };
 
   for (int sub0 = u0; sub0 < u1; sub0 += kSub) {
-    const int nsub = min(kSub, u1 - sub0);
-    const int nsteps = (nsub + 31) >> 5;
-    // slot table of this block, padded with -1 up to an even number of steps;
-    // every block-table load of a thread is issued before its first LDS write,
-    // so the table costs one memory latency (overlapping the Q loads)
-    const int npad = min(kSub, 64 * ((nsteps + 1) >> 1));
     constexpr int kPer = kSub / (64 * NW);
-    int sv[kPer];
+    int nsub, nsteps, npad;
+    if constexpr (LIST) {
+      // thread t takes list entries t*kPer .. +kPer-1 of the block; the valid
+      // ones are compacted in entry order (a workgroup-wide exclusive scan of
+      // the per-thread counts), the rest of the table up to npad holds -1
+      const int ne = min(kSub, u1 - sub0);
+      const int32_t* lrow = la.kv_index + (size_t)b * la.topk + sub0;
+      int tv[kPer], sv[kPer], cnt = 0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)  // index clamped to a selected token
-      sv[i] = slot_of(bt_row, token_of(sub0 + min(tid + i * 64 * NW, nsub - 1), L, w1, w2),
-                      page_shift);
-    // keep the loads unconditional and issued together (otherwise the compiler
-    // sinks each one into the branch that uses it and waits for it there)
+      for (int i = 0; i < kPer; ++i) {
+        const int x = tid * kPer + i;
+        const int t = lrow[min(x, ne - 1)];
+        const bool ok = (x < ne) & (t >= 0) & (t < L) & (t <= pos);
+        tv[i] = ok ? t : -1;
+        cnt += ok ? 1 : 0;
+      }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(sv[i]));
+      for (int i = 0; i < kPer; ++i) sv[i] = slot_of(bt_row, max(tv[i], 0), page_shift);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int x = tid + i * 64 * NW;
-      if (x < npad) s.slot[x] = x < nsub ? sv[i] : -1;
+      for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(sv[i]));
+      int x = cnt;  // inclusive scan over the wave
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+      }
+      if (lane == 63) s.wsum[wave] = x;
+      __syncthreads();
+      int off = x - cnt, total = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        off += w < wave ? s.wsum[w] : 0;
+        total += s.wsum[w];
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (tv[i] >= 0) s.slot[off++] = sv[i];
+      nsub = total;
+      nsteps = (nsub + 31) >> 5;
+      npad = min(kSub, 64 * max(1, (nsteps + 1) >> 1));
+      for (int y = nsub + tid; y < npad; y += 64 * NW) s.slot[y] = -1;
+    } else {
+      nsub = min(kSub, u1 - sub0);
+      nsteps = (nsub + 31) >> 5;
+      // slot table of this block, padded with -1 up to an even number of steps;
+      // every block-table load of a thread is issued before its first LDS write,
+      // so the table costs one memory latency (overlapping the Q loads)
+      npad = min(kSub, 64 * ((nsteps + 1) >> 1));
+      int sv[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)  // index clamped to a selected token
+        sv[i] = slot_of(bt_row, token_of(sub0 + min(tid + i * 64 * NW, nsub - 1), L, w1, w2),
+                        page_shift);
+      // keep the loads unconditional and issued together (otherwise the compiler
+      // sinks each one into the branch that uses it and waits for it there)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(sv[i]));
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int x = tid + i * 64 * NW;
+        if (x < npad) s.slot[x] = x < nsub ? sv[i] : -1;
+      }
     }
     __syncthreads();
     // start the step loop with no VMEM load pending, so that the compiler's
@@ -387,7 +454,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
 // One wave per (sequence, query head): merge the chunk partials and fold the
 // sink in once: M = max(sink', m_k), Z = 2^(sink'-M) + sum 2^(m_k-M) l_k,
 // O = sum 2^(m_k-M) acc_k / Z, LSE = (M + log2 Z) ln 2.
-template <int D>
+template <int D, bool LIST>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ seqlens,
     const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq,
@@ -396,8 +463,11 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
   const int bh = blockIdx.x * 4 + wave;
   if (bh >= B * Hq) return;
   const int b = bh / Hq, h = bh % Hq;
-  const int nsel = n_selected(seqlens[b], w1, w2);
-  const int nsp = nsel > 0 ? min(max_splits, (nsel + chunk - 1) / chunk) : 0;
+  int nsp = max_splits;  // LIST: every chunk of every row holds a partial
+  if constexpr (!LIST) {
+    const int nsel = n_selected(seqlens[b], w1, w2);
+    nsp = nsel > 0 ? min(max_splits, (nsel + chunk - 1) / chunk) : 0;
+  }
   const float* base = part + (size_t)bh * max_splits * (D + 2);
   const float sig2 = sink ? sink[h] * kLog2e : kNegInf;
 
@@ -442,7 +512,9 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
   const float inv = z > 0.f ? 1.f / z : 0.f;
 #pragma unroll
   for (int i = 0; i < DPL; ++i) o[(size_t)bh * D + lane + 64 * i] = (__bf16)(od[i] * inv);
-  if (lse && lane == 0) lse[bh] = z > 0.f ? (Mu + log2_fast(z)) * kLn2 : kNegInf;
+  // LSE [B, Hq], or [Hq, B] for packed rows (LIST)
+  if (lse && lane == 0)
+    lse[LIST ? (size_t)h * B + b : (size_t)bh] = z > 0.f ? (Mu + log2_fast(z)) * kLn2 : kNegInf;
 }
 
 __global__ void select_slots_kernel(const int32_t* __restrict__ bt,
@@ -552,9 +624,9 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   auto partial = [&](auto d, auto nw) {
     constexpr int D = decltype(d)::value, NW = decltype(nw)::value;
     const dim3 grid((unsigned)(((units + NW - 1) / NW) * slots));
-    decode_partial_kernel<D, NW><<<grid, 64 * NW, 0, stream>>>(
+    decode_partial_kernel<D, NW, false><<<grid, 64 * NW, 0, stream>>>(
         q, kc, vc, a.block_table, a.seqlens, a.partials, items, count, a.B, a.Hq, a.Hkv, hgroups,
-        page_shift, a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits);
+        page_shift, a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits, ListArgs{});
   };
   using I64 = std::integral_constant<int, 64>;
   using I128 = std::integral_constant<int, 128>;
@@ -565,15 +637,92 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
       partial(I64{}, W2{});
     else
       partial(I64{}, W4{});
-    decode_combine_kernel<64><<<cgrid, kThreads, 0, stream>>>(
+    decode_combine_kernel<64, false><<<cgrid, kThreads, 0, stream>>>(
         a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits);
   } else {
     if (narrow)
       partial(I128{}, W2{});
     else
       partial(I128{}, W4{});
-    decode_combine_kernel<128><<<cgrid, kThreads, 0, stream>>>(
+    decode_combine_kernel<128, false><<<cgrid, kThreads, 0, stream>>>(
         a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits);
+  }
+  return hipGetLastError();
+}
+
+// Packed row -> its sequence, for the per-query list mode.
+__global__ __launch_bounds__(256) void row_seq_kernel(const int32_t* __restrict__ cu_q,
+                                                      int32_t* __restrict__ row_seq) {
+  const int b = blockIdx.x;
+  for (int r = cu_q[b] + threadIdx.x; r < cu_q[b + 1]; r += 256) row_seq[r] = b;
+}
+
+DecodePlan plan_index_rows(int total_q, int Hq, int Hkv, int D, int topk) {
+  // the decode plan with the list length as every row's selection and the
+  // rows as its sequences
+  (void)D;
+  DecodePlan p{0, 0, 0};
+  const int g = Hq / Hkv;
+  const long long units = (long long)total_q * Hkv * ((g + 15) / 16);
+  long long chunk = 2048;
+  if (units * ((topk + chunk - 1) / chunk) < 1024) {
+    chunk = 1024;
+    while (chunk > 128 && units * ((topk + chunk - 1) / chunk) < 2048) chunk /= 2;
+  }
+  p.chunk = (int)chunk;
+  p.max_splits = (int)((topk + chunk - 1) / chunk);
+  if (p.max_splits < 1) p.max_splits = 1;
+  p.workspace_bytes = (size_t)total_q * Hq * p.max_splits * (D + 2) * sizeof(float) +
+                      (size_t)total_q * sizeof(int32_t);
+  return p;
+}
+
+hipError_t launch_index_rows_bf16(const IndexRowsArgs& a, hipStream_t stream) {
+  const DecodePlan plan = plan_index_rows(a.total_q, a.Hq, a.Hkv, a.D, a.topk);
+  const int g = a.Hq / a.Hkv;
+  const int hgroups = (g + 15) / 16;
+  const int units = a.Hkv * hgroups;
+  const int page_shift = log2_exact(a.page_size);
+  const float sl2 = a.scale * kLog2e;
+  const auto* q = static_cast<const __bf16*>(a.q);
+  const auto* kc = static_cast<const __bf16*>(a.k_cache);
+  const auto* vc = static_cast<const __bf16*>(a.v_cache);
+  auto* o = static_cast<__bf16*>(a.o);
+  float* part = static_cast<float*>(a.workspace);
+  int32_t* row_seq = reinterpret_cast<int32_t*>(part + (size_t)a.total_q * a.Hq *
+                                                            plan.max_splits * (a.D + 2));
+  row_seq_kernel<<<a.B, 256, 0, stream>>>(a.cu_seqlens_q, row_seq);
+  const ListArgs la{a.kv_index, row_seq, a.cu_seqlens_q, a.topk};
+  const long long slots = (long long)a.total_q * plan.max_splits;
+  const bool narrow = ((units + 3) / 4) * slots < 256;
+  auto partial = [&](auto d, auto nw) {
+    constexpr int D = decltype(d)::value, NW = decltype(nw)::value;
+    const dim3 grid((unsigned)(((units + NW - 1) / NW) * slots));
+    decode_partial_kernel<D, NW, true><<<grid, 64 * NW, 0, stream>>>(
+        q, kc, vc, a.block_table, a.seqlens_k, part, nullptr, nullptr, a.total_q, a.Hq, a.Hkv,
+        hgroups, page_shift, a.max_pages, sl2, -1, -1, plan.chunk, plan.max_splits, la);
+  };
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
+  using W2 = std::integral_constant<int, 2>;
+  using W4 = std::integral_constant<int, 4>;
+  const dim3 cgrid((a.total_q * a.Hq + 3) / 4);
+  if (a.D == 64) {
+    if (narrow)
+      partial(I64{}, W2{});
+    else
+      partial(I64{}, W4{});
+    decode_combine_kernel<64, true><<<cgrid, kThreads, 0, stream>>>(
+        part, a.seqlens_k, a.sink, o, a.lse, a.total_q, a.Hq, -1, -1, plan.chunk,
+        plan.max_splits);
+  } else {
+    if (narrow)
+      partial(I128{}, W2{});
+    else
+      partial(I128{}, W4{});
+    decode_combine_kernel<128, true><<<cgrid, kThreads, 0, stream>>>(
+        part, a.seqlens_k, a.sink, o, a.lse, a.total_q, a.Hq, -1, -1, plan.chunk,
+        plan.max_splits);
   }
   return hipGetLastError();
 }

@@ -96,6 +96,27 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pag
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// Per-query index lists: packed query rows against a paged cache, row r
+// attending to the tokens of kv_index row r (topk entries) at or before its
+// position.  Runs the paged-decode kernels with the rows as their sequences.
+struct IndexRowsArgs {
+  const void* q;  // [total_q, Hq, D]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seqlens_k;
+  const int32_t* kv_index;  // [total_q, topk]
+  const float* sink;
+  void* o;
+  float* lse;  // [Hq, total_q] or NULL
+  int B, total_q, Hq, Hkv, D, page_size, max_pages, topk;
+  float scale;
+  void* workspace;
+};
+DecodePlan plan_index_rows(int total_q, int Hq, int Hkv, int D, int topk);
+hipError_t launch_index_rows_bf16(const IndexRowsArgs& a, hipStream_t stream);
+
 hipError_t launch_select_slots(const int32_t* bt, const int32_t* seqlens, int B, int max_pages,
                                int page_size, int w1, int w2, int64_t* slots, int32_t* counts,
                                int max_sel, hipStream_t stream);

@@ -36,6 +36,7 @@ def test_header_declares_expected_entry_points():
     for n in ("attn_sink_fwd_prefill", "attn_sink_fwd_decode_paged", "attn_sink_bwd",
               "attn_sink_fwd_extend_paged", "attn_sink_fwd_varlen", "attn_sink_bwd_varlen",
               "attn_sink_bwd_varlen_workspace_bytes", "attn_sink_fwd_index_paged",
+              "attn_sink_fwd_index_rows_paged", "attn_sink_index_rows_workspace_bytes",
               "attn_sink_decode_workspace_bytes", "attn_sink_bwd_workspace_bytes",
               "attn_sink_decode_select_slots", "attn_sink_gather_kv", "attn_sink_last_error",
               "attn_sink_abi_version"):
@@ -230,6 +231,40 @@ def test_index_rejects(lib, kw, status, msg):
 
 def test_index_with_no_rows_is_a_no_op(lib):
     assert _index(lib, tq=0, mq=0) == binding.OK
+
+
+def _index_rows(lib, **kw):
+    a = dict(B=2, tq=10, Hq=8, Hkv=2, D=64, P=16, maxp=4, npages=8, topk=256, scale=0.125,
+             dtype=binding.BF16, q=P, idx=P, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.attn_sink_fwd_index_rows_paged(a["q"], P, P, P, P, P, a["idx"], None, P, None,
+                                              a["B"], a["tq"], a["Hq"], a["Hkv"], a["D"],
+                                              a["P"], a["maxp"], a["npages"], a["topk"],
+                                              a["scale"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dtype=binding.F32), binding.ERR_UNSUPPORTED, "bf16"),
+    (dict(B=0), binding.ERR_INVALID_ARG, "B >= 1"),
+    (dict(topk=0), binding.ERR_INVALID_ARG, "topk"),
+    (dict(Hq=9), binding.ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(P=12), binding.ERR_UNSUPPORTED, "power of two"),
+    (dict(idx=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(q=P_ODD), binding.ERR_INVALID_ARG, "aligned"),
+    (dict(ws=None), binding.ERR_WORKSPACE, "workspace"),
+    (dict(wsb=4), binding.ERR_WORKSPACE, "too small"),
+])
+def test_index_rows_rejects(lib, kw, status, msg):
+    assert _index_rows(lib, **kw) == status
+    assert msg in binding.last_error()
+
+
+def test_index_rows_workspace_query(lib):
+    # partials [rows, Hq, splits, D + 2] fp32 and the row -> sequence map
+    n = binding.attn_sink_index_rows_workspace_bytes(64, 64, 8, 64, 2048)
+    assert n == 64 * 64 * 1 * 66 * 4 + 64 * 4 or n > 64 * 64 * 66 * 4
+    assert binding.attn_sink_index_rows_workspace_bytes(64, 64, 7, 64, 2048) == 0
+    assert _index_rows(lib, tq=0) == binding.OK
 
 
 def _fwd_varlen(lib, **kw):
