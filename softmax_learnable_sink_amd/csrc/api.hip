@@ -355,7 +355,7 @@ int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v
           plan.workspace_bytes);
   DecodeArgs a{q, k_cache, v_cache, block_table, seqlens_k, sink, o, lse, B, Hq, Hkv, D,
                page_size, max_pages_per_seq, num_pages, softmax_scale, window_first, window_last,
-               plan.chunk, plan.max_splits, static_cast<float*>(workspace)};
+               plan.chunk, plan.max_splits, static_cast<float*>(workspace), plan.even};
   return hip_status(launch_decode_bf16(a, static_cast<hipStream_t>(hip_stream)),
                     "attn_sink_fwd_decode_paged launch");
 }

@@ -20,6 +20,9 @@
 // path receives the per-head sink; flash-attention PR #1819 review thread:
 // decoding with a sink through the KV-cache entry point was reported wrong,
 // so the merge is where the sink must enter, once).
+#include <algorithm>
+#include <atomic>
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -228,56 +231,70 @@ struct ListArgs {
   int topk;
 };
 
-template <int D, int NW, bool LIST>
+// Work assignment of decode_partial_kernel.
+enum : int {
+  kModeChunks = 0,  // workgroup j: the j-th chunk that holds tokens
+  kModeList = 1,    // per-query index lists (see ListArgs)
+  kModeEven = 2,    // equal token ranges (see EvenArgs)
+};
+
+// kModeEven: the selected tokens of all sequences, concatenated in sequence
+// order (T of them), are cut into G equal ranges per column of KV-head units;
+// workgroup i of a column takes tokens [i*T/G, (i+1)*T/G) and writes one
+// partial per sequence its range touches, at piece index i + b of the head's
+// row of `pstride` = G + B partials (unique: for a sequence the pieces are
+// consecutive workgroups, and a workgroup's pieces consecutive sequences).
+// With every range equally long and the grid one round of resident
+// workgroups, no short tail of lone workgroups ends the launch.  G shrinks
+// to min(G, ceil(T / kEvenMinTokens)) on the device so that every range
+// holds tokens.  Workgroup 0 also writes the sequences' first concatenated
+// token (starts[b], starts[B] = T) for the combine.
+constexpr int kEvenMinTokens = 64;
+constexpr int kEvenMaxG = 1024;  // workgroups per column the workspace has room for
+struct EvenArgs {
+  int G;
+  int pstride;
+  int32_t* starts;  // [B + 1]
+};
+__host__ __device__ __forceinline__ int even_groups(int G, int T) {
+  return max(1, min(G, (T + kEvenMinTokens - 1) / kEvenMinTokens));
+}
+// Workgroup (of Ge) whose range holds concatenated token t < T.
+__host__ __device__ __forceinline__ int even_owner(long long t, int Ge, int T) {
+  return (int)(((t + 1) * Ge + T - 1) / T) - 1;
+}
+
+template <int D, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seqlens, float* __restrict__ part,
     const int32_t* __restrict__ items, const int32_t* __restrict__ count, int B, int Hq, int Hkv,
     int hgroups, int page_shift, int max_pages, float sl2, int w1, int w2, int chunk,
-    int max_splits, ListArgs la) {
+    int max_splits, ListArgs la, EvenArgs ev) {
+  constexpr bool LIST = MODE == kModeList;
   __shared__ DecLds<D, NW> s;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int kg = lane >> 4, hl = lane & 15;
   const int nxu = (Hkv * hgroups + NW - 1) / NW;
   const int j = blockIdx.x / nxu;
-  int b, split, L, seq = 0, pos = 0;
-  if constexpr (LIST) {
-    split = j % max_splits;
-    b = j / max_splits;
-    seq = la.row_seq[b];
-    L = seqlens[seq];
-    const int qs = la.cu_q[seq];
-    pos = L - (la.cu_q[seq + 1] - qs) + (b - qs);
-    seq = __builtin_amdgcn_readfirstlane(seq);
-    pos = __builtin_amdgcn_readfirstlane(pos);
-  } else if (items) {
-    if (j >= *count) return;  // uniform over the workgroup
-    const int item = items[j];
-    split = item % max_splits;
-    b = item / max_splits;
-    L = seqlens[b];
-  } else if (!find_chunk(seqlens, B, w1, w2, chunk, max_splits, j, lane, b, split, L)) {
-    return;  // uniform over the workgroup
-  }
-  b = __builtin_amdgcn_readfirstlane(b);
-  split = __builtin_amdgcn_readfirstlane(split);
-  L = __builtin_amdgcn_readfirstlane(L);
   const int unit = (blockIdx.x % nxu) * NW + wave;
   const bool active = unit < Hkv * hgroups;
   const int kvh = active ? unit / hgroups : 0, hgi = active ? unit % hgroups : 0;
   const int g = Hq / Hkv;
   const int g_eff = min(16, g - 16 * hgi);
   const int h0 = kvh * g + 16 * hgi;
-  const int nsel = LIST ? la.topk : n_selected(L, w1, w2);
-  const int u0 = split * chunk;
-  if (u0 >= nsel) return;  // uniform over the workgroup
-  const int u1 = min(nsel, u0 + chunk);
-  const int32_t* bt_row = bt + (size_t)(LIST ? seq : b) * max_pages;
   const size_t rs = (size_t)Hkv * D;
   const __bf16* kbase = kc + (size_t)kvh * D;
   const __bf16* vbase = vc + (size_t)kvh * D;
+  constexpr int TPL = KVRegs<D>::TPL, NTG = KVRegs<D>::NTG;
+  __bf16* vt = s.v[wave];
 
+  // One piece: selected tokens u0 .. u1-1 of sequence b (L cached tokens;
+  // LIST: packed row b of sequence seq at position pos), with its partial
+  // (acc, m, l) for head h written at index pbase + h * pstride.
+  auto run = [&](int b, int seq, int L, int pos, int u0, int u1, size_t pbase, size_t pstride) {
+  const int32_t* bt_row = bt + (size_t)(LIST ? seq : b) * max_pages;
   // Q^T fragments (B operand): column = head hl, k = d = 32*s + 8*kg ..
   bf16x8 qf[D / 32];
 #pragma unroll
@@ -290,9 +307,6 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
   f32x4 acc[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{};
-
-  constexpr int TPL = KVRegs<D>::TPL, NTG = KVRegs<D>::NTG;
-  __bf16* vt = s.v[wave];
 
   // One 32-token step of this wave: scores, online softmax, V^T staging, P.V.
   auto step = [&](const KVRegs<D>& cur, int base, int nsub) {
@@ -440,7 +454,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   if (hl < g_eff) {
-    float* dst = part + (((size_t)b * Hq + h0 + hl) * max_splits + split) * (D + 2);
+    float* dst = part + (pbase + (size_t)(h0 + hl) * pstride) * (D + 2);
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
       *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * kg) = acc[db];
@@ -449,26 +463,121 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
       dst[D + 1] = l;
     }
   }
+  };  // run
+
+  if constexpr (MODE == kModeEven) {
+    // every wave scans the selected-token counts itself (B <= kScanSeqs;
+    // T < 2^31 is checked by the host)
+    constexpr int R = kScanSeqs / 64;
+    int len[R], nsel[R], st[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) len[r] = seqlens[min(64 * r + lane, B - 1)];
+    int T = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      nsel[r] = 64 * r + lane < B ? n_selected(len[r], w1, w2) : 0;
+      int x = nsel[r];  // inclusive scan over the wave
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+      }
+      st[r] = T + x - nsel[r];
+      T += __shfl(x, 63, 64);
+    }
+    if (blockIdx.x == 0 && wave == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (64 * r + lane < B) ev.starts[64 * r + lane] = st[r];
+      if (lane == 0) ev.starts[B] = T;
+    }
+    if (T == 0) return;  // uniform over the workgroup
+    const int Ge = even_groups(ev.G, T);
+    if (j >= Ge) return;  // uniform over the workgroup
+    const int lo = (int)((long long)j * T / Ge), hi = (int)((long long)(j + 1) * T / Ge);
+    // first sequence whose tokens reach past lo, then every one starting before hi
+    int rem = lo, first = 0, before = 0, b = -1;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (b < 0 && wave_find(nsel[r], rem, lane, first, before)) b = 64 * r + first;
+    b = __builtin_amdgcn_readfirstlane(b);
+    for (; b < B; ++b) {
+      int sb = 0, nb = 0, Lb = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if ((b >> 6) == r) {
+          sb = __shfl(st[r], b & 63, 64);
+          nb = __shfl(nsel[r], b & 63, 64);
+          Lb = __shfl(len[r], b & 63, 64);
+        }
+      sb = __builtin_amdgcn_readfirstlane(sb);
+      nb = __builtin_amdgcn_readfirstlane(nb);
+      Lb = __builtin_amdgcn_readfirstlane(Lb);
+      if (sb >= hi) break;
+      if (nb == 0) continue;
+      run(b, 0, Lb, 0, max(lo, sb) - sb, min(hi, sb + nb) - sb, (size_t)j + b,
+          (size_t)ev.pstride);
+    }
+  } else {
+    int b, split, L, seq = 0, pos = 0;
+    if constexpr (LIST) {
+      split = j % max_splits;
+      b = j / max_splits;
+      seq = la.row_seq[b];
+      L = seqlens[seq];
+      const int qs = la.cu_q[seq];
+      pos = L - (la.cu_q[seq + 1] - qs) + (b - qs);
+      seq = __builtin_amdgcn_readfirstlane(seq);
+      pos = __builtin_amdgcn_readfirstlane(pos);
+    } else if (items) {
+      if (j >= *count) return;  // uniform over the workgroup
+      const int item = items[j];
+      split = item % max_splits;
+      b = item / max_splits;
+      L = seqlens[b];
+    } else if (!find_chunk(seqlens, B, w1, w2, chunk, max_splits, j, lane, b, split, L)) {
+      return;  // uniform over the workgroup
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    split = __builtin_amdgcn_readfirstlane(split);
+    L = __builtin_amdgcn_readfirstlane(L);
+    const int nsel = LIST ? la.topk : n_selected(L, w1, w2);
+    const int u0 = split * chunk;
+    if (u0 >= nsel) return;  // uniform over the workgroup
+    run(b, seq, L, pos, u0, min(nsel, u0 + chunk), (size_t)b * Hq * max_splits + split,
+        (size_t)max_splits);
+  }
 }
 
 // One wave per (sequence, query head): merge the chunk partials and fold the
 // sink in once: M = max(sink', m_k), Z = 2^(sink'-M) + sum 2^(m_k-M) l_k,
 // O = sum 2^(m_k-M) acc_k / Z, LSE = (M + log2 Z) ln 2.
-template <int D, bool LIST>
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ seqlens,
     const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq,
-    int w1, int w2, int chunk, int max_splits) {
+    int w1, int w2, int chunk, int max_splits, EvenArgs ev) {
+  constexpr bool LIST = MODE == kModeList;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bh = blockIdx.x * 4 + wave;
   if (bh >= B * Hq) return;
   const int b = bh / Hq, h = bh % Hq;
   int nsp = max_splits;  // LIST: every chunk of every row holds a partial
-  if constexpr (!LIST) {
+  const float* base = part + (size_t)bh * max_splits * (D + 2);
+  if constexpr (MODE == kModeEven) {
+    // pieces i0 .. i1: the workgroups whose ranges hold this sequence's tokens
+    const int sb = ev.starts[b], nb = ev.starts[b + 1] - sb, T = ev.starts[B];
+    nsp = 0;
+    if (nb > 0) {
+      const int Ge = even_groups(ev.G, T);
+      const int i0 = even_owner(sb, Ge, T), i1 = even_owner((long long)sb + nb - 1, Ge, T);
+      nsp = i1 - i0 + 1;
+      base = part + ((size_t)h * ev.pstride + i0 + b) * (D + 2);
+    }
+  } else if constexpr (!LIST) {
     const int nsel = n_selected(seqlens[b], w1, w2);
     nsp = nsel > 0 ? min(max_splits, (nsel + chunk - 1) / chunk) : 0;
   }
-  const float* base = part + (size_t)bh * max_splits * (D + 2);
   const float sig2 = sink ? sink[h] * kLog2e : kNegInf;
 
   // pass 1: lane k reads chunk k's (m, l); the max and the weighted sum of l
@@ -565,20 +674,33 @@ int log2_exact(int x) {
 
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pages, int w1, int w2,
                        int num_splits) {
-  DecodePlan p{0, 0, 0};
+  DecodePlan p{0, 0, 0, false};
   const long long maxL = (long long)max_pages * page_size;
   const long long max_sel = (w2 > 0) ? std::min<long long>(maxL, (long long)w1 + w2) : maxL;
   const int g = Hq / Hkv;
   const long long units = (long long)B * Hkv * ((g + 15) / 16);
+  // Equal token ranges (kModeEven) unless a split count is asked for, the
+  // sequences are too many for the in-kernel scan, their total could overflow
+  // int32, or the work is small: with fewer than 1024 units x 2048-token
+  // chunks, equal ranges become short pieces that each pay a workgroup's
+  // start and a partial (the single-sequence 1024 + 7168 window decode:
+  // 24 -> 32 us), and the chunks below serve better.
+  if (num_splits == 0 && B <= kScanSeqs && (long long)B * max_sel <= INT32_MAX &&
+      units * ((max_sel + 2047) / 2048) >= 1024) {
+    p.even = true;
+    p.chunk = 0;
+    p.max_splits = 0;
+    p.workspace_bytes = (size_t)Hq * (kEvenMaxG + B) * (D + 2) * sizeof(float) +
+                        ((size_t)B + 1) * sizeof(int32_t);
+    return p;
+  }
   long long chunk;
   if (num_splits > 0) {
     chunk = (max_sel + num_splits - 1) / num_splits;
     chunk = (chunk + 31) / 32 * 32;
   } else {
     // Long chunks amortise each workgroup's start (slot table, first loads);
-    // shorter ones only when long ones leave too few waves in flight.  The
-    // starting length of 2048 tokens is the measured optimum on the paged
-    // (D = 64) and the windowed (D = 128) decode workloads.
+    // shorter ones only when long ones leave too few waves in flight.
     chunk = 2048;
     if (units * ((max_sel + chunk - 1) / chunk) < 1024) {
       chunk = 1024;
@@ -595,6 +717,30 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pag
   return p;
 }
 
+namespace {
+// Workgroups of decode_partial_kernel<D, 4, kModeEven> resident on the whole
+// device at once (CUs x workgroups per CU), per device, computed once.
+template <int D>
+int even_capacity() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, decode_partial_kernel<D, 4, kModeEven>, 256, 0) != hipSuccess ||
+      cus <= 0 || per_cu <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  c = cus * per_cu;
+  cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+}  // namespace
+
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   const int g = a.Hq / a.Hkv;
   const int hgroups = (g + 15) / 16;
@@ -606,6 +752,38 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   const auto* vc = static_cast<const __bf16*>(a.v_cache);
   auto* o = static_cast<__bf16*>(a.o);
   const dim3 cgrid((a.B * a.Hq + 3) / 4);
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
+  using W2 = std::integral_constant<int, 2>;
+  using W4 = std::integral_constant<int, 4>;
+  using MChunks = std::integral_constant<int, kModeChunks>;
+  using MEven = std::integral_constant<int, kModeEven>;
+
+  if (a.even) {
+    // one round of resident workgroups (measured: two rounds of half-length
+    // ranges are 1-4 % slower), split evenly over the columns of 4 KV-head
+    // units
+    const int ncols = (units + 3) / 4;
+    const int cap = a.D == 64 ? even_capacity<64>() : even_capacity<128>();
+    const int G = std::max(1, std::min(kEvenMaxG, cap / ncols));
+    const EvenArgs ev{G, G + a.B,
+                      reinterpret_cast<int32_t*>(a.partials +
+                                                 (size_t)a.Hq * (kEvenMaxG + a.B) * (a.D + 2))};
+    auto run = [&](auto d) {
+      constexpr int D = decltype(d)::value;
+      decode_partial_kernel<D, 4, kModeEven><<<dim3((unsigned)(ncols * G)), 256, 0, stream>>>(
+          q, kc, vc, a.block_table, a.seqlens, a.partials, nullptr, nullptr, a.B, a.Hq, a.Hkv,
+          hgroups, page_shift, a.max_pages, sl2, a.w1, a.w2, 0, 0, ListArgs{}, ev);
+      decode_combine_kernel<D, kModeEven><<<cgrid, kThreads, 0, stream>>>(
+          a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, 0, 0, ev);
+    };
+    if (a.D == 64)
+      run(I64{});
+    else
+      run(I128{});
+    return hipGetLastError();
+  }
+
   int32_t* items = reinterpret_cast<int32_t*>(a.partials + (size_t)a.B * a.Hq * a.max_splits *
                                                                (a.D + 2));
   int32_t* count = items + (size_t)a.B * a.max_splits;
@@ -624,29 +802,29 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   auto partial = [&](auto d, auto nw) {
     constexpr int D = decltype(d)::value, NW = decltype(nw)::value;
     const dim3 grid((unsigned)(((units + NW - 1) / NW) * slots));
-    decode_partial_kernel<D, NW, false><<<grid, 64 * NW, 0, stream>>>(
+    decode_partial_kernel<D, NW, kModeChunks><<<grid, 64 * NW, 0, stream>>>(
         q, kc, vc, a.block_table, a.seqlens, a.partials, items, count, a.B, a.Hq, a.Hkv, hgroups,
-        page_shift, a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits, ListArgs{});
+        page_shift, a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits, ListArgs{}, EvenArgs{});
   };
-  using I64 = std::integral_constant<int, 64>;
-  using I128 = std::integral_constant<int, 128>;
-  using W2 = std::integral_constant<int, 2>;
-  using W4 = std::integral_constant<int, 4>;
   if (a.D == 64) {
     if (narrow)
       partial(I64{}, W2{});
     else
       partial(I64{}, W4{});
-    decode_combine_kernel<64, false><<<cgrid, kThreads, 0, stream>>>(
-        a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits);
+    decode_combine_kernel<64, kModeChunks><<<cgrid, kThreads, 0, stream>>>(
+        a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits,
+        EvenArgs{});
   } else {
     if (narrow)
       partial(I128{}, W2{});
     else
       partial(I128{}, W4{});
-    decode_combine_kernel<128, false><<<cgrid, kThreads, 0, stream>>>(
-        a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits);
+    decode_combine_kernel<128, kModeChunks><<<cgrid, kThreads, 0, stream>>>(
+        a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits,
+        EvenArgs{});
   }
+  (void)MChunks{};
+  (void)MEven{};
   return hipGetLastError();
 }
 
@@ -698,9 +876,10 @@ hipError_t launch_index_rows_bf16(const IndexRowsArgs& a, hipStream_t stream) {
   auto partial = [&](auto d, auto nw) {
     constexpr int D = decltype(d)::value, NW = decltype(nw)::value;
     const dim3 grid((unsigned)(((units + NW - 1) / NW) * slots));
-    decode_partial_kernel<D, NW, true><<<grid, 64 * NW, 0, stream>>>(
+    decode_partial_kernel<D, NW, kModeList><<<grid, 64 * NW, 0, stream>>>(
         q, kc, vc, a.block_table, a.seqlens_k, part, nullptr, nullptr, a.total_q, a.Hq, a.Hkv,
-        hgroups, page_shift, a.max_pages, sl2, -1, -1, plan.chunk, plan.max_splits, la);
+        hgroups, page_shift, a.max_pages, sl2, -1, -1, plan.chunk, plan.max_splits, la,
+        EvenArgs{});
   };
   using I64 = std::integral_constant<int, 64>;
   using I128 = std::integral_constant<int, 128>;
@@ -712,17 +891,17 @@ hipError_t launch_index_rows_bf16(const IndexRowsArgs& a, hipStream_t stream) {
       partial(I64{}, W2{});
     else
       partial(I64{}, W4{});
-    decode_combine_kernel<64, true><<<cgrid, kThreads, 0, stream>>>(
+    decode_combine_kernel<64, kModeList><<<cgrid, kThreads, 0, stream>>>(
         part, a.seqlens_k, a.sink, o, a.lse, a.total_q, a.Hq, -1, -1, plan.chunk,
-        plan.max_splits);
+        plan.max_splits, EvenArgs{});
   } else {
     if (narrow)
       partial(I128{}, W2{});
     else
       partial(I128{}, W4{});
-    decode_combine_kernel<128, true><<<cgrid, kThreads, 0, stream>>>(
+    decode_combine_kernel<128, kModeList><<<cgrid, kThreads, 0, stream>>>(
         part, a.seqlens_k, a.sink, o, a.lse, a.total_q, a.Hq, -1, -1, plan.chunk,
-        plan.max_splits);
+        plan.max_splits, EvenArgs{});
   }
   return hipGetLastError();
 }

@@ -82,7 +82,10 @@ struct DecodeArgs {
   int chunk;       // selected tokens per split
   int max_splits;  // grid extent over splits
   float* partials; // workspace: [B, Hq, max_splits, D + 2] fp32 partials, then the
-                   // chunk list (B * max_splits int32) and its length (int32)
+                   // chunk list (B * max_splits int32) and its length (int32);
+                   // equal ranges: [Hq, G + B, D + 2] partials (room for
+                   // G <= 1024), then the sequences' starts (B + 1 int32)
+  bool even;       // equal token ranges instead of chunks
 };
 
 // Split plan shared by the workspace query and the launch.
@@ -90,6 +93,7 @@ struct DecodePlan {
   int chunk;
   int max_splits;
   size_t workspace_bytes;
+  bool even;  // equal token ranges per workgroup (chunk, max_splits unused)
 };
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pages, int w1,
                        int w2, int num_splits);

@@ -119,16 +119,29 @@ def test_decode_rejects(lib, kw, status, msg):
 
 def test_decode_workspace_query(lib):
     # 64 sequences of up to 2048 pages of 16 tokens, 64/8 heads, D 64
+    # default (num_splits 0, at most 256 sequences): equal token ranges per workgroup,
+    # fp32 partials [Hq, 1024 + B, D + 2], then the sequences' starts [B + 1]
     n = binding.attn_sink_decode_workspace_bytes(64, 64, 8, 64, 16, 2048)
-    # fp32 partials [B, Hq, splits, D + 2], then the chunk list [B * splits] and its length
-    splits = 2048 * 16 // 2048  # 2048-token chunks
+    assert n == 64 * (1024 + 64) * 66 * 4 + 65 * 4
+    # an explicit split count: fp32 partials [B, Hq, splits, D + 2], then the chunk list
+    # [B * splits] and its length
+    splits = 16
+    n = binding.attn_sink_decode_workspace_bytes(64, 64, 8, 64, 16, 2048, None, splits)
     assert n == 64 * 64 * splits * 66 * 4 + (64 * splits + 1) * 4
-    # the window caps the selected length, so the workspace shrinks
-    assert binding.attn_sink_decode_workspace_bytes(64, 64, 8, 64, 16, 2048, (1024, 7168)) < n
+    # with chunks the window caps the selected length, so the workspace shrinks
+    assert binding.attn_sink_decode_workspace_bytes(300, 64, 8, 64, 16, 2048, (1024, 7168)) < \
+        binding.attn_sink_decode_workspace_bytes(300, 64, 8, 64, 16, 2048)
     # more requested splits never need less workspace
     a = binding.attn_sink_decode_workspace_bytes(4, 8, 2, 64, 16, 64, None, 2)
     b = binding.attn_sink_decode_workspace_bytes(4, 8, 2, 64, 16, 64, None, 8)
     assert 0 < a < b
+    # little work (1 sequence, 32/8 heads, D 128, the 1024 + 7168 window: 8 units x 4
+    # chunks of 2048): 128-token chunks instead of equal ranges
+    n = binding.attn_sink_decode_workspace_bytes(1, 32, 8, 128, 16, 4096, (1024, 7168))
+    assert n == 32 * 64 * 130 * 4 + (64 + 1) * 4
+    # more than 256 sequences: 2048-token chunks
+    n = binding.attn_sink_decode_workspace_bytes(300, 8, 2, 64, 16, 256)
+    assert n == 300 * 8 * 2 * 66 * 4 + (300 * 2 + 1) * 4
     assert binding.attn_sink_decode_workspace_bytes(4, 8, 2, 96, 16, 64) == 0
 
 

@@ -114,6 +114,33 @@ def test_split_invariance_and_determinism():
     say(f"  max spread across split counts: {spread:.3e}")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,D,lo,hi,window", [
+    (128, 8, 8, 64, 1, 2, None),           # 192 tokens: few ranges, each over many sequences
+    (200, 8, 8, 64, 1, 300, None),         # ranges cross many sequence boundaries
+    (128, 8, 8, 128, 1, 2100, None),       # D 128
+    (129, 16, 8, 64, 100, 3000, (64, 512)),  # window, g 2
+    (256, 8, 8, 64, 1000, 1300, None),     # 256 sequences (the largest scanned count)
+])
+def test_equal_ranges_match_oracle_and_one_split(B, Hq, Hkv, D, lo, hi, window):
+    """The default work split for many KV-head units (equal token ranges per
+    workgroup, crossing sequence boundaries) against the oracle, against one split
+    per sequence, and run to run."""
+    need_gpu()
+    case = synth.decode_case(B, Hq, Hkv, D, 16, lo, hi, seed=21)
+    d = _dev(case)
+    scale = 1 / math.sqrt(D)
+    ro, rl = _oracle_decode(case, scale, window)
+    o, lse = _decode(d, scale, window)
+    check_close("O", host64(o), ro, TOL_O)
+    check_close("LSE", host64(lse), rl, TOL_LSE)
+    o1, l1 = _decode(d, scale, window, 1)
+    check_close("O vs one split", host64(o), host64(o1), TOL_O)
+    check_close("LSE vs one split", host64(lse), host64(l1), TOL_LSE)
+    o2, l2 = _decode(d, scale, window)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "run-to-run difference"
+    assert torch.equal(lse, l2), "run-to-run difference (LSE)"
+
+
 def test_paged_equals_identity_block_table_bitwise():
     """The physical page order does not change any bit of the result."""
     need_gpu()
