@@ -13,13 +13,19 @@ One step runs every entry point once over its synthetic workload:
   index     index-list selection: B2 x 4096 new tokens on 4096 cached ones, 64/8 heads, D64,
             page 16, one list of 2048 positions per 128 queries (first 64, last 512, uniform
             middle), sink
-Each entry point is bracketed by HIP events on the stream it is launched on;
+Each entry point is bracketed by HIP events on the stream it is launched on
+(the HBM-bound decode parts are preceded, outside their events, by a 512 MiB
+read that leaves the caches holding clean lines);
 `value` is the prefill throughput in TFLOP/s of algorithmic work (4*D flops per
 visible (query, key) pair), `decode_gbps` the paged decode's algorithmic HBM
 bytes (K and V rows of the attended tokens + Q + O + block table) per second.
 A bounded sample of the fp64 CPU oracle is timed on the host for comparison.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--parts a,b] [--no-cpu-baseline]
+Profile summaries (after rocprofv3 runs of this script):
+       python bench.py --kernel-stats-from run_kernel_trace.csv [--parts ...]
+       python bench.py --sq-from run_counter_collection.csv --parts ...
+       python bench.py --traffic-from FETCH.csv WRITE.csv --copy-probe-mib 1024
 """
 
 import argparse
@@ -37,6 +43,7 @@ METRIC = "prefill attention TFLOP/s + paged-decode HBM GB/s (% of MI355X rooflin
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PARTS = ("prefill", "decode", "window32", "window1", "extend", "train", "varlen", "index")
+HBM_PARTS = ("decode", "window32", "window1")
 
 
 def causal_pairs(B, Hq, Sq, Sk):
@@ -107,6 +114,118 @@ def write_traffic(fetch_csv, write_csv, probe_mib):
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def _grid(row):
+    if "Grid_Size" in row and row["Grid_Size"]:
+        return int(row["Grid_Size"])
+    g = 1
+    for ax in ("X", "Y", "Z"):
+        g *= int(row.get("Grid_Size_" + ax) or 1)
+    return g
+
+
+def _short(name):
+    """kernel<template args> from a profiler's kernel name (mangled or not)."""
+    import re
+    m = re.search(r"GLOBAL__N_1(\d+)", name) or re.search(r"attn_sink(\d+)", name)
+    if m:
+        n = int(m.group(1))
+        rest = name[m.end():]
+        base, rest = rest[:n], rest[n:]
+        args = re.match(r"I((?:L[a-z]+\d+E)+)E", rest)
+        if args:
+            base += "<" + ",".join(re.findall(r"L[a-z]+(\d+)E", args.group(1))) + ">"
+        return base
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return name.replace("attn_sink::", "").split("(")[0].replace(" ", "")
+
+
+# Library kernels each bench part launches, in launch order (one stream).
+PART_KERNELS = {
+    "prefill": ("prefill_bf16_kernel",),
+    "decode": ("decode_partial_kernel", "decode_combine_kernel"),
+    "window32": ("decode_partial_kernel", "decode_combine_kernel"),
+    "window1": ("decode_partial_kernel", "decode_combine_kernel"),
+    "extend": ("extend_kernel",),
+    "train": ("prefill_bf16_kernel", "bwd_preprocess_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
+              "bwd_dsink_reduce_kernel"),
+    "varlen": ("extend_kernel", "bwd_preprocess_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
+               "bwd_dsink_reduce_kernel"),
+    "index": ("index_kernel",),
+}
+
+
+def _label(names, parts):
+    """The bench part of each dispatch (None for kernels not of this library):
+    the parts run in order every step, each launching PART_KERNELS[part]."""
+    ours = {k for p in parts for k in PART_KERNELS[p]}
+    seq = [k for p in parts for k in PART_KERNELS[p]]
+    owner = [p for p in parts for _ in PART_KERNELS[p]]
+    out, i = [], 0
+    for n in names:
+        base = n.split("<")[0]
+        if base not in ours:
+            out.append(None)
+            continue
+        if base != seq[i % len(seq)]:
+            raise SystemExit(f"dispatch {n} does not follow the part order {parts}")
+        out.append(owner[i % len(seq)])
+        i += 1
+    return out
+
+
+def kernel_stats(trace_csv, parts):
+    """Per (bench part, kernel) launch count and duration from the
+    kernel_trace.csv of a `rocprofv3 --kernel-trace` run of this script with
+    these parts."""
+    import csv
+    with open(trace_csv) as f:
+        recs = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    names = [_short(r["Kernel_Name"]) for r in recs]
+    rows = {}
+    for r, n, p in zip(recs, names, _label(names, parts)):
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        rows.setdefault((p or "-", n, _grid(r)), []).append(us)
+    total = sum(sum(v) for v in rows.values())
+    print(f"{'part':9s} {'kernel':34s} {'grid':>9s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} "
+          f"{'max_us':>9s} {'share%':>7s}")
+    order = {p: i for i, p in enumerate(parts)}
+    for (p, k, g), v in sorted(rows.items(), key=lambda kv: (order.get(kv[0][0], 99), kv[0][1])):
+        print(f"{p:9s} {k:34s} {g:9d} {len(v):6d} {sum(v) / len(v):9.1f} {min(v):9.1f} "
+              f"{max(v):9.1f} {100 * sum(v) / total:7.2f}")
+
+
+def sq_stats(counter_csv, parts, xcds=8, simds=1024):
+    """MFMA busy fraction, VALU instructions per MFMA and the waves' wait fraction
+    per (bench part, kernel) from the counter_collection.csv of a rocprofv3 run
+    with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, SQ_INSTS_VALU, SQ_WAIT_INST_ANY,
+    SQ_WAVE_CYCLES and GRBM_GUI_ACTIVE: mfma_busy = MFMA busy cycles /
+    (GRBM_GUI_ACTIVE / XCDs * SIMDs); SQ_INSTS_VALU counts the MFMA issues too.
+    The last launch of each (part, kernel) is reported."""
+    import csv
+    disp = {}
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            d = disp.setdefault(int(r["Dispatch_Id"]),
+                                {"name": _short(r["Kernel_Name"]), "grid": _grid(r)})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(disp)
+    labels = _label([disp[i]["name"] for i in ids], parts)
+    last = {}
+    for i, p in zip(ids, labels):
+        if p:
+            last[(p, disp[i]["name"])] = disp[i]
+    print(f"{'part':9s} {'kernel':34s} {'grid':>9s} {'mfma_busy':>9s} {'MFMA_instr':>10s} "
+          f"{'VALU_instr':>10s} {'valu/mfma':>9s} {'wait/wave_cyc':>13s}")
+    for (p, k), d in last.items():
+        mf, va = d.get("SQ_INSTS_MFMA", 0.0), d.get("SQ_INSTS_VALU", 0.0)
+        gui = d.get("GRBM_GUI_ACTIVE", 0.0)
+        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui / xcds * simds) if gui else 0.0
+        wait = d.get("SQ_WAIT_INST_ANY", 0.0) / max(1.0, d.get("SQ_WAVE_CYCLES", 0.0))
+        ratio = f"{va / mf:9.1f}" if mf else f"{'-':>9s}"
+        print(f"{p:9s} {k:34s} {d['grid']:9d} {busy:9.3f} {mf:10.3g} {va:10.3g} {ratio} "
+              f"{wait:13.3f}")
 
 
 def load_traffic():
@@ -369,7 +488,19 @@ def main():
                     help="write profiles/hbm_traffic.json from the counter_collection.csv of a "
                          "FETCH_SIZE and a WRITE_SIZE rocprofv3 run made with --copy-probe-mib, "
                          "then exit")
+    ap.add_argument("--kernel-stats-from", metavar="TRACE_CSV",
+                    help="print per-kernel launch times from the kernel_trace.csv of a "
+                         "rocprofv3 --kernel-trace run, then exit")
+    ap.add_argument("--sq-from", metavar="COUNTER_CSV",
+                    help="print MFMA utilisation per kernel from the counter_collection.csv of "
+                         "a rocprofv3 SQ counter run, then exit")
     args = ap.parse_args()
+    if args.kernel_stats_from:
+        kernel_stats(args.kernel_stats_from, [p for p in args.parts.split(",") if p])
+        return
+    if args.sq_from:
+        sq_stats(args.sq_from, [p for p in args.parts.split(",") if p])
+        return
     if args.traffic_from:
         write_traffic(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib or 1024)
         return
@@ -401,9 +532,17 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     events = {p: [] for p in parts}
+    # Before each HBM-bound part, a 512 MiB read (outside the part's events) leaves
+    # the L2 and the 256 MB Infinity Cache holding clean lines: otherwise the decode
+    # pays for writing back the dirty output of the part before it (the prefill's
+    # 128 MiB of O), which is that part's traffic, not its own.
+    flush = (torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+             if any(p in HBM_PARTS for p in parts) else None)
 
     def step(record):
         for p in parts:
+            if p in HBM_PARTS:
+                flush.sum()
             if record:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)

@@ -158,7 +158,7 @@ struct RowGeom {
 
 // The running state of one wave: 32*QB query rows of one head, Q^T fragments,
 // running max / sum per row (one row per lane) and the O^T accumulators.  The
-// tile steps below are shared by the 4-wave and the 8-wave kernels, so both
+// tile steps below are shared by every forward kernel here, so all of them
 // compute the same arithmetic in the same order.
 template <int D, int QB>
 struct WaveRows {
