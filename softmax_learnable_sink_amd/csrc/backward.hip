@@ -246,9 +246,18 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   tq.init(rs, tid);
   tdo.init(rs, tid);
   float lse_r = 0.f, di_r = 0.f;
+  // iteration -> (query head, query tile): the last query tile first, all heads
+  // of the group for each tile.  Every key block's range of tiles ends at the
+  // sequence's last tile, so the key blocks of one KV head that run together
+  // (all on one XCD: the grid's fastest index is the KV head) walk the same
+  // Q/dO tiles at the same time and share them in L2.  Training workload
+  // (B2 S8192 64/8 heads): 6.6 -> 1.6 GB of HBM reads per launch against the
+  // first tile first, head by head; the time is the same.
+  auto head_of = [&](int it) { return kvh * g + it % g; };
+  auto row_of = [&](int it) { return (t_hi - 1 - it / g) * kTile; };
   auto load_iter = [&](int it) {
-    const int h = kvh * g + it / ntq;
-    const int i0 = (t_lo + it % ntq) * kTile;
+    const int h = head_of(it);
+    const int i0 = row_of(it);
     const size_t base = ((size_t)sr.q0 * Hq + h) * D;
     tq.load(q + base, rs, i0, nq);
     tdo.load(dout + base, rs, i0, nq);
@@ -278,7 +287,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 
   for (int it = 0; it < niter; ++it) {
     const int buf = it & 1;
-    const int i0 = (t_lo + it % ntq) * kTile;
+    const int i0 = row_of(it);
     if (it + 1 < niter) load_iter(it + 1);
     const int p0 = off + i0;
     const bool need_mask = (i0 + kTile > nq) || (causal && p0 < k1 - 1) ||
