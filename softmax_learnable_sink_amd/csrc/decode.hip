@@ -1,9 +1,12 @@
 // Paged decode with a learnable per-head sink and optional first/last window.
 //
-// Split-K: each sequence's selected tokens are cut into chunks of `chunk`
-// tokens.  A workgroup takes one chunk and NW (4, or 2 for small grids) KV
-// heads of it; wave w computes the scores of all query heads of its KV head
-// (GQA group, up to 16 per wave), so every K/V byte is read from HBM once:
+// Split-K: each sequence's selected tokens are cut into pieces, each with its
+// own partial: for large work, equal token ranges of the whole batch's
+// concatenated selections, one per resident workgroup (a range may cross
+// sequence boundaries); otherwise chunks of `chunk` tokens.  A workgroup takes
+// one range or chunk and NW (4, or 2 for small grids) KV heads of it; wave w
+// computes the scores of all query heads of its KV head (GQA group, up to 16
+// per wave), so every K/V byte is read from HBM once:
 //   * the slots of the chunk's tokens are computed once into LDS from the
 //     block table and the window rule (sglang PR #12504 "To implement
 //     attention-sink": first W1 tokens followed by the last W2 tokens of each
@@ -14,8 +17,8 @@
 //     the paged cache, a running max / sum per head WITHOUT the sink, and
 //     O^T += V^T P^T with V staged in a wave-private LDS tile and read back
 //     transposed;
-//   * each wave writes one partial (acc[D], m, l) per (sequence, head, chunk).
-// The combine kernel merges the chunks and folds the sink into the
+//   * each wave writes one partial (acc[D], m, l) per (sequence, head, piece).
+// The combine kernel merges the pieces and folds the sink into the
 // denominator exactly once (sglang PR #8825, Summary of Changes: the decode
 // path receives the per-head sink; flash-attention PR #1819 review thread:
 // decoding with a sink through the KV-cache entry point was reported wrong,
@@ -294,175 +297,175 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
   // LIST: packed row b of sequence seq at position pos), with its partial
   // (acc, m, l) for head h written at index pbase + h * pstride.
   auto run = [&](int b, int seq, int L, int pos, int u0, int u1, size_t pbase, size_t pstride) {
-  const int32_t* bt_row = bt + (size_t)(LIST ? seq : b) * max_pages;
-  // Q^T fragments (B operand): column = head hl, k = d = 32*s + 8*kg ..
-  bf16x8 qf[D / 32];
+    const int32_t* bt_row = bt + (size_t)(LIST ? seq : b) * max_pages;
+    // Q^T fragments (B operand): column = head hl, k = d = 32*s + 8*kg ..
+    bf16x8 qf[D / 32];
 #pragma unroll
-  for (int s2 = 0; s2 < D / 32; ++s2)
-    qf[s2] = (active && hl < g_eff)
-                 ? *reinterpret_cast<const bf16x8*>(q + ((size_t)b * Hq + h0 + hl) * D + 32 * s2 + 8 * kg)
-                 : bf16x8{};
+    for (int s2 = 0; s2 < D / 32; ++s2)
+      qf[s2] = (active && hl < g_eff)
+                   ? *reinterpret_cast<const bf16x8*>(q + ((size_t)b * Hq + h0 + hl) * D + 32 * s2 + 8 * kg)
+                   : bf16x8{};
 
-  float m = kNegInf, l = 0.f;
-  f32x4 acc[D / 16];
+    float m = kNegInf, l = 0.f;
+    f32x4 acc[D / 16];
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{};
+    for (int db = 0; db < D / 16; ++db) acc[db] = f32x4{};
 
-  // One 32-token step of this wave: scores, online softmax, V^T staging, P.V.
-  auto step = [&](const KVRegs<D>& cur, int base, int nsub) {
-    f32x4 sc[2] = {f32x4{}, f32x4{}};
+    // One 32-token step of this wave: scores, online softmax, V^T staging, P.V.
+    auto step = [&](const KVRegs<D>& cur, int base, int nsub) {
+      f32x4 sc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-    for (int G = 0; G < 2; ++G)
+      for (int G = 0; G < 2; ++G)
 #pragma unroll
-      for (int s2 = 0; s2 < D / 32; ++s2)
-        sc[G] = mfma16(__builtin_bit_cast(bf16x8, cur.kr[G][s2]), qf[s2], sc[G]);
-    float x[8];
+        for (int s2 = 0; s2 < D / 32; ++s2)
+          sc[G] = mfma16(__builtin_bit_cast(bf16x8, cur.kr[G][s2]), qf[s2], sc[G]);
+      float x[8];
 #pragma unroll
-    for (int G = 0; G < 2; ++G)
+      for (int G = 0; G < 2; ++G)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        x[4 * G + j] = (base + 8 * kg + 4 * G + j < nsub) ? sc[G][j] : kNegInf;
-    float mx = x[0];
+        for (int j = 0; j < 4; ++j)
+          x[4 * G + j] = (base + 8 * kg + 4 * G + j < nsub) ? sc[G][j] : kNegInf;
+      float mx = x[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m, mx * sl2);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2_fast(m - m_use);
-    m = m_new;
-    float p[8], rsum = 0.f;
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      const float m_new = fmaxf(m, mx * sl2);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = exp2_fast(m - m_use);
+      m = m_new;
+      float p[8], rsum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2_fast(__builtin_fmaf(x[e], sl2, -m_use));
-      rsum += p[e];
-    }
-    l = l * alpha + rsum;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
-    const bf16x8 pf = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-
-    // V staging, natural rows: token TPL*tg + t, d-chunk c; rows without a
-    // selected token are written as zeros
-    {
-      const int tg = lane % NTG, c = lane / NTG;
-#pragma unroll
-      for (int t = 0; t < TPL; ++t) {
-        const bool ok = (cur.vvalid >> t) & 1u;
-        const uint4 x = cur.vr[t];
-        *reinterpret_cast<uint4*>(vt + (TPL * tg + t) * vrow<D>() + 8 * c) =
-            uint4{ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u};
+      for (int e = 0; e < 8; ++e) {
+        p[e] = exp2_fast(__builtin_fmaf(x[e], sl2, -m_use));
+        rsum += p[e];
       }
-    }
-    wave_lds_sync();
+      l = l * alpha + rsum;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) acc[db] = mfma16(vt_frag16<D>(vt, db, lane), pf, acc[db]);
-    wave_lds_sync();
-  };
+      for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
+      const bf16x8 pf = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
 
-  for (int sub0 = u0; sub0 < u1; sub0 += kSub) {
-    constexpr int kPer = kSub / (64 * NW);
-    int nsub, nsteps, npad;
-    if constexpr (LIST) {
-      // thread t takes list entries t*kPer .. +kPer-1 of the block; the valid
-      // ones are compacted in entry order (a workgroup-wide exclusive scan of
-      // the per-thread counts), the rest of the table up to npad holds -1
-      const int ne = min(kSub, u1 - sub0);
-      const int32_t* lrow = la.kv_index + (size_t)b * la.topk + sub0;
-      int tv[kPer], sv[kPer], cnt = 0;
+      // V staging, natural rows: token TPL*tg + t, d-chunk c; rows without a
+      // selected token are written as zeros
+      {
+        const int tg = lane % NTG, c = lane / NTG;
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int x = tid * kPer + i;
-        const int t = lrow[min(x, ne - 1)];
-        const bool ok = (x < ne) & (t >= 0) & (t < L) & (t <= pos);
-        tv[i] = ok ? t : -1;
-        cnt += ok ? 1 : 0;
+        for (int t = 0; t < TPL; ++t) {
+          const bool ok = (cur.vvalid >> t) & 1u;
+          const uint4 x = cur.vr[t];
+          *reinterpret_cast<uint4*>(vt + (TPL * tg + t) * vrow<D>() + 8 * c) =
+              uint4{ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u};
+        }
       }
+      wave_lds_sync();
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) sv[i] = slot_of(bt_row, max(tv[i], 0), page_shift);
+      for (int db = 0; db < D / 16; ++db) acc[db] = mfma16(vt_frag16<D>(vt, db, lane), pf, acc[db]);
+      wave_lds_sync();
+    };
+
+    for (int sub0 = u0; sub0 < u1; sub0 += kSub) {
+      constexpr int kPer = kSub / (64 * NW);
+      int nsub, nsteps, npad;
+      if constexpr (LIST) {
+        // thread t takes list entries t*kPer .. +kPer-1 of the block; the valid
+        // ones are compacted in entry order (a workgroup-wide exclusive scan of
+        // the per-thread counts), the rest of the table up to npad holds -1
+        const int ne = min(kSub, u1 - sub0);
+        const int32_t* lrow = la.kv_index + (size_t)b * la.topk + sub0;
+        int tv[kPer], sv[kPer], cnt = 0;
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(sv[i]));
-      int x = cnt;  // inclusive scan over the wave
+        for (int i = 0; i < kPer; ++i) {
+          const int x = tid * kPer + i;
+          const int t = lrow[min(x, ne - 1)];
+          const bool ok = (x < ne) & (t >= 0) & (t < L) & (t <= pos);
+          tv[i] = ok ? t : -1;
+          cnt += ok ? 1 : 0;
+        }
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
+        for (int i = 0; i < kPer; ++i) sv[i] = slot_of(bt_row, max(tv[i], 0), page_shift);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(sv[i]));
+        int x = cnt;  // inclusive scan over the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(x, d, 64);
+          if (lane >= d) x += y;
+        }
+        if (lane == 63) s.wsum[wave] = x;
+        __syncthreads();
+        int off = x - cnt, total = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          off += w < wave ? s.wsum[w] : 0;
+          total += s.wsum[w];
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          if (tv[i] >= 0) s.slot[off++] = sv[i];
+        nsub = total;
+        nsteps = (nsub + 31) >> 5;
+        npad = min(kSub, 64 * max(1, (nsteps + 1) >> 1));
+        for (int y = nsub + tid; y < npad; y += 64 * NW) s.slot[y] = -1;
+      } else {
+        nsub = min(kSub, u1 - sub0);
+        nsteps = (nsub + 31) >> 5;
+        // slot table of this block, padded with -1 up to an even number of steps;
+        // every block-table load of a thread is issued before its first LDS write,
+        // so the table costs one memory latency (overlapping the Q loads)
+        npad = min(kSub, 64 * ((nsteps + 1) >> 1));
+        int sv[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)  // index clamped to a selected token
+          sv[i] = slot_of(bt_row, token_of(sub0 + min(tid + i * 64 * NW, nsub - 1), L, w1, w2),
+                          page_shift);
+        // keep the loads unconditional and issued together (otherwise the compiler
+        // sinks each one into the branch that uses it and waits for it there)
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(sv[i]));
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const int x = tid + i * 64 * NW;
+          if (x < npad) s.slot[x] = x < nsub ? sv[i] : -1;
+        }
       }
-      if (lane == 63) s.wsum[wave] = x;
       __syncthreads();
-      int off = x - cnt, total = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        off += w < wave ? s.wsum[w] : 0;
-        total += s.wsum[w];
+      // start the step loop with no VMEM load pending, so that the compiler's
+      // wait tracking does not hold a step's MFMAs on the next step's prefetch
+      __builtin_amdgcn_s_waitcnt(0);
+      if (active) {
+        // Two register sets in turn, two steps per iteration with no exit in
+        // between (so the compiler cannot sink the prefetch below a branch); an
+        // odd last step runs on padding slots and is fully masked.
+        // sched_barrier keeps each prefetch issued ahead of the step it overlaps
+        KVRegs<D> ra, rb;
+        ra.load(s.slot, 0, kbase, vbase, rs, lane);
+        for (int st = 0; st < nsteps; st += 2) {
+          rb.load(s.slot, 32 * (st + 1), kbase, vbase, rs, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          step(ra, 32 * st, nsub);
+          ra.load(s.slot, 32 * min(st + 2, npad / 32 - 1), kbase, vbase, rs, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          step(rb, 32 * (st + 1), nsub);
+        }
       }
-#pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (tv[i] >= 0) s.slot[off++] = sv[i];
-      nsub = total;
-      nsteps = (nsub + 31) >> 5;
-      npad = min(kSub, 64 * max(1, (nsteps + 1) >> 1));
-      for (int y = nsub + tid; y < npad; y += 64 * NW) s.slot[y] = -1;
-    } else {
-      nsub = min(kSub, u1 - sub0);
-      nsteps = (nsub + 31) >> 5;
-      // slot table of this block, padded with -1 up to an even number of steps;
-      // every block-table load of a thread is issued before its first LDS write,
-      // so the table costs one memory latency (overlapping the Q loads)
-      npad = min(kSub, 64 * ((nsteps + 1) >> 1));
-      int sv[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i)  // index clamped to a selected token
-        sv[i] = slot_of(bt_row, token_of(sub0 + min(tid + i * 64 * NW, nsub - 1), L, w1, w2),
-                        page_shift);
-      // keep the loads unconditional and issued together (otherwise the compiler
-      // sinks each one into the branch that uses it and waits for it there)
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(sv[i]));
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int x = tid + i * 64 * NW;
-        if (x < npad) s.slot[x] = x < nsub ? sv[i] : -1;
-      }
+      __syncthreads();
     }
-    __syncthreads();
-    // start the step loop with no VMEM load pending, so that the compiler's
-    // wait tracking does not hold a step's MFMAs on the next step's prefetch
-    __builtin_amdgcn_s_waitcnt(0);
-    if (active) {
-      // Two register sets in turn, two steps per iteration with no exit in
-      // between (so the compiler cannot sink the prefetch below a branch); an
-      // odd last step runs on padding slots and is fully masked.
-      // sched_barrier keeps each prefetch issued ahead of the step it overlaps
-      KVRegs<D> ra, rb;
-      ra.load(s.slot, 0, kbase, vbase, rs, lane);
-      for (int st = 0; st < nsteps; st += 2) {
-        rb.load(s.slot, 32 * (st + 1), kbase, vbase, rs, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        step(ra, 32 * st, nsub);
-        ra.load(s.slot, 32 * min(st + 2, npad / 32 - 1), kbase, vbase, rs, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        step(rb, 32 * (st + 1), nsub);
-      }
-    }
-    __syncthreads();
-  }
-  if (!active) return;
+    if (!active) return;
 
-  // ---- partial (acc, m, l) of this wave's heads: lane (kg, hl) holds head hl,
-  // d = 16*db + 4*kg + j
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (hl < g_eff) {
-    float* dst = part + (pbase + (size_t)(h0 + hl) * pstride) * (D + 2);
+    // ---- partial (acc, m, l) of this wave's heads: lane (kg, hl) holds head hl,
+    // d = 16*db + 4*kg + j
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (hl < g_eff) {
+      float* dst = part + (pbase + (size_t)(h0 + hl) * pstride) * (D + 2);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-      *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * kg) = acc[db];
-    if (kg == 0) {
-      dst[D] = m;
-      dst[D + 1] = l;
+      for (int db = 0; db < D / 16; ++db)
+        *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * kg) = acc[db];
+      if (kg == 0) {
+        dst[D] = m;
+        dst[D + 1] = l;
+      }
     }
-  }
   };  // run
 
   if constexpr (MODE == kModeEven) {
