@@ -148,9 +148,9 @@ PART_KERNELS = {
     "window32": ("decode_partial_kernel", "decode_combine_kernel"),
     "window1": ("decode_partial_kernel", "decode_combine_kernel"),
     "extend": ("extend_kernel",),
-    "train": ("prefill_bf16_kernel", "bwd_preprocess_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
+    "train": ("prefill_bf16_kernel", "bwd_preprocess_kernel", "bwd_main_kernel",
               "bwd_dsink_reduce_kernel"),
-    "varlen": ("extend_kernel", "bwd_preprocess_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
+    "varlen": ("extend_kernel", "bwd_preprocess_kernel", "bwd_main_kernel",
                "bwd_dsink_reduce_kernel"),
     "index": ("index_kernel",),
 }

@@ -20,8 +20,8 @@ import bench  # noqa: E402
      "prefill_bf16_kernel<64,2>"),
     ("_ZN9attn_sink12_GLOBAL__N_121decode_partial_kernelILi128ELi4ELi2EEEvPKDF16bS3_S3_PKiS5_",
      "decode_partial_kernel<128,4,2>"),
-    ("_ZN9attn_sink12_GLOBAL__N_115bwd_dkdv_kernelILi64EEEvPKDF16bS3_S3_S3_PKfS5_PDF16bS6_",
-     "bwd_dkdv_kernel<64>"),
+    ("_ZN9attn_sink12_GLOBAL__N_115bwd_main_kernelILi64EEEvPKDF16bS3_S3_S3_PKfS5_PDF16bS6_",
+     "bwd_main_kernel<64>"),
     ("void attn_sink::(anonymous namespace)::decode_combine_kernel<64, 2>(float const*, int)",
      "decode_combine_kernel<64,2>"),
     ("bwd_dsink_reduce_kernel(float const*, float*, int, int, int)", "bwd_dsink_reduce_kernel"),
@@ -35,11 +35,11 @@ def test_dispatches_are_labelled_by_part_in_step_order():
     parts = ["prefill", "decode", "train"]
     one_step = (["prefill_bf16_kernel<64,2>", "reduce_kernel",
                  "decode_partial_kernel<64,4,2>", "decode_combine_kernel<64,2>"]
-                + ["prefill_bf16_kernel<64,2>", "bwd_preprocess_kernel<64>", "bwd_dkdv_kernel<64>",
-                   "bwd_dq_kernel<64>", "bwd_dsink_reduce_kernel"])
+                + ["prefill_bf16_kernel<64,2>", "bwd_preprocess_kernel<64>", "bwd_main_kernel<64>",
+                   "bwd_dsink_reduce_kernel"])
     names = ["__amd_rocclr_copyBuffer"] + one_step * 2
     labels = bench._label(names, parts)
-    want_step = ["prefill", None, "decode", "decode"] + ["train"] * 5
+    want_step = ["prefill", None, "decode", "decode"] + ["train"] * 4
     assert labels == [None] + want_step * 2
 
 
@@ -62,8 +62,8 @@ def test_kernel_stats_per_part(tmp_path, capsys):
     p = tmp_path / "trace.csv"
     # two steps of prefill (same kernel, same grid as the training forward) + train
     step = [("prefill_bf16_kernel<64,2>", 1000), ("prefill_bf16_kernel<64,2>", 3000),
-            ("bwd_preprocess_kernel<64>", 10), ("bwd_dkdv_kernel<64>", 5000),
-            ("bwd_dq_kernel<64>", 4000), ("bwd_dsink_reduce_kernel", 5)]
+            ("bwd_preprocess_kernel<64>", 10), ("bwd_main_kernel<64>", 9000),
+            ("bwd_dsink_reduce_kernel", 5)]
     rows, t = [], 0
     for _ in range(2):
         for name, dur in step:
