@@ -233,8 +233,11 @@ int attn_sink_fwd_varlen(const void* q, const void* k, const void* v, const int3
  *   sink         [Hq] fp32 or NULL
  *   o            [B, Hq, D] bf16                   -- output
  *   lse          [B, Hq] fp32 or NULL              -- output
- *   num_splits   split-K parts per sequence; 0 picks a heuristic. The result
- *                does not depend on it beyond fp32 rounding order.
+ *   num_splits   split-K parts per sequence; 0 picks the split itself: for
+ *                large work (at most 256 sequences) equal token ranges of the
+ *                whole batch, one per workgroup the device holds at once, else
+ *                fixed-length chunks.  The result does not depend on it beyond
+ *                fp32 rounding order.
  *   workspace    device scratch of at least attn_sink_decode_workspace_bytes()
  *                bytes for the same arguments; contents need no initialisation.
  * Requirements: D in {64, 128}; page_size a power of two in [1, 256];
