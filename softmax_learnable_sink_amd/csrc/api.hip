@@ -156,7 +156,8 @@ int attn_sink_fwd_extend_paged(const void* q, const void* k_cache, const void* v
   if (total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;  // nothing to compute
   ExtendArgs a{q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, nullptr, sink, o, lse,
                B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages_per_seq,
-               softmax_scale, 1, window_first, window_last};
+               softmax_scale, 1, window_first, window_last,
+               (long long)num_pages * page_size};
   return hip_status(launch_extend_bf16(a, static_cast<hipStream_t>(hip_stream)),
                     "attn_sink_fwd_extend_paged launch");
 }
@@ -203,7 +204,7 @@ int attn_sink_fwd_index_paged(const void* q, const void* k_cache, const void* v_
   if (total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;  // nothing to compute
   IndexArgs a{q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, kv_index, cu_blocks,
               sink, o, lse, B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages_per_seq,
-              block_q, topk, softmax_scale};
+              block_q, topk, softmax_scale, (long long)num_pages * page_size};
   return hip_status(launch_index_bf16(a, static_cast<hipStream_t>(hip_stream)),
                     "attn_sink_fwd_index_paged launch");
 }
@@ -291,7 +292,8 @@ int attn_sink_fwd_varlen(const void* q, const void* k, const void* v, const int3
           "cu_seqlens_q, cu_seqlens_k, sink and lse must be 4-byte aligned");
   if (total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;  // nothing to compute
   ExtendArgs a{q, k, v, nullptr, cu_seqlens_q, nullptr, cu_seqlens_k, sink, o, lse, B, total_q,
-               max_seqlen_q, Hq, Hkv, D, 1, 0, softmax_scale, causal, window_first, window_last};
+               max_seqlen_q, Hq, Hkv, D, 1, 0, softmax_scale, causal, window_first, window_last,
+               (long long)total_k};
   return hip_status(launch_extend_bf16(a, static_cast<hipStream_t>(hip_stream)),
                     "attn_sink_fwd_varlen launch");
 }

@@ -41,6 +41,7 @@ struct ExtendArgs {
   int B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages;
   float scale;
   int causal, w1, w2;
+  long long kv_rows;  // rows of k and v: num_pages * page_size, or total_k
 };
 
 hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream);
@@ -63,6 +64,7 @@ struct IndexArgs {
   float* lse;  // [Hq, total_q] or NULL
   int B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages, block_q, topk;
   float scale;
+  long long kv_rows;  // num_pages * page_size
 };
 
 hipError_t launch_index_bf16(const IndexArgs& a, hipStream_t stream);
