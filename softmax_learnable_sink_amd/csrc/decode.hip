@@ -86,6 +86,30 @@ struct KVRegs {
       vvalid |= (vs[t] >= 0 ? 1u : 0u) << t;
     }
   }
+  // The same through buffer resources over the K and V caches (each below
+  // 4 GiB): 32-bit byte offsets, no 64-bit address per row.
+  __device__ __forceinline__ void load(const int* slot, int base, __amdgpu_buffer_rsrc_t rk,
+                                       __amdgpu_buffer_rsrc_t rv, uint32_t rs_bytes, int lane) {
+    const int kg = lane >> 4, r = lane & 15;
+    const int tg = lane % NTG, c = lane / NTG;
+    int ks[2], vs[TPL];
+#pragma unroll
+    for (int G = 0; G < 2; ++G) ks[G] = slot[base + 8 * (r >> 2) + 4 * G + (r & 3)];
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) vs[t] = slot[base + TPL * tg + t];
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      const uint32_t row = (uint32_t)max(ks[G], 0) * rs_bytes + 16 * kg;
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) kr[G][s2] = buf_load16(rk, row + 64 * s2);
+    }
+    vvalid = 0;
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      vr[t] = buf_load16(rv, (uint32_t)max(vs[t], 0) * rs_bytes + 16 * c);
+      vvalid |= (vs[t] >= 0 ? 1u : 0u) << t;
+    }
+  }
 };
 
 // A operand (16 d x 32 tokens) of O^T += V^T P^T read from the natural V tile:
@@ -267,13 +291,13 @@ __host__ __device__ __forceinline__ int even_owner(long long t, int Ge, int T) {
   return (int)(((t + 1) * Ge + T - 1) / T) - 1;
 }
 
-template <int D, int NW, int MODE>
+template <int D, int NW, int MODE, bool BUF>
 __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seqlens, float* __restrict__ part,
     const int32_t* __restrict__ items, const int32_t* __restrict__ count, int B, int Hq, int Hkv,
     int hgroups, int page_shift, int max_pages, float sl2, int w1, int w2, int chunk,
-    int max_splits, ListArgs la, EvenArgs ev) {
+    int max_splits, ListArgs la, EvenArgs ev, uint32_t kv_bytes) {
   constexpr bool LIST = MODE == kModeList;
   __shared__ DecLds<D, NW> s;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -290,6 +314,16 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
   const size_t rs = (size_t)Hkv * D;
   const __bf16* kbase = kc + (size_t)kvh * D;
   const __bf16* vbase = vc + (size_t)kvh * D;
+  const uint32_t head_bytes = (uint32_t)(kvh * D * 2);
+  const auto rk = make_rsrc(kbase, kv_bytes - head_bytes);
+  const auto rv = make_rsrc(vbase, kv_bytes - head_bytes);
+  const uint32_t rs_bytes = (uint32_t)(rs * 2);
+  auto load_step = [&](KVRegs<D>& regs, int base) {
+    if constexpr (BUF)
+      regs.load(s.slot, base, rk, rv, rs_bytes, lane);
+    else
+      regs.load(s.slot, base, kbase, vbase, rs, lane);
+  };
   constexpr int TPL = KVRegs<D>::TPL, NTG = KVRegs<D>::NTG;
   __bf16* vt = s.v[wave];
 
@@ -438,12 +472,12 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
         // odd last step runs on padding slots and is fully masked.
         // sched_barrier keeps each prefetch issued ahead of the step it overlaps
         KVRegs<D> ra, rb;
-        ra.load(s.slot, 0, kbase, vbase, rs, lane);
+        load_step(ra, 0);
         for (int st = 0; st < nsteps; st += 2) {
-          rb.load(s.slot, 32 * (st + 1), kbase, vbase, rs, lane);
+          load_step(rb, 32 * (st + 1));
           __builtin_amdgcn_sched_barrier(0);
           step(ra, 32 * st, nsub);
-          ra.load(s.slot, 32 * min(st + 2, npad / 32 - 1), kbase, vbase, rs, lane);
+          load_step(ra, 32 * min(st + 2, npad / 32 - 1));
           __builtin_amdgcn_sched_barrier(0);
           step(rb, 32 * (st + 1), nsub);
         }
@@ -721,9 +755,9 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pag
 }
 
 namespace {
-// Workgroups of decode_partial_kernel<D, 4, kModeEven> resident on the whole
-// device at once (CUs x workgroups per CU), per device, computed once.
-template <int D>
+// Workgroups of decode_partial_kernel<D, 4, kModeEven, BUF> resident on the
+// whole device at once (CUs x workgroups per CU), per device, computed once.
+template <int D, bool BUF>
 int even_capacity() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -733,7 +767,7 @@ int even_capacity() {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, decode_partial_kernel<D, 4, kModeEven>, 256, 0) != hipSuccess ||
+          &per_cu, decode_partial_kernel<D, 4, kModeEven, BUF>, 256, 0) != hipSuccess ||
       cus <= 0 || per_cu <= 0) {
     (void)hipGetLastError();
     return 256;
@@ -759,31 +793,39 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   using I128 = std::integral_constant<int, 128>;
   using W2 = std::integral_constant<int, 2>;
   using W4 = std::integral_constant<int, 4>;
-  using MChunks = std::integral_constant<int, kModeChunks>;
-  using MEven = std::integral_constant<int, kModeEven>;
+
+  // caches below 4 GiB (each of K and V) are read through buffer resources
+  const long long kv_bytes = (long long)a.num_pages * a.page_size * a.Hkv * a.D * 2;
+  const bool buf = kv_bytes > 0 && kv_bytes < (1LL << 32);
+  const uint32_t kvb = buf ? (uint32_t)kv_bytes : 0u;
+  using T = std::true_type;
+  using F = std::false_type;
 
   if (a.even) {
     // one round of resident workgroups (measured: two rounds of half-length
     // ranges are 1-4 % slower), split evenly over the columns of 4 KV-head
     // units
     const int ncols = (units + 3) / 4;
-    const int cap = a.D == 64 ? even_capacity<64>() : even_capacity<128>();
-    const int G = std::max(1, std::min(kEvenMaxG, cap / ncols));
-    const EvenArgs ev{G, G + a.B,
-                      reinterpret_cast<int32_t*>(a.partials +
-                                                 (size_t)a.Hq * (kEvenMaxG + a.B) * (a.D + 2))};
-    auto run = [&](auto d) {
+    auto run = [&](auto d, auto use_buf) {
       constexpr int D = decltype(d)::value;
-      decode_partial_kernel<D, 4, kModeEven><<<dim3((unsigned)(ncols * G)), 256, 0, stream>>>(
-          q, kc, vc, a.block_table, a.seqlens, a.partials, nullptr, nullptr, a.B, a.Hq, a.Hkv,
-          hgroups, page_shift, a.max_pages, sl2, a.w1, a.w2, 0, 0, ListArgs{}, ev);
+      constexpr bool BUF = decltype(use_buf)::value;
+      const int cap = even_capacity<D, BUF>();
+      const int G = std::max(1, std::min(kEvenMaxG, cap / ncols));
+      const EvenArgs ev{G, G + a.B,
+                        reinterpret_cast<int32_t*>(a.partials +
+                                                   (size_t)a.Hq * (kEvenMaxG + a.B) * (a.D + 2))};
+      decode_partial_kernel<D, 4, kModeEven, BUF>
+          <<<dim3((unsigned)(ncols * G)), 256, 0, stream>>>(
+              q, kc, vc, a.block_table, a.seqlens, a.partials, nullptr, nullptr, a.B, a.Hq,
+              a.Hkv, hgroups, page_shift, a.max_pages, sl2, a.w1, a.w2, 0, 0, ListArgs{}, ev,
+              kvb);
       decode_combine_kernel<D, kModeEven><<<cgrid, kThreads, 0, stream>>>(
           a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, 0, 0, ev);
     };
     if (a.D == 64)
-      run(I64{});
+      buf ? run(I64{}, T{}) : run(I64{}, F{});
     else
-      run(I128{});
+      buf ? run(I128{}, T{}) : run(I128{}, F{});
     return hipGetLastError();
   }
 
@@ -805,9 +847,16 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   auto partial = [&](auto d, auto nw) {
     constexpr int D = decltype(d)::value, NW = decltype(nw)::value;
     const dim3 grid((unsigned)(((units + NW - 1) / NW) * slots));
-    decode_partial_kernel<D, NW, kModeChunks><<<grid, 64 * NW, 0, stream>>>(
-        q, kc, vc, a.block_table, a.seqlens, a.partials, items, count, a.B, a.Hq, a.Hkv, hgroups,
-        page_shift, a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits, ListArgs{}, EvenArgs{});
+    if (buf)
+      decode_partial_kernel<D, NW, kModeChunks, true><<<grid, 64 * NW, 0, stream>>>(
+          q, kc, vc, a.block_table, a.seqlens, a.partials, items, count, a.B, a.Hq, a.Hkv,
+          hgroups, page_shift, a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits, ListArgs{},
+          EvenArgs{}, kvb);
+    else
+      decode_partial_kernel<D, NW, kModeChunks, false><<<grid, 64 * NW, 0, stream>>>(
+          q, kc, vc, a.block_table, a.seqlens, a.partials, items, count, a.B, a.Hq, a.Hkv,
+          hgroups, page_shift, a.max_pages, sl2, a.w1, a.w2, a.chunk, a.max_splits, ListArgs{},
+          EvenArgs{}, 0u);
   };
   if (a.D == 64) {
     if (narrow)
@@ -826,8 +875,6 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
         a.partials, a.seqlens, a.sink, o, a.lse, a.B, a.Hq, a.w1, a.w2, a.chunk, a.max_splits,
         EvenArgs{});
   }
-  (void)MChunks{};
-  (void)MEven{};
   return hipGetLastError();
 }
 
@@ -879,10 +926,10 @@ hipError_t launch_index_rows_bf16(const IndexRowsArgs& a, hipStream_t stream) {
   auto partial = [&](auto d, auto nw) {
     constexpr int D = decltype(d)::value, NW = decltype(nw)::value;
     const dim3 grid((unsigned)(((units + NW - 1) / NW) * slots));
-    decode_partial_kernel<D, NW, kModeList><<<grid, 64 * NW, 0, stream>>>(
+    decode_partial_kernel<D, NW, kModeList, false><<<grid, 64 * NW, 0, stream>>>(
         q, kc, vc, a.block_table, a.seqlens_k, part, nullptr, nullptr, a.total_q, a.Hq, a.Hkv,
         hgroups, page_shift, a.max_pages, sl2, -1, -1, plan.chunk, plan.max_splits, la,
-        EvenArgs{});
+        EvenArgs{}, 0u);
   };
   using I64 = std::integral_constant<int, 64>;
   using I128 = std::integral_constant<int, 128>;
