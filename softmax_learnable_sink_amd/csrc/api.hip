@@ -257,7 +257,7 @@ int attn_sink_fwd_index_rows_paged(const void* q, const void* k_cache, const voi
           plan.workspace_bytes);
   IndexRowsArgs a{q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, kv_index, sink, o,
                   lse, B, total_q, Hq, Hkv, D, page_size, max_pages_per_seq, topk,
-                  softmax_scale, workspace};
+                  softmax_scale, workspace, (long long)num_pages * page_size};
   return hip_status(launch_index_rows_bf16(a, static_cast<hipStream_t>(hip_stream)),
                     "attn_sink_fwd_index_rows_paged launch");
 }

@@ -923,13 +923,22 @@ hipError_t launch_index_rows_bf16(const IndexRowsArgs& a, hipStream_t stream) {
   const ListArgs la{a.kv_index, row_seq, a.cu_seqlens_q, a.topk};
   const long long slots = (long long)a.total_q * plan.max_splits;
   const bool narrow = ((units + 3) / 4) * slots < 256;
+  // caches below 4 GiB (each of K and V) are read through buffer resources
+  const long long kv_bytes = a.kv_rows * a.Hkv * a.D * 2;
+  const bool buf = kv_bytes > 0 && kv_bytes < (1LL << 32);
   auto partial = [&](auto d, auto nw) {
     constexpr int D = decltype(d)::value, NW = decltype(nw)::value;
     const dim3 grid((unsigned)(((units + NW - 1) / NW) * slots));
-    decode_partial_kernel<D, NW, kModeList, false><<<grid, 64 * NW, 0, stream>>>(
-        q, kc, vc, a.block_table, a.seqlens_k, part, nullptr, nullptr, a.total_q, a.Hq, a.Hkv,
-        hgroups, page_shift, a.max_pages, sl2, -1, -1, plan.chunk, plan.max_splits, la,
-        EvenArgs{}, 0u);
+    if (buf)
+      decode_partial_kernel<D, NW, kModeList, true><<<grid, 64 * NW, 0, stream>>>(
+          q, kc, vc, a.block_table, a.seqlens_k, part, nullptr, nullptr, a.total_q, a.Hq, a.Hkv,
+          hgroups, page_shift, a.max_pages, sl2, -1, -1, plan.chunk, plan.max_splits, la,
+          EvenArgs{}, (uint32_t)kv_bytes);
+    else
+      decode_partial_kernel<D, NW, kModeList, false><<<grid, 64 * NW, 0, stream>>>(
+          q, kc, vc, a.block_table, a.seqlens_k, part, nullptr, nullptr, a.total_q, a.Hq, a.Hkv,
+          hgroups, page_shift, a.max_pages, sl2, -1, -1, plan.chunk, plan.max_splits, la,
+          EvenArgs{}, 0u);
   };
   using I64 = std::integral_constant<int, 64>;
   using I128 = std::integral_constant<int, 128>;

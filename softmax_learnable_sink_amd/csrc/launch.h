@@ -119,6 +119,7 @@ struct IndexRowsArgs {
   int B, total_q, Hq, Hkv, D, page_size, max_pages, topk;
   float scale;
   void* workspace;
+  long long kv_rows;  // num_pages * page_size
 };
 DecodePlan plan_index_rows(int total_q, int Hq, int Hkv, int D, int topk);
 hipError_t launch_index_rows_bf16(const IndexRowsArgs& a, hipStream_t stream);
