@@ -1,0 +1,81 @@
+"""The forward entry points inside a captured HIP graph: the library launches kernels
+only (no allocation, no memset, no host synchronisation), so a serving loop can
+capture a decode or prefill step and replay it.  Each replay must reproduce the
+eager result bit for bit, with eager work and synchronisations between replays."""
+
+import math
+
+import pytest
+import torch
+
+from softmax_learnable_sink_amd import synth
+from tests.gpu_util import dev_tensor, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _replay_and_compare(capture_fn, outputs, eager_fn, replays=3):
+    # eager reference (also the warm-up before capture)
+    ref = [t.clone() for t in eager_fn()]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        capture_fn()
+    for r in range(replays):
+        for t in outputs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outputs, ref):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want), \
+                f"replay {r} differs from the eager result"
+        eager_fn()  # eager work between replays
+        torch.cuda.synchronize()
+    say(f"  {replays} replays equal the eager result bitwise")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,lo,hi,window", [
+    (130, 16, 8, 64, 100, 2100, None),       # many KV-head units: equal token ranges
+    (3, 32, 8, 128, 9000, 12000, (1024, 2048)),  # few: chunks, with the first/last window
+])
+def test_paged_decode_replays_in_a_graph(B, Hq, Hkv, D, lo, hi, window):
+    need_gpu()
+    from softmax_learnable_sink_amd import binding
+    say(f"case: graph decode B{B} H{Hq}/{Hkv} D{D} L~U[{lo},{hi}] window={window}")
+    c = synth.decode_case(B, Hq, Hkv, D, 16, lo, hi, seed=5)
+    q, kc, vc = (dev_tensor(c[n], synth.BF16) for n in ("q", "k_cache", "v_cache"))
+    bt = torch.from_numpy(c["block_table"]).cuda()
+    sl = torch.from_numpy(c["seqlens"]).cuda()
+    sink = torch.from_numpy(c["sink"]).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = binding.lib().attn_sink_decode_workspace_bytes(B, Hq, Hkv, D, 16, bt.shape[1],
+                                                         *binding._window(window), 0)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    scale = 1 / math.sqrt(D)
+
+    def run(out, l, w):
+        return binding.attn_sink_fwd_decode_paged(q, kc, vc, bt, sl, sink, softmax_scale=scale,
+                                                  window=window, out=out, lse=l, workspace=w)
+
+    o2, lse2, ws2 = torch.empty_like(o), torch.empty_like(lse), torch.empty_like(ws)
+    _replay_and_compare(lambda: run(o, lse, ws), [o, lse], lambda: run(o2, lse2, ws2))
+
+
+def test_prefill_replays_in_a_graph():
+    need_gpu()
+    from softmax_learnable_sink_amd import binding
+    say("case: graph prefill B2 S700 H16/2 D64 causal")
+    c = synth.prefill_case(2, 700, 700, 16, 2, 64, seed=6)
+    q, k, v = (dev_tensor(c[n], synth.BF16) for n in ("q", "k", "v"))
+    sink = torch.from_numpy(c["sink"]).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((2, 16, 700), dtype=torch.float32, device=q.device)
+
+    def run(out, l):
+        return binding.attn_sink_fwd_prefill(q, k, v, sink, causal=True, softmax_scale=0.125,
+                                             out=out, lse=l)
+
+    o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+    _replay_and_compare(lambda: run(o, lse), [o, lse], lambda: run(o2, lse2))
