@@ -79,3 +79,28 @@ def test_prefill_replays_in_a_graph():
 
     o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
     _replay_and_compare(lambda: run(o, lse), [o, lse], lambda: run(o2, lse2))
+
+
+def test_backward_replays_in_a_graph():
+    """The training backward (preprocess, one launch of dK/dV and dQ, dSink reduction)."""
+    need_gpu()
+    from softmax_learnable_sink_amd import binding
+    say("case: graph backward B1 S600 H16/2 D64 causal")
+    c = synth.prefill_case(1, 600, 600, 16, 2, 64, seed=7, dout=True)
+    q, k, v, do = (dev_tensor(c[n], synth.BF16) for n in ("q", "k", "v", "dout"))
+    sink = torch.from_numpy(c["sink"]).cuda()
+    o, lse = binding.attn_sink_fwd_prefill(q, k, v, sink, causal=True, softmax_scale=0.125)
+    need = binding.lib().attn_sink_bwd_workspace_bytes(1, 600, 600, 16, 2, 64)
+
+    def buffers():
+        return (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                torch.empty_like(sink), torch.empty(max(need, 16), dtype=torch.uint8,
+                                                    device=q.device))
+
+    def run(bufs):
+        dq, dk, dv, ds, ws = bufs
+        return binding.attn_sink_bwd(q, k, v, o, do, lse, sink, causal=True, softmax_scale=0.125,
+                                     dq=dq, dk=dk, dv=dv, dsink=ds, workspace=ws)
+
+    cap, eager = buffers(), buffers()
+    _replay_and_compare(lambda: run(cap), list(cap[:4]), lambda: run(eager))
