@@ -96,3 +96,24 @@ def poison_unselected(case, window):
 
 def env_flag(name):
     return os.environ.get(name, "") not in ("", "0")
+
+
+def oracle_map(fn, items):
+    """Run fn over items on a thread pool, one BLAS thread each: the oracle's
+    elementwise NumPy work releases the GIL, so independent (sequence,
+    KV-head group) sub-problems of a full-size workload run side by side.
+    Results come back in the order of items."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(items)))
+    with threadpool_limits(limits=1):
+        with ThreadPoolExecutor(workers) as ex:
+            return list(ex.map(fn, items))
+
+
+def grad_ratio(got, ref):
+    """max |got - ref| / (3e-2 (1 + |ref|)) -- at most 1 within the bound."""
+    if got.size == 0:
+        return 0.0
+    return float(np.max(np.abs(got - ref) / (TOL_GRAD * (1.0 + np.abs(ref)))))

@@ -107,7 +107,10 @@ def test_config5_full_size_sampled():
                             case["sink"][h:h + 1],
                             vals(case["dout"][b:b + 1, i:i + 1, h:h + 1], synth.BF16), scale, True)
         check_grad(f"dQ[b{b} row{i} h{h}]", dq[b, i, h], r[0][0, 0, 0])
-    # dSink of heads 0 and 37: every row of both sequences
+    # dSink of heads 0 and 37: every row of both sequences; the bound is the
+    # max-norm relative one over these two heads, normalised by the oracle alone
+    # (every head at full size: tests/test_gpu_fullsize.py)
+    ref = {}
     for h in (0, 37):
         kh = h // g
         r = oracle.backward(vals(case["q"][:, :, h:h + 1], synth.BF16),
@@ -115,6 +118,8 @@ def test_config5_full_size_sampled():
                             vals(case["v"][:, :, kh:kh + 1], synth.BF16),
                             case["sink"][h:h + 1], vals(case["dout"][:, :, h:h + 1], synth.BF16),
                             scale, True)
-        err = abs(ds[h] - r[3][0])
-        say(f"  dSink[{h}] gpu {ds[h]:.6f} oracle {r[3][0]:.6f} abs err {err:.3e}")
-        assert err <= TOL_DSINK_REL * max(abs(r[3][0]), float(np.max(np.abs(ds))))
+        ref[h] = r[3][0]
+        say(f"  dSink[{h}] gpu {ds[h]:.6f} oracle {ref[h]:.6f} abs err {abs(ds[h] - ref[h]):.3e}")
+    norm = max(abs(x) for x in ref.values())
+    for h, x in ref.items():
+        assert abs(ds[h] - x) <= TOL_DSINK_REL * norm
