@@ -38,9 +38,13 @@
  *   - All tensor pointers are DEVICE pointers to contiguous row-major
  *     tensors, 16-byte aligned.  Shapes are given with each function.
  *   - The caller allocates and owns every buffer, including workspaces.  The
- *     library allocates no device memory, keeps no state other than a
- *     thread-local error message, and never synchronises: work is enqueued on
- *     `hip_stream` (a hipStream_t; NULL = the default stream).
+ *     library never synchronises: work is enqueued on `hip_stream` (a
+ *     hipStream_t; NULL = the default stream).  It allocates no device memory
+ *     at run time.  Its state: a thread-local error message; per device, the
+ *     number of paged-decode workgroups resident at once (queried from HIP on
+ *     the first decode call with equal token ranges, then reused); and, for
+ *     attn_sink_fwd_decode_paged_noalloc only, a fixed device array per device
+ *     (below).
  *   - Outputs are overwritten (never accumulated into) and must not alias
  *     inputs.  Inputs are never written.
  *   - Every argument is validated on the host BEFORE any HIP call.  On error
@@ -259,6 +263,31 @@ int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v
 size_t attn_sink_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int page_size,
                                         int max_pages_per_seq, int window_first,
                                         int window_last, int num_splits);
+
+/*
+ * attn_sink_fwd_decode_paged without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Arguments, results and errors are
+ * those of attn_sink_fwd_decode_paged; the split partials go to a device array
+ * that the library holds, one per device (allocated when the library's code
+ * is loaded on that device, held until the process ends), of
+ * ATTN_SINK_DECODE_SCRATCH_BYTES bytes.  A call whose
+ * attn_sink_decode_workspace_bytes() exceeds that returns
+ * ATTN_SINK_ERR_UNSUPPORTED before any HIP call.  The first call on a device
+ * looks the array's device address up (hipGetSymbolAddress, with that device
+ * current); no call allocates or frees memory.  Every call on one device
+ * shares that device's array: calls that overlap on one device (on different
+ * streams, or from several threads) race and give wrong results; calls
+ * ordered on one stream do not.
+ */
+#define ATTN_SINK_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_sink_fwd_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_table, const int32_t* seqlens_k,
+                                       const float* sink, void* o, float* lse, int B, int Hq,
+                                       int Hkv, int D, int page_size, int max_pages_per_seq,
+                                       int num_pages, float softmax_scale, int window_first,
+                                       int window_last, int num_splits, int dtype,
+                                       void* hip_stream);
 
 /*
  * Backward of the forward prefill (bf16).  Gradients of sum(dO * O):

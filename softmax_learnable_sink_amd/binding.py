@@ -29,6 +29,7 @@ _SIGNATURES = {
     "attn_sink_last_error": ([], ctypes.c_char_p),
     "attn_sink_fwd_prefill": ([_vp, _vp, _vp, _vp, _vp, _vp] + [_i] * 6 + [_f, _i, _i, _i, _i, _vp], _i),
     "attn_sink_fwd_decode_paged": ([_vp] * 8 + [_i] * 7 + [_f, _i, _i, _i, _vp, _sz, _i, _vp], _i),
+    "attn_sink_fwd_decode_paged_noalloc": ([_vp] * 8 + [_i] * 7 + [_f, _i, _i, _i, _i, _vp], _i),
     "attn_sink_fwd_extend_paged": ([_vp] * 9 + [_i] * 9 + [_f, _i, _i, _i, _vp], _i),
     "attn_sink_fwd_varlen": ([_vp] * 8 + [_i] * 7 + [_f, _i, _i, _i, _i, _vp], _i),
     "attn_sink_fwd_index_paged": ([_vp] * 11 + [_i] * 11 + [_f, _i, _vp], _i),
@@ -188,6 +189,43 @@ def attn_sink_fwd_decode_paged(q, k_cache, v_cache, block_table, seqlens_k, sink
         _ptr(out), _ptr(lse), B, Hq, Hkv, D, page_size, max_pages, num_pages, scale, w1, w2,
         num_splits, _ptr(workspace), workspace.numel() * workspace.element_size(), BF16,
         _stream(dev)))
+    return out, lse
+
+
+DECODE_SCRATCH_BYTES = 32 << 20  # ATTN_SINK_DECODE_SCRATCH_BYTES
+
+
+def attn_sink_fwd_decode_paged_noalloc(q, k_cache, v_cache, block_table, seqlens_k, sink=None,
+                                       softmax_scale=None, window=None, num_splits=0, out=None,
+                                       lse=None):
+    """attn_sink_fwd_decode_paged on the library's own scratch: with `out` (and `lse`, if
+    wanted) given, nothing is allocated on the device."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(seqlens_k, "seqlens_k", torch.int32, dev)
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (num_pages, page_size, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [num_pages, page_size, Hkv, D]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seqlens_k.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seqlens_k [B]")
+    max_pages = block_table.shape[1]
+    if sink is not None:
+        _need(sink, "sink", torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    w1, w2 = _window(window)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    _check(lib().attn_sink_fwd_decode_paged_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seqlens_k), _ptr(sink),
+        _ptr(out), _ptr(lse), B, Hq, Hkv, D, page_size, max_pages, num_pages, scale, w1, w2,
+        num_splits, BF16, _stream(dev)))
     return out, lse
 
 

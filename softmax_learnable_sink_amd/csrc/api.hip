@@ -322,13 +322,15 @@ size_t attn_sink_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int page_
       .workspace_bytes;
 }
 
-int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                               const int32_t* block_table, const int32_t* seqlens_k,
-                               const float* sink, void* o, float* lse, int B, int Hq, int Hkv,
-                               int D, int page_size, int max_pages_per_seq, int num_pages,
-                               float softmax_scale, int window_first, int window_last,
-                               int num_splits, void* workspace, size_t workspace_bytes, int dtype,
-                               void* hip_stream) {
+}  // extern "C"
+
+// Validation shared by the two paged-decode entry points; fills the plan.
+static int check_decode_call(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seqlens_k,
+                             const float* sink, const void* o, const float* lse, int B, int Hq,
+                             int Hkv, int D, int page_size, int max_pages_per_seq, int num_pages,
+                             float softmax_scale, int window_first, int window_last,
+                             int num_splits, int dtype, DecodePlan* plan) {
   REQUIRE(dtype == ATTN_SINK_BF16, ATTN_SINK_ERR_UNSUPPORTED,
           "paged decode supports bf16 only (dtype %d)", dtype);
   if (int r = check_decode_common(B, Hq, Hkv, D, page_size, max_pages_per_seq, window_first,
@@ -344,12 +346,29 @@ int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v
           ATTN_SINK_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
   REQUIRE(aligned4(block_table) && aligned4(seqlens_k) && aligned4(sink) && aligned4(lse),
           ATTN_SINK_ERR_INVALID_ARG, "block_table, seqlens_k, sink and lse must be 4-byte aligned");
-  const DecodePlan plan = plan_decode(B, Hq, Hkv, D, page_size, max_pages_per_seq, window_first,
-                                      window_last, num_splits);
-  REQUIRE(B <= kMaxGridYZ && plan.max_splits <= kMaxGridYZ, ATTN_SINK_ERR_UNSUPPORTED,
-          "B (%d) and the split count (%d) must each be <= %lld", B, plan.max_splits, kMaxGridYZ);
-  REQUIRE(fits_int32((long long)B * plan.max_splits * ((Hkv * ((Hq / Hkv + 15) / 16) + 3) / 4)),
+  *plan = plan_decode(B, Hq, Hkv, D, page_size, max_pages_per_seq, window_first, window_last,
+                      num_splits);
+  REQUIRE(B <= kMaxGridYZ && plan->max_splits <= kMaxGridYZ, ATTN_SINK_ERR_UNSUPPORTED,
+          "B (%d) and the split count (%d) must each be <= %lld", B, plan->max_splits, kMaxGridYZ);
+  REQUIRE(fits_int32((long long)B * plan->max_splits * ((Hkv * ((Hq / Hkv + 15) / 16) + 3) / 4)),
           ATTN_SINK_ERR_UNSUPPORTED, "B * splits * KV-head units exceeds 2^31 - 1 workgroups");
+  return ATTN_SINK_OK;
+}
+
+extern "C" {
+
+int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* seqlens_k,
+                               const float* sink, void* o, float* lse, int B, int Hq, int Hkv,
+                               int D, int page_size, int max_pages_per_seq, int num_pages,
+                               float softmax_scale, int window_first, int window_last,
+                               int num_splits, void* workspace, size_t workspace_bytes, int dtype,
+                               void* hip_stream) {
+  DecodePlan plan{};
+  if (int r = check_decode_call(q, k_cache, v_cache, block_table, seqlens_k, sink, o, lse, B, Hq,
+                                Hkv, D, page_size, max_pages_per_seq, num_pages, softmax_scale,
+                                window_first, window_last, num_splits, dtype, &plan))
+    return r;
   REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
           "a 16-byte aligned workspace of %zu bytes is required", plan.workspace_bytes);
   REQUIRE(workspace_bytes >= plan.workspace_bytes, ATTN_SINK_ERR_WORKSPACE,
@@ -360,6 +379,32 @@ int attn_sink_fwd_decode_paged(const void* q, const void* k_cache, const void* v
                plan.chunk, plan.max_splits, static_cast<float*>(workspace), plan.even};
   return hip_status(launch_decode_bf16(a, static_cast<hipStream_t>(hip_stream)),
                     "attn_sink_fwd_decode_paged launch");
+}
+
+int attn_sink_fwd_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_table, const int32_t* seqlens_k,
+                                       const float* sink, void* o, float* lse, int B, int Hq,
+                                       int Hkv, int D, int page_size, int max_pages_per_seq,
+                                       int num_pages, float softmax_scale, int window_first,
+                                       int window_last, int num_splits, int dtype,
+                                       void* hip_stream) {
+  DecodePlan plan{};
+  if (int r = check_decode_call(q, k_cache, v_cache, block_table, seqlens_k, sink, o, lse, B, Hq,
+                                Hkv, D, page_size, max_pages_per_seq, num_pages, softmax_scale,
+                                window_first, window_last, num_splits, dtype, &plan))
+    return r;
+  REQUIRE(plan.workspace_bytes <= kDecodeScratchBytes, ATTN_SINK_ERR_UNSUPPORTED,
+          "this decode needs %zu bytes of scratch; the library's scratch holds %zu (use "
+          "attn_sink_fwd_decode_paged with a workspace)",
+          plan.workspace_bytes, kDecodeScratchBytes);
+  float* ws = nullptr;
+  if (int r = hip_status(decode_scratch(&ws), "attn_sink_fwd_decode_paged_noalloc scratch"))
+    return r;
+  DecodeArgs a{q, k_cache, v_cache, block_table, seqlens_k, sink, o, lse, B, Hq, Hkv, D,
+               page_size, max_pages_per_seq, num_pages, softmax_scale, window_first, window_last,
+               plan.chunk, plan.max_splits, ws, plan.even};
+  return hip_status(launch_decode_bf16(a, static_cast<hipStream_t>(hip_stream)),
+                    "attn_sink_fwd_decode_paged_noalloc launch");
 }
 
 size_t attn_sink_bwd_workspace_bytes(int B, int Sq, int Sk, int Hq, int Hkv, int D) {

@@ -26,6 +26,7 @@
 #include <algorithm>
 #include <atomic>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -777,6 +778,43 @@ int even_capacity() {
   return c;
 }
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Library-held scratch of attn_sink_fwd_decode_paged_noalloc, for callers that
+// cannot allocate: the split partials and their bookkeeping of one call (the
+// workspace of attn_sink_fwd_decode_paged).  Each device that runs the entry
+// point holds its own copy until the process ends; host code reaches it only
+// through the device address hipGetSymbolAddress returns for that device.
+// ---------------------------------------------------------------------------
+namespace {
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t decode_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // once per device, with that device current
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      p = static_cast<float*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   const int g = a.Hq / a.Hkv;

@@ -102,6 +102,11 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_pag
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// Size of the library-held decode scratch (one copy per device) and this
+// device's address of it, looked up on the first call per device.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;  // ATTN_SINK_DECODE_SCRATCH_BYTES
+hipError_t decode_scratch(float** ptr);
+
 // Per-query index lists: packed query rows against a paged cache, row r
 // attending to the tokens of kv_index row r (topk entries) at or before its
 // position.  Runs the paged-decode kernels with the rows as their sequences.

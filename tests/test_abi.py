@@ -39,7 +39,7 @@ def test_header_declares_expected_entry_points():
               "attn_sink_fwd_index_rows_paged", "attn_sink_index_rows_workspace_bytes",
               "attn_sink_decode_workspace_bytes", "attn_sink_bwd_workspace_bytes",
               "attn_sink_decode_select_slots", "attn_sink_gather_kv", "attn_sink_last_error",
-              "attn_sink_abi_version"):
+              "attn_sink_abi_version", "attn_sink_fwd_decode_paged_noalloc"):
         assert n in names
 
 
@@ -115,6 +115,48 @@ def _decode(lib, **kw):
 def test_decode_rejects(lib, kw, status, msg):
     assert _decode(lib, **kw) == status
     assert msg in binding.last_error()
+
+
+def _decode_noalloc(lib, **kw):
+    a = dict(B=2, Hq=8, Hkv=2, D=64, P=16, maxp=4, npages=8, scale=0.125, w1=-1, w2=-1, ns=0,
+             dtype=binding.BF16, q=P, bt=P, sl=P, o=P)
+    a.update(kw)
+    return lib.attn_sink_fwd_decode_paged_noalloc(
+        a["q"], P, P, a["bt"], a["sl"], None, a["o"], None, a["B"], a["Hq"], a["Hkv"], a["D"],
+        a["P"], a["maxp"], a["npages"], a["scale"], a["w1"], a["w2"], a["ns"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(P=12), binding.ERR_UNSUPPORTED, "power of two"),
+    (dict(D=32), binding.ERR_UNSUPPORTED, "64 or 128"),
+    (dict(Hq=9), binding.ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(npages=0), binding.ERR_INVALID_ARG, "num_pages"),
+    (dict(ns=-1), binding.ERR_INVALID_ARG, "num_splits"),
+    (dict(o=None), binding.ERR_INVALID_ARG, "must not be NULL"),
+    (dict(q=P_ODD), binding.ERR_INVALID_ARG, "16-byte aligned"),
+    (dict(dtype=binding.F32), binding.ERR_UNSUPPORTED, "bf16"),
+    (dict(w1=3, w2=-1), binding.ERR_INVALID_ARG, "window"),
+    (dict(scale=float("nan")), binding.ERR_INVALID_ARG, "softmax_scale"),
+    # equal token ranges over 256 sequences at D 128 need 64 * 1280 * 130 * 4 B > 32 MiB
+    (dict(B=256, Hq=64, Hkv=8, D=128, maxp=2048, npages=1 << 16), binding.ERR_UNSUPPORTED,
+     "scratch"),
+])
+def test_decode_noalloc_rejects(lib, kw, status, msg):
+    assert _decode_noalloc(lib, **kw) == status
+    assert msg in binding.last_error()
+
+
+def test_decode_noalloc_scratch_limit(lib):
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_SINK_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.DECODE_SCRATCH_BYTES
+    # the benchmark's decode workloads fit the scratch
+    assert 0 < binding.attn_sink_decode_workspace_bytes(64, 64, 8, 64, 16, 2048) <= \
+        binding.DECODE_SCRATCH_BYTES
+    assert 0 < binding.attn_sink_decode_workspace_bytes(32, 32, 8, 128, 16, 4096, (1024, 7168)) <= \
+        binding.DECODE_SCRATCH_BYTES
+    assert binding.attn_sink_decode_workspace_bytes(256, 64, 8, 128, 16, 2048) > \
+        binding.DECODE_SCRATCH_BYTES
 
 
 def test_decode_workspace_query(lib):
