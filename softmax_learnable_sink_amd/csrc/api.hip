@@ -78,6 +78,9 @@ bool fits_int32(long long x) { return x >= 0 && x <= INT_MAX; }
 // resource addresses (the kernels address a batch's K/V or Q/dO slice through one).
 constexpr long long kMaxGridYZ = 65535;
 constexpr long long kMaxSlice = 0xffffffffLL;
+constexpr const char* kGridMsg =
+    "the problem is too large for one launch (a grid's work-items must fit 32 bits and its "
+    "y/z extents 65535)";
 
 }  // namespace
 
@@ -113,6 +116,9 @@ int attn_sink_fwd_prefill(const void* q, const void* k, const void* v, const flo
           B);
   REQUIRE(dtype != ATTN_SINK_BF16 || (long long)Sk * Hkv * D * 2 <= kMaxSlice,
           ATTN_SINK_ERR_UNSUPPORTED, "one batch's K or V slice exceeds 4 GiB");
+  REQUIRE(dtype == ATTN_SINK_BF16 ? dispatch_fits(fwd_workgroups(B, Sq, Hq, Hkv, D), 256)
+                                  : Hq <= kMaxGridYZ,
+          ATTN_SINK_ERR_UNSUPPORTED, "%s", kGridMsg);
   PrefillArgs a{q, k, v, sink, o, lse, B, Sq, Sk, Hq, Hkv, D, softmax_scale, causal,
                 window_first, window_last};
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -153,6 +159,8 @@ int attn_sink_fwd_extend_paged(const void* q, const void* k_cache, const void* v
               aligned4(sink) && aligned4(lse),
           ATTN_SINK_ERR_INVALID_ARG,
           "block_table, cu_seqlens_q, seqlens_k, sink and lse must be 4-byte aligned");
+  REQUIRE(dispatch_fits(fwd_workgroups(B, max_seqlen_q, Hq, Hkv, D), 256),
+          ATTN_SINK_ERR_UNSUPPORTED, "%s", kGridMsg);
   if (total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;  // nothing to compute
   ExtendArgs a{q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, nullptr, sink, o, lse,
                B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages_per_seq,
@@ -201,6 +209,8 @@ int attn_sink_fwd_index_paged(const void* q, const void* k_cache, const void* v_
   REQUIRE(aligned4(block_table) && aligned4(cu_seqlens_q) && aligned4(seqlens_k) &&
               aligned4(kv_index) && aligned4(cu_blocks) && aligned4(sink) && aligned4(lse),
           ATTN_SINK_ERR_INVALID_ARG, "int32 and fp32 arrays must be 4-byte aligned");
+  REQUIRE(dispatch_fits(index_workgroups(B, max_seqlen_q, Hq, Hkv, D), 256),
+          ATTN_SINK_ERR_UNSUPPORTED, "%s", kGridMsg);
   if (total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;  // nothing to compute
   IndexArgs a{q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, kv_index, cu_blocks,
               sink, o, lse, B, total_q, max_seqlen_q, Hq, Hkv, D, page_size, max_pages_per_seq,
@@ -248,8 +258,10 @@ int attn_sink_fwd_index_rows_paged(const void* q, const void* k_cache, const voi
           ATTN_SINK_ERR_INVALID_ARG, "int32 and fp32 arrays must be 4-byte aligned");
   if (total_q == 0) return ATTN_SINK_OK;  // nothing to compute
   const DecodePlan plan = plan_index_rows(total_q, Hq, Hkv, D, topk);
-  REQUIRE(fits_int32((long long)total_q * plan.max_splits * ((Hkv * ((Hq / Hkv + 15) / 16) + 1) / 2)),
-          ATTN_SINK_ERR_UNSUPPORTED, "rows * splits * KV-head units exceeds 2^31 - 1 workgroups");
+  REQUIRE(dispatch_fits((long long)total_q * plan.max_splits * (Hkv * ((Hq / Hkv + 15) / 16) + 3),
+                        64) &&
+              dispatch_fits(((long long)total_q * Hq + 3) / 4, 256),
+          ATTN_SINK_ERR_UNSUPPORTED, "%s", kGridMsg);
   REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
           "a 16-byte aligned workspace of %zu bytes is required", plan.workspace_bytes);
   REQUIRE(workspace_bytes >= plan.workspace_bytes, ATTN_SINK_ERR_WORKSPACE,
@@ -290,6 +302,8 @@ int attn_sink_fwd_varlen(const void* q, const void* k, const void* v, const int3
   REQUIRE(aligned4(cu_seqlens_q) && aligned4(cu_seqlens_k) && aligned4(sink) && aligned4(lse),
           ATTN_SINK_ERR_INVALID_ARG,
           "cu_seqlens_q, cu_seqlens_k, sink and lse must be 4-byte aligned");
+  REQUIRE(dispatch_fits(fwd_workgroups(B, max_seqlen_q, Hq, Hkv, D), 256),
+          ATTN_SINK_ERR_UNSUPPORTED, "%s", kGridMsg);
   if (total_q == 0 || max_seqlen_q == 0) return ATTN_SINK_OK;  // nothing to compute
   ExtendArgs a{q, k, v, nullptr, cu_seqlens_q, nullptr, cu_seqlens_k, sink, o, lse, B, total_q,
                max_seqlen_q, Hq, Hkv, D, 1, 0, softmax_scale, causal, window_first, window_last,
@@ -350,8 +364,13 @@ static int check_decode_call(const void* q, const void* k_cache, const void* v_c
                       num_splits);
   REQUIRE(B <= kMaxGridYZ && plan->max_splits <= kMaxGridYZ, ATTN_SINK_ERR_UNSUPPORTED,
           "B (%d) and the split count (%d) must each be <= %lld", B, plan->max_splits, kMaxGridYZ);
-  REQUIRE(fits_int32((long long)B * plan->max_splits * ((Hkv * ((Hq / Hkv + 15) / 16) + 3) / 4)),
-          ATTN_SINK_ERR_UNSUPPORTED, "B * splits * KV-head units exceeds 2^31 - 1 workgroups");
+  // chunk grid: ceil(units / NW) workgroups of 64 * NW threads per slot (NW 2 or 4); the
+  // equal-range grid is at most 1024 workgroups per column of 4 units
+  REQUIRE(dispatch_fits((long long)B * plan->max_splits * (Hkv * ((Hq / Hkv + 15) / 16) + 3), 64) &&
+              dispatch_fits((long long)kDecodeEvenMaxG *
+                                ((Hkv * ((Hq / Hkv + 15) / 16) + 3) / 4), 256) &&
+              dispatch_fits(((long long)B * Hq + 3) / 4, 256),
+          ATTN_SINK_ERR_UNSUPPORTED, "%s", kGridMsg);
   return ATTN_SINK_OK;
 }
 
@@ -446,6 +465,10 @@ int attn_sink_bwd(const void* q, const void* k, const void* v, const void* o, co
           "B (%d) and ceil(Sk / 128) (%d) must each be <= %lld", B, (Sk + 127) / 128, kMaxGridYZ);
   REQUIRE((long long)Sk * Hkv * D * 2 <= kMaxSlice && (long long)Sq * Hq * D * 2 <= kMaxSlice,
           ATTN_SINK_ERR_UNSUPPORTED, "one batch's K/V or Q/dO slice exceeds 4 GiB");
+  REQUIRE(Hq <= kMaxGridYZ &&
+              dispatch_fits(bwd_dkdv_workgroups(B, Sk, Hkv) + bwd_dq_workgroups(B, Sq, Hq, Hkv),
+                            256),
+          ATTN_SINK_ERR_UNSUPPORTED, "%s", kGridMsg);
   const size_t need = backward_workspace_bytes(B, Sq, Hq, (size_t)B * Sq);
   REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
           "a 16-byte aligned workspace of %zu bytes is required", need);
@@ -495,6 +518,11 @@ int attn_sink_bwd_varlen(const void* q, const void* k, const void* v, const void
   REQUIRE((long long)max_seqlen_k * Hkv * D * 2 <= kMaxSlice &&
               (long long)max_seqlen_q * Hq * D * 2 <= kMaxSlice,
           ATTN_SINK_ERR_UNSUPPORTED, "one sequence's K/V or Q/dO slice exceeds 4 GiB");
+  REQUIRE(Hq <= kMaxGridYZ &&
+              dispatch_fits(bwd_dkdv_workgroups(B, max_seqlen_k, Hkv) +
+                                bwd_dq_workgroups(B, max_seqlen_q, Hq, Hkv),
+                            256),
+          ATTN_SINK_ERR_UNSUPPORTED, "%s", kGridMsg);
   const size_t need = backward_workspace_bytes(B, max_seqlen_q, Hq, (size_t)total_q);
   REQUIRE(workspace && aligned16(workspace), ATTN_SINK_ERR_WORKSPACE,
           "a 16-byte aligned workspace of %zu bytes is required", need);
@@ -521,6 +549,7 @@ int attn_sink_decode_select_slots(const int32_t* block_table, const int32_t* seq
   REQUIRE(aligned4(block_table) && aligned4(seqlens_k) && aligned4(counts) &&
               (reinterpret_cast<uintptr_t>(slots) & 7u) == 0,
           ATTN_SINK_ERR_INVALID_ARG, "misaligned pointer");
+  REQUIRE(dispatch_fits(B, 256), ATTN_SINK_ERR_UNSUPPORTED, "%s", kGridMsg);
   return hip_status(launch_select_slots(block_table, seqlens_k, B, max_pages_per_seq, page_size,
                                         window_first, window_last, slots, counts, max_sel,
                                         static_cast<hipStream_t>(hip_stream)),
@@ -543,6 +572,8 @@ int attn_sink_gather_kv(const void* k_cache, const void* v_cache, const int32_t*
   REQUIRE(aligned4(block_table) && aligned4(seqlens_k) && aligned4(k_cache) && aligned4(v_cache) &&
               aligned4(k_out) && aligned4(v_out),
           ATTN_SINK_ERR_INVALID_ARG, "misaligned pointer");
+  REQUIRE(dispatch_fits(max_sel, 256) && B <= kMaxGridYZ, ATTN_SINK_ERR_UNSUPPORTED, "%s",
+          kGridMsg);
   return hip_status(launch_gather_kv(k_cache, v_cache, block_table, seqlens_k, B, Hkv, D,
                                      page_size, max_pages_per_seq, window_first, window_last,
                                      k_out, v_out, max_sel, dtype == ATTN_SINK_BF16 ? 2 : 4,

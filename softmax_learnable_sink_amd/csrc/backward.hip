@@ -139,8 +139,11 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
     const size_t x = sr.l0 + h * sr.lh + row;
     di[x] = acc;
     if (sink) {
+      // a head whose sink is -inf contributes nothing, also on rows that see
+      // no key (LSE = -inf there, and -inf - -inf would be NaN)
+      const float sh = sink[h];
       const float L = lse[x];
-      contrib = -exp2_fast((sink[h] - L) * kLog2e) * acc;
+      contrib = sh == kNegInf ? 0.f : -exp2_fast((sh - L) * kLog2e) * acc;
     }
   }
   if (!sink) return;
@@ -630,7 +633,7 @@ size_t backward_workspace_bytes(int B, int max_sq, int Hq, size_t rows) {
 // and rows come from the cu arrays.  Grids that would be empty are skipped.
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
   const int g = a.Hq / a.Hkv;
-  const int hpw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
+  const int hpw = heads_per_wg(g);
   const float sl2 = a.scale * kLog2e;
   const int nblk = (a.Sq + 63) / 64;
   const size_t rows = a.cu_seqlens_q ? (size_t)a.total_q : (size_t)a.B * a.Sq;
@@ -649,8 +652,7 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
   const int tq = a.total_q;
   const dim3 pgrid(nblk, a.Hq, a.B);
   const dim3 kgrid(a.Hkv, a.B, (a.Sk + 127) / 128);
-  const int R = 32 * (4 / hpw);
-  const dim3 qgrid(a.B * a.Hkv * (g / hpw) * ((a.Sq + R - 1) / R));
+  const dim3 qgrid((unsigned)bwd_dq_workgroups(a.B, a.Sq, a.Hq, a.Hkv));
   const bool rows_q = a.Sq > 0, rows_k = a.Sk > 0;
   if (a.D == 64) {
     if (rows_q)

@@ -278,7 +278,7 @@ enum : int {
 // holds tokens.  Workgroup 0 also writes the sequences' first concatenated
 // token (starts[b], starts[B] = T) for the combine.
 constexpr int kEvenMinTokens = 64;
-constexpr int kEvenMaxG = 1024;  // workgroups per column the workspace has room for
+constexpr int kEvenMaxG = kDecodeEvenMaxG;  // workgroups per column the workspace has room for
 struct EvenArgs {
   int G;
   int pstride;

@@ -9,6 +9,37 @@
 
 namespace attn_sink {
 
+// ---------------------------------------------------------------------------
+// Grid sizes of the launches that grow with the problem, shared by the
+// launchers and the C ABI's size checks.  A dispatch's work-item count (per
+// grid dimension) must fit 32 bits.
+// ---------------------------------------------------------------------------
+// Query heads per wave group of the forward and dQ workgroups (4 waves).
+inline int heads_per_wg(int g) { return (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1); }
+// Forward prefill / extend / variable-length workgroups over `rows` rows.
+inline long long fwd_workgroups(int B, int rows, int Hq, int Hkv, int D) {
+  const int g = Hq / Hkv, hpw = heads_per_wg(g);
+  const long long R = (long long)(D == 64 ? 64 : 32) * (4 / hpw);
+  return (long long)B * Hkv * (g / hpw) * ((rows + R - 1) / R);
+}
+// Index-list workgroups (4 query heads per workgroup, 32*QB rows).
+inline long long index_workgroups(int B, int rows, int Hq, int Hkv, int D) {
+  const long long R = D == 64 ? 64 : 32;
+  return (long long)B * Hkv * (Hq / Hkv / 4) * ((rows + R - 1) / R);
+}
+// Backward dQ and dK/dV workgroups.
+inline long long bwd_dq_workgroups(int B, int Sq, int Hq, int Hkv) {
+  const int g = Hq / Hkv, hpw = heads_per_wg(g);
+  const long long R = 32LL * (4 / hpw);
+  return (long long)B * Hkv * (g / hpw) * ((Sq + R - 1) / R);
+}
+inline long long bwd_dkdv_workgroups(int B, int Sk, int Hkv) {
+  return (long long)Hkv * B * ((Sk + 127) / 128);
+}
+inline bool dispatch_fits(long long workgroups, int threads) {
+  return workgroups >= 0 && workgroups * threads <= 0xffffffffLL;
+}
+
 struct PrefillArgs {
   const void* q;
   const void* k;
@@ -68,6 +99,10 @@ struct IndexArgs {
 };
 
 hipError_t launch_index_bf16(const IndexArgs& a, hipStream_t stream);
+
+// Workgroups per column of 4 KV-head units in the equal-range decode grid (the
+// workspace has room for this many partials per head and sequence).
+constexpr int kDecodeEvenMaxG = 1024;
 
 struct DecodeArgs {
   const void* q;

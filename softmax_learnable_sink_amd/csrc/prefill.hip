@@ -836,23 +836,19 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   const int g = a.Hq / a.Hkv;
-  const int hpw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
+  const int hpw = heads_per_wg(g);
   const float sl2 = a.scale * kLog2e;
   const dim3 block(kThreads);
   const auto* q = static_cast<const __bf16*>(a.q);
   const auto* k = static_cast<const __bf16*>(a.k);
   const auto* v = static_cast<const __bf16*>(a.v);
   auto* o = static_cast<__bf16*>(a.o);
-  const int cols = a.B * a.Hkv * (g / hpw);
+  const dim3 grid((unsigned)fwd_workgroups(a.B, a.Sq, a.Hq, a.Hkv, a.D));
   if (a.D == 64) {
-    const int R = 64 * (4 / hpw);
-    const dim3 grid(cols * ((a.Sq + R - 1) / R));
     prefill_bf16_kernel<64, 2><<<grid, block, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.B, a.Sq,
                                                            a.Sk, a.Hq, a.Hkv, hpw, sl2, a.causal,
                                                            a.w1, a.w2);
   } else {
-    const int R = 32 * (4 / hpw);
-    const dim3 grid(cols * ((a.Sq + R - 1) / R));
     prefill_bf16_kernel<128, 1><<<grid, block, 0, stream>>>(q, k, v, a.sink, o, a.lse, a.B,
                                                             a.Sq, a.Sk, a.Hq, a.Hkv, hpw, sl2,
                                                             a.causal, a.w1, a.w2);
@@ -862,7 +858,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream) {
   const int g = a.Hq / a.Hkv;
-  const int hpw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
+  const int hpw = heads_per_wg(g);
   const float sl2 = a.scale * kLog2e;
   int shift = 0;
   while ((1 << shift) < a.page_size) ++shift;
@@ -870,7 +866,6 @@ hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream) {
   const auto* kc = static_cast<const __bf16*>(a.k);
   const auto* vc = static_cast<const __bf16*>(a.v);
   auto* o = static_cast<__bf16*>(a.o);
-  const int cols = a.B * a.Hkv * (g / hpw);
   // K/V arrays below 4 GiB are read through buffer resources with 32-bit
   // offsets (chunked-prefill workload: 2.33 -> 2.07 ms against 64-bit
   // addresses per 16-byte chunk); larger ones through global addresses
@@ -878,8 +873,7 @@ hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream) {
   const bool buf = kv_bytes > 0 && kv_bytes < (1LL << 32);
   auto run = [&](auto d, auto qb, auto use_buf) {
     constexpr int D = decltype(d)::value, QB = decltype(qb)::value;
-    const int R = 32 * QB * (4 / hpw);
-    const dim3 grid(cols * ((a.max_seqlen_q + R - 1) / R));
+    const dim3 grid((unsigned)fwd_workgroups(a.B, a.max_seqlen_q, a.Hq, a.Hkv, D));
     extend_kernel<D, QB, decltype(use_buf)::value><<<grid, kThreads, 0, stream>>>(
         q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.cu_seqlens_k, a.sink, o, a.lse,
         a.B, a.total_q, a.max_seqlen_q, a.Hq, a.Hkv, hpw, shift, a.max_pages, sl2, a.causal, a.w1,
@@ -913,13 +907,12 @@ hipError_t launch_index_bf16(const IndexArgs& a, hipStream_t stream) {
   const auto* kc = static_cast<const __bf16*>(a.k_cache);
   const auto* vc = static_cast<const __bf16*>(a.v_cache);
   auto* o = static_cast<__bf16*>(a.o);
-  const int cols = a.B * a.Hkv * (a.Hq / a.Hkv / 4);
   // caches below 4 GiB through buffer resources, as in launch_extend_bf16
   const long long kv_bytes = a.kv_rows * a.Hkv * a.D * 2;
   const bool buf = kv_bytes > 0 && kv_bytes < (1LL << 32);
   auto run = [&](auto d, auto qb, auto use_buf) {
     constexpr int D = decltype(d)::value, QB = decltype(qb)::value;
-    const dim3 grid(cols * ((a.max_seqlen_q + 32 * QB - 1) / (32 * QB)));
+    const dim3 grid((unsigned)index_workgroups(a.B, a.max_seqlen_q, a.Hq, a.Hkv, D));
     index_kernel<D, QB, decltype(use_buf)::value><<<grid, kThreads, 0, stream>>>(
         q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.kv_index, a.cu_blocks, a.sink, o,
         a.lse, a.B, a.total_q, a.max_seqlen_q, a.Hq, a.Hkv, shift, a.max_pages, a.block_q, a.topk,

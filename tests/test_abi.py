@@ -411,3 +411,36 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         binding.lib()
+
+
+def test_launch_size_limits(lib):
+    """Problems whose grid would exceed 32-bit work-item counts (or 65535 in y/z) are
+    rejected on the host with ERR_UNSUPPORTED before any HIP call."""
+    big = "too large for one launch"
+    # prefill: 25165824 one-head groups -> as many 256-thread workgroups
+    h = 25165824
+    assert _prefill(lib, Sq=1, Sk=1, Hq=h, Hkv=h) == binding.ERR_UNSUPPORTED
+    assert big in binding.last_error()
+    # fp32 prefill: the head count is a grid's y extent
+    assert _prefill(lib, Hq=70000, Hkv=70000, Sq=1, Sk=1, dtype=binding.F32) == \
+        binding.ERR_UNSUPPORTED
+    assert big in binding.last_error()
+    # paged decode: 60000 sequences x ~60000 explicit splits
+    assert _decode(lib, B=60000, maxp=(1 << 26), ns=60000, wsb=1 << 62) == binding.ERR_UNSUPPORTED
+    assert big in binding.last_error()
+    assert _decode_noalloc(lib, B=60000, maxp=(1 << 26), ns=60000) == binding.ERR_UNSUPPORTED
+    assert big in binding.last_error()
+    # backward: the head count is the preprocess grid's y extent
+    assert _bwd(lib, Hq=70000, Hkv=70000, Sq=1, Sk=1) == binding.ERR_UNSUPPORTED
+    assert big in binding.last_error()
+    assert _bwd_varlen(lib, Hq=70000, Hkv=70000) == binding.ERR_UNSUPPORTED
+    assert big in binding.last_error()
+    # test exports: 2^24 selected rows x 256 threads, 2^24 sequences x 256 threads
+    r = lib.attn_sink_gather_kv(P, P, P, P, 1, 2, 64, 16, 4, -1, -1, P, P, 1 << 24, binding.BF16,
+                                None)
+    assert r == binding.ERR_UNSUPPORTED and big in binding.last_error()
+    r = lib.attn_sink_decode_select_slots(P, P, 1 << 24, 4, 16, -1, -1, P, P, 8, None)
+    assert r == binding.ERR_UNSUPPORTED and big in binding.last_error()
+    # extend: 16 sequences x 64 one-head groups x 2^24 / 256 row tiles = 2^26 workgroups
+    assert _extend(lib, B=16, tq=1 << 24, mq=1 << 24, Hq=64, Hkv=64) == binding.ERR_UNSUPPORTED
+    assert big in binding.last_error()

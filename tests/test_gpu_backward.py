@@ -60,6 +60,34 @@ def test_backward_matches_oracle(B, Sq, Sk, Hq, Hkv, D, causal, window, use_sink
         assert ds is None
 
 
+def test_backward_minus_inf_sink_entries_and_rows_before_the_context():
+    """Sq > Sk under the causal mask (the first 30 rows see no key) with a sink vector
+    whose heads 1 and 5 are -inf: those heads' dSink is exactly 0 (no NaN from the rows
+    with LSE = -inf), everything matches the oracle, and an all -inf vector gives the
+    gradients of sink = NULL bitwise."""
+    need_gpu()
+    say("case: bwd B1 Sq90 Sk60 H8/2 D64 causal, sink with -inf entries, seed 77")
+    case = synth.prefill_case(1, 90, 60, 8, 2, 64, seed=77, dout=True)
+    case["sink"][[1, 5]] = -np.inf
+    dq, dk, dv, ds = _gpu_fwd_bwd(case, 0.125, True, None)
+    rdq, rdk, rdv, rds, _, _ = oracle.backward(
+        vals(case["q"], synth.BF16), vals(case["k"], synth.BF16), vals(case["v"], synth.BF16),
+        case["sink"], vals(case["dout"], synth.BF16), 0.125, True)
+    check_grad("dQ", host64(dq), rdq)
+    check_grad("dK", host64(dk), rdk)
+    check_grad("dV", host64(dv), rdv)
+    dsg = host64(ds)
+    assert np.all(np.isfinite(dsg))
+    assert dsg[1] == 0.0 and dsg[5] == 0.0
+    _check_dsink(dsg, rds)
+    case["sink"][:] = -np.inf
+    a = _gpu_fwd_bwd(case, 0.125, True, None)
+    b = _gpu_fwd_bwd(case, 0.125, True, None, use_sink=False)
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(a[3], torch.zeros_like(a[3]))
+
+
 def test_backward_deterministic():
     need_gpu()
     case = synth.prefill_case(1, 256, 256, 8, 2, 64, seed=31, dout=True)
