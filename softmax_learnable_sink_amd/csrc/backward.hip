@@ -296,34 +296,49 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
     const bool need_mask = (i0 + kTile > nq) || (causal && p0 < k1 - 1) ||
                            (w2 > 0 && k1 - 1 >= w1 && p0 + kTile - 1 - w2 >= k0);
 
-    // One tile on one of two straight-line paths (mask or not), chosen once per
-    // tile, so that the whole tile is one block for the scheduler: S and dP of
-    // both 32-row blocks first (four independent MFMA chains), then per row
-    // block P = 2^(S sl2 - LSE log2 e), dS = P (dP - Di) (rounded to bf16
-    // operands) and dV^T += dO^T P, dK^T += Q^T dS, so the exps of one row
-    // block can run under the other's MFMAs.  Lane (hh, l32): key l32, rows
-    // 32*qb + 16*hh + i.  The dV/dK A operands are read transposed from the
-    // natural tiles; k-step (qb, c) covers rows 32*qb + 16*hh + 8*c .. +7.
-    auto tile = [&](auto masked) {
-      f32x16 sa[2], pa[2];
+    // S and dP of both 32-row blocks first (four independent MFMA chains), then
+    // per row block P = 2^(S sl2 - LSE log2 e), dS = P (dP - Di) (rounded to
+    // bf16 operands) and dV^T += dO^T P, dK^T += Q^T dS, so the exps of one
+    // row block can run under the other's MFMAs.  Lane (hh, l32): key l32,
+    // rows 32*qb + 16*hh + i.  The dV/dK A operands are read transposed from
+    // the natural tiles; k-step (qb, c) covers rows 32*qb + 16*hh + 8*c .. +7.
+    // Only the P / dS arithmetic sits on one of two straight-line paths (mask
+    // or not, chosen per row block); the accumulating MFMAs are common code.
+    // (With the whole tile in each arm, the join of the two arms' dK/dV
+    // accumulators cost 64 register copies per tile.)
+    f32x16 sa[2], pa[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      sa[qb] = f32x16{};
+      pa[qb] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        sa[qb] = f32x16{};
-        pa[qb] = f32x16{};
+        const int r = (32 * qb + l32) * NS + 16 * ks + 8 * hh;
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&s.q[buf][r]);
+        const bf16x8 da = *reinterpret_cast<const bf16x8*>(&s.dO[buf][r]);
+        sa[qb] = mfma32(qa, kf[ks], sa[qb]);
+        pa[qb] = mfma32(da, vf[ks], pa[qb]);
       }
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int r = (32 * qb + l32) * NS + 16 * ks + 8 * hh;
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&s.q[buf][r]);
-          const bf16x8 da = *reinterpret_cast<const bf16x8*>(&s.dO[buf][r]);
-          sa[qb] = mfma32(qa, kf[ks], sa[qb]);
-          pa[qb] = mfma32(da, vf[ks], pa[qb]);
+    for (int qb = 0; qb < 2; ++qb) {
+      const int rbase = 32 * qb + 16 * hh;
+      bf16x8 pb[2], sb[2];
+      // masked: element i (row i0 + rbase + i) is visible iff lo <= i < hi,
+      // from the causal bound (key <= the row's position), the last window
+      // (the row's position < key + w2 when key >= w1), the rows past nq and
+      // the keys past nk
+      auto grads = [&](auto masked) {
+        int lo = 0, hi = 16;
+        if constexpr (decltype(masked)::value) {
+          const int rb = i0 + rbase;
+          lo = causal ? key - off - rb : -16;
+          hi = nq - rb;
+          if (w2 > 0 && key >= w1) hi = min(hi, key + w2 - off - rb);
+          if (key >= nk) hi = -16;
         }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int rbase = 32 * qb + 16 * hh;
         float pv[16], dsv[16];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
@@ -333,16 +348,11 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * c4 + e;
             float p = exp2_fast(__builtin_fmaf(sa[qb][i], sl2, -a[e]));
-            if constexpr (decltype(masked)::value) {
-              const int row = i0 + rbase + i;
-              const bool ok = (row < nq) & (key < nk) & key_visible(key, off + row, causal, w1, w2);
-              p = ok ? p : 0.f;
-            }
+            if constexpr (decltype(masked)::value) p = (i >= lo) & (i < hi) ? p : 0.f;
             pv[i] = p;
             dsv[i] = p * (pa[qb][i] - d2[e]);
           }
         }
-        bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           pb[c] = to_bf16x8(pv[8 * c], pv[8 * c + 1], pv[8 * c + 2], pv[8 * c + 3],
@@ -350,22 +360,22 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
           sb[c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
                             dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
         }
+      };
+      if (need_mask)
+        grads(std::true_type{});
+      else
+        grads(std::false_type{});
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+      for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const bf16x8 dot = tr_frag<D>(s.dO[buf], 32 * qb + 8 * c, db, lane);
-            const bf16x8 qt = tr_frag<D>(s.q[buf], 32 * qb + 8 * c, db, lane);
-            dva[db] = mfma32(dot, pb[c], dva[db]);
-            dka[db] = mfma32(qt, sb[c], dka[db]);
-          }
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 dot = tr_frag<D>(s.dO[buf], 32 * qb + 8 * c, db, lane);
+          const bf16x8 qt = tr_frag<D>(s.q[buf], 32 * qb + 8 * c, db, lane);
+          dva[db] = mfma32(dot, pb[c], dva[db]);
+          dka[db] = mfma32(qt, sb[c], dka[db]);
         }
       }
-    };
-    if (need_mask)
-      tile(std::true_type{});
-    else
-      tile(std::false_type{});
+    }
 
     if (it + 1 < niter) store_iter(buf ^ 1);
     __syncthreads();
@@ -537,16 +547,34 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
     auto grad_scores = [&](auto masked) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        float dsv[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pr = exp2_fast(__builtin_fmaf(st[kb][i], sl2, -lse2));
-          if constexpr (decltype(masked)::value) {
-            const int j = key0 + 32 * kb + 16 * hh + i;
-            const bool ok = (row < nq) & (j < nk) & key_visible(j, p, causal, w1, w2);
-            pr = ok ? pr : 0.f;
+        // masked: element i (key jb + i) is visible iff i <= hi (the causal
+        // bound, the keys past nk, the rows past nq) and, with a window,
+        // i < a (first window) or i > bnd (last window)
+        const int jb = key0 + 32 * kb + 16 * hh;
+        int hi = 15, a = 16, bnd = -1;
+        if constexpr (decltype(masked)::value) {
+          hi = min(causal ? p - jb : 15, nk - 1 - jb);
+          if (row >= nq) hi = -1;
+          if (w2 > 0) {
+            a = w1 - jb;
+            bnd = p - w2 - jb;
           }
-          dsv[i] = pr * (dp[kb][i] - di_r);
+        }
+        float dsv[16];
+        if (w2 > 0) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float pr = exp2_fast(__builtin_fmaf(st[kb][i], sl2, -lse2));
+            if constexpr (decltype(masked)::value) pr = (i <= hi) & ((i < a) | (i > bnd)) ? pr : 0.f;
+            dsv[i] = pr * (dp[kb][i] - di_r);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float pr = exp2_fast(__builtin_fmaf(st[kb][i], sl2, -lse2));
+            if constexpr (decltype(masked)::value) pr = i <= hi ? pr : 0.f;
+            dsv[i] = pr * (dp[kb][i] - di_r);
+          }
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c)
