@@ -15,7 +15,8 @@ One step runs every entry point once over its synthetic workload:
             middle), sink
 Each entry point is bracketed by HIP events on the stream it is launched on
 (the HBM-bound decode parts are preceded, outside their events, by a 512 MiB
-read that leaves the caches holding clean lines);
+read that leaves the caches holding clean lines); every rate is taken from the
+median step of its part, with the minimum and the mean reported beside it;
 `value` is the prefill throughput in TFLOP/s of algorithmic work (4*D flops per
 visible (query, key) pair), `decode_gbps` the paged decode's algorithmic HBM
 bytes (K and V rows of the attended tokens + Q + O + block table) per second.
@@ -442,19 +443,40 @@ class Workloads:
                                          dsink=t["dsink"], workspace=t["ws"])
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The fp64 oracle (as it stands) on a bounded sample of the prefill workload:
-    the first (batch, head) pairs, in order, that fit the time budget, all 4096
-    query rows each."""
+def host_info():
+    """CPU model (/proc/cpuinfo), BLAS library and thread count NumPy runs with."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = libs[0]
+            blas = f"{i.get('internal_api', '?')} {i.get('version', '?')}"
+            threads = int(i.get("num_threads", threads))
+    except Exception:  # noqa: BLE001
+        pass
+    return model, blas, threads
+
+
+def cpu_baseline(wl, budget_s=10.0, train_budget_s=10.0):
+    """The fp64 oracle (as it stands) on bounded samples: the prefill workload's
+    first (batch, head) pairs, in order, that fit the time budget, all 4096 query
+    rows each; and, for the training workload (B2 S8192 64/8 heads D64 causal),
+    the forward + backward of its first (batch, head) pairs in order, all 8192
+    rows each, within its own budget."""
     import numpy as np
     import oracle
     from softmax_learnable_sink_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
-                    default=1)
-    except Exception:  # noqa: BLE001
-        cores = len(os.sched_getaffinity(0))
+    model, blas, cores = host_info()
     c = wl.pf_case
     B, S, Hq, Hkv, D = 4, 4096, 64, 8, 64
     g = Hq // Hkv
@@ -469,10 +491,32 @@ def cpu_baseline(wl, budget_s=12.0):
         t_total += time.perf_counter() - t0
         n += 1
     flops = 4 * D * causal_pairs(1, n, S, S)
-    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"prefill S4096 D64 causal, the first {n} of 256 (batch, head) pairs "
-                      f"in (batch, head) order, all rows; {t_total:.1f} s of oracle time"}
+    out = {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+           "kind": "oracle",
+           "sample": f"prefill S4096 D64 causal, the first {n} of 256 (batch, head) pairs "
+                     f"in (batch, head) order, all rows; {t_total:.1f} s of oracle time",
+           "cpu_model": model, "blas": blas}
+    # training fwd + bwd (14 D flops per visible pair), the workload's own inputs
+    S = 8192
+    ct = synth.prefill_case(2, S, S, Hq, Hkv, D, seed=0, dout=True)
+    t_total, n = 0.0, 0
+    while t_total < train_budget_s and n < 2 * Hq:
+        b, h = divmod(n, Hq)
+        sl = (slice(b, b + 1), slice(None))
+        q = synth.bf16_to_f32(ct["q"][sl + (slice(h, h + 1),)]).astype(np.float64)
+        do = synth.bf16_to_f32(ct["dout"][sl + (slice(h, h + 1),)]).astype(np.float64)
+        k = synth.bf16_to_f32(ct["k"][sl + (slice(h // g, h // g + 1),)]).astype(np.float64)
+        v = synth.bf16_to_f32(ct["v"][sl + (slice(h // g, h // g + 1),)]).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.backward(q, k, v, ct["sink"][h:h + 1], do, 0.125, True)
+        t_total += time.perf_counter() - t0
+        n += 1
+    flops = 14 * D * causal_pairs(1, n, S, S)
+    out["train"] = {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s",
+                    "sample": f"training fwd+bwd S8192 D64 causal (14 D flops per pair), the "
+                              f"first {n} of 128 (batch, head) pairs in order, all rows; "
+                              f"{t_total:.1f} s of oracle time"}
+    return out
 
 
 def main():
@@ -561,7 +605,10 @@ def main():
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {p: sum(a.elapsed_time(b) for a, b in events[p]) / max(1, args.steps) for p in parts}
+    times = {p: sorted(a.elapsed_time(b) for a, b in events[p]) for p in parts}
+    # rates from the median step of each part; min and mean reported beside it
+    ms = {p: (t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2]))
+          for p, t in times.items()}
 
     traffic = load_traffic()
     out = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -573,7 +620,8 @@ def main():
     parts_out = {}
     for p in parts:
         info = wl.info[p]
-        rec = {"ms": round(ms[p], 5), "shape": info["shape"]}
+        rec = {"ms": round(ms[p], 5), "ms_min": round(times[p][0], 5),
+               "ms_mean": round(sum(times[p]) / len(times[p]), 5), "shape": info["shape"]}
         if "bytes" in info:
             gbps = info["bytes"] / (ms[p] * 1e-3) / 1e9
             rec.update(gbps=round(gbps, 2), hbm_frac=round(gbps / PEAK_HBM_GBPS, 4),
