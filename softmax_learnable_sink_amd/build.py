@@ -53,6 +53,36 @@ def build(verbose=False, extra_flags=()):
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (device code is built
+# as usual): every sanitizer flag applies to the host compilation only.
+SANITIZE_HOST_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-g",
+]
+
+
+def build_sanitized(out):
+    """Build the library with host-side ASan/UBSan into `out` (for the CPU tests of
+    the argument validation; load it with the ASan runtime preloaded)."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1"] + SANITIZE_HOST_FLAGS
+    cmd = [hipcc(), *flags, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+    return out
+
+
+def asan_runtime():
+    """Path of the ASan runtime library of hipcc's clang."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    return res.stdout.strip()
+
+
 if __name__ == "__main__":
     build(verbose="-v" in sys.argv)
     print(LIB)

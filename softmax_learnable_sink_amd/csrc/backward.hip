@@ -348,7 +348,7 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * c4 + e;
             float p = exp2_fast(__builtin_fmaf(sa[qb][i], sl2, -a[e]));
-            if constexpr (decltype(masked)::value) p = (i >= lo) & (i < hi) ? p : 0.f;
+            if constexpr (decltype(masked)::value) p = ((i >= lo) & (i < hi)) ? p : 0.f;
             pv[i] = p;
             dsv[i] = p * (pa[qb][i] - d2[e]);
           }
@@ -565,7 +565,7 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             float pr = exp2_fast(__builtin_fmaf(st[kb][i], sl2, -lse2));
-            if constexpr (decltype(masked)::value) pr = (i <= hi) & ((i < a) | (i > bnd)) ? pr : 0.f;
+            if constexpr (decltype(masked)::value) pr = ((i <= hi) & ((i < a) | (i > bnd))) ? pr : 0.f;
             dsv[i] = pr * (dp[kb][i] - di_r);
           }
         } else {
