@@ -367,6 +367,40 @@ int attn_sink_gather_kv(const void* k_cache, const void* v_cache, const int32_t*
                         int max_pages_per_seq, int window_first, int window_last, void* k_out,
                         void* v_out, int max_sel, int dtype, void* hip_stream);
 
+/*
+ * Device-side preconditions.  The values that live on the device -- seqlens_k
+ * (decode: in [1, max_pages_per_seq * page_size]; extend and index lists: in
+ * [0, that]), the block-table entries a call reads (in [0, num_pages)) and the
+ * cumulative offsets cu_seqlens_q / cu_seqlens_k (0 = cu[0] <= ... <= cu[B] =
+ * the total, no length above its stated maximum) -- are not checked by the
+ * release library.  The debug build, libattn_sink_debug.so (the same sources
+ * compiled with ATTN_SINK_DEVICE_CHECKS), checks them on the device ahead of
+ * each paged or packed launch and ORs the violations into an error word; its
+ * kernels then return without reading through the bad values (their outputs
+ * are left unwritten).
+ */
+#define ATTN_SINK_CHECK_SEQLEN 1u     /* a sequence length out of range          */
+#define ATTN_SINK_CHECK_PAGE 2u       /* a block-table entry read out of range   */
+#define ATTN_SINK_CHECK_CU_SEQLENS 4u /* cumulative offsets not well formed      */
+
+/* Debug build: waits for `hip_stream`, then stores in *flags the violations
+ * recorded so far (ATTN_SINK_CHECK_* bits) and clears them when `clear` != 0.
+ * This call synchronises.  The release library returns ATTN_SINK_ERR_UNSUPPORTED
+ * and stores 0. */
+int attn_sink_device_check_flags(unsigned* flags, int clear, void* hip_stream);
+
+/* The same checks on HOST arrays (any build, no HIP call): block_table [B,
+ * max_pages_per_seq], seqlens_k [B], cu_seqlens_q [B+1] or NULL (with total_q
+ * and max_seqlen_q).  decode != 0 checks what the paged decode reads (lengths
+ * >= 1, the pages of the selected tokens only); decode == 0 what the extend
+ * and index-list paths read (lengths >= 0, every page of [0, L)).  *flags
+ * receives the ATTN_SINK_CHECK_* bits of every violation. */
+int attn_sink_check_paged_inputs(const int32_t* block_table, const int32_t* seqlens_k,
+                                 const int32_t* cu_seqlens_q, int B, int total_q,
+                                 int max_seqlen_q, int max_pages_per_seq, int page_size,
+                                 int num_pages, int window_first, int window_last, int decode,
+                                 unsigned* flags);
+
 #ifdef __cplusplus
 }
 #endif

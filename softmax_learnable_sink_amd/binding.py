@@ -14,12 +14,16 @@ import os
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_sink.so")
+# the same library with device-side precondition checks (a debug build)
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_sink_debug.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 BF16, F32 = 0, 1
 
 _lib = None
+_debug_lib = None
 _vp = ctypes.c_void_p
+_pu = ctypes.POINTER(ctypes.c_uint)
 _i = ctypes.c_int
 _f = ctypes.c_float
 _sz = ctypes.c_size_t
@@ -42,23 +46,68 @@ _SIGNATURES = {
     "attn_sink_bwd_varlen_workspace_bytes": ([_i] * 4, _sz),
     "attn_sink_decode_select_slots": ([_vp, _vp] + [_i] * 5 + [_vp, _vp, _i, _vp], _i),
     "attn_sink_gather_kv": ([_vp] * 4 + [_i] * 7 + [_vp, _vp, _i, _i, _vp], _i),
+    "attn_sink_device_check_flags": ([_pu, _i, _vp], _i),
+    "attn_sink_check_paged_inputs": ([_vp] * 3 + [_i] * 9 + [_pu], _i),
 }
+
+CHECK_SEQLEN, CHECK_PAGE, CHECK_CU_SEQLENS = 1, 2, 4
+
+
+def _load(path):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m softmax_learnable_sink_amd.build`")
+    handle = ctypes.CDLL(path)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.argtypes = args
+        fn.restype = res
+    return handle
 
 
 def lib():
     """Load libattn_sink.so once (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -m softmax_learnable_sink_amd.build`")
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (args, res) in _SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.argtypes = args
-            fn.restype = res
-        _lib = handle
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def debug_lib():
+    """Load libattn_sink_debug.so (device-side precondition checks) once."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(DEBUG_LIB_PATH)
+    return _debug_lib
+
+
+def attn_sink_device_check_flags(clear=True, handle=None, stream=None):
+    """ATTN_SINK_CHECK_* bits recorded by a debug library's device checks (waits for
+    the stream).  Raises AttnSinkError with the release library."""
+    h = handle if handle is not None else lib()
+    flags = ctypes.c_uint(0)
+    st = stream if stream is not None else _stream(torch.cuda.current_device())
+    status = h.attn_sink_device_check_flags(ctypes.byref(flags), int(bool(clear)), st)
+    if status != OK:
+        raise AttnSinkError(status, h.attn_sink_last_error().decode())
+    return flags.value
+
+
+def attn_sink_check_paged_inputs(block_table, seqlens_k, page_size, num_pages, cu_seqlens_q=None,
+                                 total_q=0, max_seqlen_q=0, window=None, decode=True):
+    """The device-side precondition checks applied to host (NumPy) arrays: the
+    ATTN_SINK_CHECK_* bits of every violation."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seqlens_k, dtype=np.int32)
+    cu = None if cu_seqlens_q is None else np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    w1, w2 = _window(window)
+    flags = ctypes.c_uint(0)
+    _check(lib().attn_sink_check_paged_inputs(
+        bt.ctypes.data, sl.ctypes.data, None if cu is None else cu.ctypes.data, bt.shape[0],
+        total_q, max_seqlen_q, bt.shape[1], page_size, num_pages, w1, w2, int(bool(decode)),
+        ctypes.byref(flags)))
+    return flags.value
 
 
 class AttnSinkError(RuntimeError):

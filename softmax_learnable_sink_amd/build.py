@@ -13,6 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_sink.so")
+LIB_DEBUG = os.path.join(PKG, "libattn_sink_debug.so")  # with device-side checks
 SOURCES = ["api.hip", "prefill.hip", "decode.hip", "backward.hip"]
 
 HIPCC_FLAGS = [
@@ -35,21 +36,30 @@ def hipcc():
     return path
 
 
-def build(verbose=False, extra_flags=()):
-    """Compile every HIP source into softmax_learnable_sink_amd/libattn_sink.so."""
+def _compile(out, extra_flags, verbose):
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
-                    if "is not a recognized feature for this target" not in line)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True), tmp
+
+
+def build(verbose=False, extra_flags=()):
+    """Compile every HIP source into softmax_learnable_sink_amd/libattn_sink.so and,
+    with device-side precondition checks, libattn_sink_debug.so (in parallel)."""
+    jobs = [(LIB, _compile(LIB, list(extra_flags), verbose)),
+            (LIB_DEBUG, _compile(LIB_DEBUG, list(extra_flags) + ["-DATTN_SINK_DEVICE_CHECKS=1"],
+                                 verbose))]
+    for out, (proc, tmp) in jobs:
+        text = proc.communicate()[0]
+        text = "\n".join(line for line in text.splitlines()
+                         if "is not a recognized feature for this target" not in line)
+        if proc.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({proc.returncode}) for {out}:\n{text}")
+        if verbose and text.strip():
+            print(text)
+        os.replace(tmp, out)
     return LIB
 
 

@@ -10,6 +10,7 @@
 #include <string>
 
 #include "attn_sink.h"
+#include "checks.h"
 #include "launch.h"
 
 using namespace attn_sink;
@@ -474,8 +475,8 @@ int attn_sink_bwd(const void* q, const void* k, const void* v, const void* o, co
           "a 16-byte aligned workspace of %zu bytes is required", need);
   REQUIRE(workspace_bytes >= need, ATTN_SINK_ERR_WORKSPACE,
           "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
-  BackwardArgs a{q,  k,  v,      o,  dout, lse, sink, dq, dk, dv, dsink, nullptr, nullptr, B,
-                 Sq, Sk, B * Sq, Hq, Hkv,  D,   softmax_scale, causal, window_first,
+  BackwardArgs a{q,  k,  v,      o,      dout, lse, sink, dq, dk, dv, dsink, nullptr, nullptr, B,
+                 Sq, Sk, B * Sq, B * Sk, Hq,   Hkv, D,    softmax_scale, causal, window_first,
                  window_last, workspace};
   return hip_status(launch_backward_bf16(a, static_cast<hipStream_t>(hip_stream)),
                     "attn_sink_bwd launch");
@@ -529,8 +530,8 @@ int attn_sink_bwd_varlen(const void* q, const void* k, const void* v, const void
   REQUIRE(workspace_bytes >= need, ATTN_SINK_ERR_WORKSPACE,
           "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
   BackwardArgs a{q,  k,  v,  o,  dout, lse, sink, dq, dk, dv, dsink, cu_seqlens_q, cu_seqlens_k,
-                 B,  max_seqlen_q, max_seqlen_k, total_q, Hq, Hkv, D, softmax_scale, causal,
-                 window_first, window_last, workspace};
+                 B,  max_seqlen_q, max_seqlen_k, total_q, total_k, Hq, Hkv, D, softmax_scale,
+                 causal, window_first, window_last, workspace};
   return hip_status(launch_backward_bf16(a, static_cast<hipStream_t>(hip_stream)),
                     "attn_sink_bwd_varlen launch");
 }
@@ -579,6 +580,57 @@ int attn_sink_gather_kv(const void* k_cache, const void* v_cache, const int32_t*
                                      k_out, v_out, max_sel, dtype == ATTN_SINK_BF16 ? 2 : 4,
                                      static_cast<hipStream_t>(hip_stream)),
                     "attn_sink_gather_kv launch");
+}
+
+int attn_sink_device_check_flags(unsigned* flags, int clear, void* hip_stream) {
+  REQUIRE(flags, ATTN_SINK_ERR_INVALID_ARG, "flags must not be NULL");
+#ifdef ATTN_SINK_DEVICE_CHECKS
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  unsigned a = 0, b = 0, c = 0;
+  if (int r = hip_status(read_check_word_decode(&a, clear != 0, st), "device check word")) return r;
+  if (int r = hip_status(read_check_word_prefill(&b, clear != 0, st), "device check word")) return r;
+  if (int r = hip_status(read_check_word_backward(&c, clear != 0, st), "device check word"))
+    return r;
+  *flags = a | b | c;
+  return ok();
+#else
+  (void)clear;
+  (void)hip_stream;
+  *flags = 0;
+  return fail(ATTN_SINK_ERR_UNSUPPORTED,
+              "this library was built without device checks (libattn_sink_debug.so has them)");
+#endif
+}
+
+int attn_sink_check_paged_inputs(const int32_t* block_table, const int32_t* seqlens_k,
+                                 const int32_t* cu_seqlens_q, int B, int total_q,
+                                 int max_seqlen_q, int max_pages_per_seq, int page_size,
+                                 int num_pages, int window_first, int window_last, int decode,
+                                 unsigned* flags) {
+  REQUIRE(block_table && seqlens_k && flags, ATTN_SINK_ERR_INVALID_ARG,
+          "block_table, seqlens_k and flags must not be NULL");
+  REQUIRE(B >= 1 && max_pages_per_seq >= 1 && num_pages >= 1, ATTN_SINK_ERR_INVALID_ARG,
+          "B, max_pages_per_seq and num_pages must be >= 1");
+  REQUIRE(pow2(page_size) && page_size <= 256, ATTN_SINK_ERR_UNSUPPORTED,
+          "page_size must be a power of two in [1, 256] (got %d)", page_size);
+  if (int r = check_window(window_first, window_last)) return r;
+  unsigned f = 0;
+  for (int b = 0; b < B; ++b) {
+    if (cu_seqlens_q && !cu_ok(cu_seqlens_q, b, B, total_q, max_seqlen_q)) f |= kCheckCuSeqlens;
+    const int L = seqlens_k[b];
+    if (!seqlen_ok(L, decode ? 1 : 0, max_pages_per_seq, page_size)) {
+      f |= kCheckSeqlen;
+      continue;
+    }
+    const PageRanges r = page_ranges(L, page_size, window_first, window_last, decode != 0);
+    const int32_t* row = block_table + (size_t)b * max_pages_per_seq;
+    for (int i = 0; i < r.n_first; ++i)
+      if (!page_ok(row[i], num_pages)) f |= kCheckPage;
+    for (int i = r.last0; i < r.n_pages; ++i)
+      if (!page_ok(row[i], num_pages)) f |= kCheckPage;
+  }
+  *flags = f;
+  return ok();
 }
 
 }  // extern "C"

@@ -21,6 +21,7 @@
 //   bwd_dsink_reduce fixed-order sum of the dSink partials
 #include <type_traits>
 
+#include "checks.h"
 #include "common.h"
 #include "launch.h"
 
@@ -114,6 +115,7 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
     const __bf16* __restrict__ o, const __bf16* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ sink, float* __restrict__ di, float* __restrict__ dsink_part,
     const int32_t* __restrict__ cu_q, int Sq, int Hq, int total_q) {
+  ATTN_SINK_CHECK_GUARD();
   constexpr int PER = D / 4;  // elements per thread
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -162,6 +164,7 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
 // by a fixed tree: the order depends only on B and nblk, never on timing.
 __global__ __launch_bounds__(kThreads) void bwd_dsink_reduce_kernel(
     const float* __restrict__ part, float* __restrict__ dsink, int Hq, int B, int nblk) {
+  ATTN_SINK_CHECK_GUARD();
   const int h = blockIdx.x, tid = threadIdx.x;
   const int n = B * nblk;
   float acc = 0.f;
@@ -401,6 +404,7 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
 // that see the most query rows (the first ones under a causal mask) start first
 template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(DKDV_PARAMS) {
+  ATTN_SINK_CHECK_GUARD();
   __shared__ DkdvLds<D> s;
   dkdv_block<D>(s, blockIdx.x, blockIdx.y, blockIdx.z, q, k, v, dout, lse, di, dk, dv, cu_q, cu_k,
                 Sq, Sk, Hq, Hkv, total_q, scale, sl2, causal, w1, w2);
@@ -616,6 +620,7 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
 
 template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(DQ_PARAMS) {
+  ATTN_SINK_CHECK_GUARD();
   __shared__ DqLds<D> s;
   dq_block<D>(s, blockIdx.x, q, k, v, dout, lse, di, dq, cu_q, cu_k, B, Sq, Sk, Hq, Hkv, total_q,
               hpw, scale, sl2, causal, w1, w2);
@@ -633,6 +638,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_main_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int B, int Sq, int Sk,
     int Hq, int Hkv, int total_q, int hpw, float scale, float sl2, int causal, int w1, int w2,
     int nkv) {
+  ATTN_SINK_CHECK_GUARD();
   __shared__ union {
     DkdvLds<D> kv;
     DqLds<D> q;
@@ -682,6 +688,11 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
   const dim3 kgrid(a.Hkv, a.B, (a.Sk + 127) / 128);
   const dim3 qgrid((unsigned)bwd_dq_workgroups(a.B, a.Sq, a.Hq, a.Hkv));
   const bool rows_q = a.Sq > 0, rows_k = a.Sk > 0;
+#ifdef ATTN_SINK_DEVICE_CHECKS
+  if (cq)  // packed query and key offsets
+    check_cu_kernel<<<(a.B + 255) / 256, 256, 0, stream>>>(cq, ck, a.B, a.total_q, a.total_k,
+                                                            a.Sq, a.Sk);
+#endif
   if (a.D == 64) {
     if (rows_q)
       bwd_preprocess_kernel<64><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di, part,
@@ -720,5 +731,9 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
     bwd_dsink_reduce_kernel<<<a.Hq, kThreads, 0, stream>>>(part, a.dsink, a.Hq, a.B, nblk);
   return hipGetLastError();
 }
+
+#ifdef ATTN_SINK_DEVICE_CHECKS
+ATTN_SINK_DEFINE_CHECK_READER(read_check_word_backward)
+#endif
 
 }  // namespace attn_sink

@@ -29,6 +29,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "checks.h"
 #include "common.h"
 #include "launch.h"
 
@@ -212,6 +213,7 @@ __global__ __launch_bounds__(256) void decode_plan_kernel(const int32_t* __restr
                                                           int max_splits,
                                                           int32_t* __restrict__ items,
                                                           int32_t* __restrict__ count) {
+  ATTN_SINK_CHECK_GUARD();
   __shared__ int wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int base = 0;
@@ -299,6 +301,7 @@ __global__ __launch_bounds__(64 * NW) void decode_partial_kernel(
     const int32_t* __restrict__ items, const int32_t* __restrict__ count, int B, int Hq, int Hkv,
     int hgroups, int page_shift, int max_pages, float sl2, int w1, int w2, int chunk,
     int max_splits, ListArgs la, EvenArgs ev, uint32_t kv_bytes) {
+  ATTN_SINK_CHECK_GUARD();
   constexpr bool LIST = MODE == kModeList;
   __shared__ DecLds<D, NW> s;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -595,6 +598,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ seqlens,
     const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq,
     int w1, int w2, int chunk, int max_splits, EvenArgs ev) {
+  ATTN_SINK_CHECK_GUARD();
   constexpr bool LIST = MODE == kModeList;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bh = blockIdx.x * 4 + wave;
@@ -838,6 +842,13 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
   const uint32_t kvb = buf ? (uint32_t)kv_bytes : 0u;
   using T = std::true_type;
   using F = std::false_type;
+#ifdef ATTN_SINK_DEVICE_CHECKS
+  // sequence lengths in [1, max_pages * page_size], block-table entries of the
+  // selected tokens' pages in [0, num_pages)
+  check_paged_kernel<<<a.B, 256, 0, stream>>>(a.block_table, a.seqlens, nullptr, a.B, 0, 0,
+                                               a.max_pages, a.page_size, a.num_pages, 1, a.w1,
+                                               a.w2, 1);
+#endif
 
   if (a.even) {
     // one round of resident workgroups (measured: two rounds of half-length
@@ -919,6 +930,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {
 // Packed row -> its sequence, for the per-query list mode.
 __global__ __launch_bounds__(256) void row_seq_kernel(const int32_t* __restrict__ cu_q,
                                                       int32_t* __restrict__ row_seq) {
+  ATTN_SINK_CHECK_GUARD();
   const int b = blockIdx.x;
   for (int r = cu_q[b] + threadIdx.x; r < cu_q[b + 1]; r += 256) row_seq[r] = b;
 }
@@ -957,6 +969,12 @@ hipError_t launch_index_rows_bf16(const IndexRowsArgs& a, hipStream_t stream) {
   float* part = static_cast<float*>(a.workspace);
   int32_t* row_seq = reinterpret_cast<int32_t*>(part + (size_t)a.total_q * a.Hq *
                                                             plan.max_splits * (a.D + 2));
+#ifdef ATTN_SINK_DEVICE_CHECKS
+  // query offsets, lengths in [0, max_pages * page_size] and every page of [0, L)
+  check_paged_kernel<<<a.B, 256, 0, stream>>>(
+      a.block_table, a.seqlens_k, a.cu_seqlens_q, a.B, a.total_q, a.total_q, a.max_pages,
+      a.page_size, (int)(a.kv_rows / a.page_size), 0, -1, -1, 0);
+#endif
   row_seq_kernel<<<a.B, 256, 0, stream>>>(a.cu_seqlens_q, row_seq);
   const ListArgs la{a.kv_index, row_seq, a.cu_seqlens_q, a.topk};
   const long long slots = (long long)a.total_q * plan.max_splits;
@@ -1022,5 +1040,9 @@ hipError_t launch_gather_kv(const void* kc, const void* vc, const int32_t* bt,
       static_cast<uint16_t*>(v_out), max_sel, elem_bytes / 2);
   return hipGetLastError();
 }
+
+#ifdef ATTN_SINK_DEVICE_CHECKS
+ATTN_SINK_DEFINE_CHECK_READER(read_check_word_decode)
+#endif
 
 }  // namespace attn_sink

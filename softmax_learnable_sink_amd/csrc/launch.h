@@ -189,7 +189,7 @@ struct BackwardArgs {
   // total_q packed query rows, LSE [Hq, total_q].
   const int32_t* cu_seqlens_q;
   const int32_t* cu_seqlens_k;
-  int B, Sq, Sk, total_q, Hq, Hkv, D;
+  int B, Sq, Sk, total_q, total_k, Hq, Hkv, D;
   float scale;
   int causal, w1, w2;
   void* workspace;
@@ -198,5 +198,13 @@ struct BackwardArgs {
 // most max_sq rows.
 size_t backward_workspace_bytes(int B, int max_sq, int Hq, size_t rows);
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream);
+
+#ifdef ATTN_SINK_DEVICE_CHECKS
+// Error words of the files with device checks (ORed kCheck* flags), read after
+// the stream's work and cleared if asked.
+hipError_t read_check_word_decode(unsigned* word, bool clear, hipStream_t stream);
+hipError_t read_check_word_prefill(unsigned* word, bool clear, hipStream_t stream);
+hipError_t read_check_word_backward(unsigned* word, bool clear, hipStream_t stream);
+#endif
 
 }  // namespace attn_sink

@@ -24,6 +24,7 @@
 #include <climits>
 #include <type_traits>
 
+#include "checks.h"
 #include "common.h"
 #include "launch.h"
 
@@ -517,6 +518,7 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
     const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int B,
     int total_q, int max_sq, int Hq, int Hkv, int hpw, int page_shift, int max_pages, float sl2,
     int causal, int w1, int w2, uint32_t kv_bytes) {
+  ATTN_SINK_CHECK_GUARD();
   __shared__ Lds<D> s;
   constexpr int RW = 32 * QB;
   const int tid = threadIdx.x;
@@ -676,6 +678,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_kernel(
     const int32_t* __restrict__ cu_blocks, const float* __restrict__ sink, __bf16* __restrict__ o,
     float* __restrict__ lse, int B, int total_q, int max_sq, int Hq, int Hkv, int page_shift,
     int max_pages, int block_q, int topk, float sl2, uint32_t kv_bytes) {
+  ATTN_SINK_CHECK_GUARD();
   __shared__ Lds<D> s;
   __shared__ __attribute__((aligned(16))) int tokl[kMaxList];
   __shared__ int tmax[kMaxList / kBN];  // largest token of each tile (INT_MAX if one is empty)
@@ -866,6 +869,15 @@ hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream) {
   const auto* kc = static_cast<const __bf16*>(a.k);
   const auto* vc = static_cast<const __bf16*>(a.v);
   auto* o = static_cast<__bf16*>(a.o);
+#ifdef ATTN_SINK_DEVICE_CHECKS
+  if (a.block_table)  // query offsets, lengths, every page of [0, L)
+    check_paged_kernel<<<a.B, 256, 0, stream>>>(
+        a.block_table, a.seqlens_k, a.cu_seqlens_q, a.B, a.total_q, a.max_seqlen_q, a.max_pages,
+        a.page_size, (int)(a.kv_rows / a.page_size), 0, -1, -1, 0);
+  else  // packed query and key offsets
+    check_cu_kernel<<<(a.B + 255) / 256, 256, 0, stream>>>(
+        a.cu_seqlens_q, a.cu_seqlens_k, a.B, a.total_q, (int)a.kv_rows, a.max_seqlen_q, INT_MAX);
+#endif
   // K/V arrays below 4 GiB are read through buffer resources with 32-bit
   // offsets (chunked-prefill workload: 2.33 -> 2.07 ms against 64-bit
   // addresses per 16-byte chunk); larger ones through global addresses
@@ -907,6 +919,11 @@ hipError_t launch_index_bf16(const IndexArgs& a, hipStream_t stream) {
   const auto* kc = static_cast<const __bf16*>(a.k_cache);
   const auto* vc = static_cast<const __bf16*>(a.v_cache);
   auto* o = static_cast<__bf16*>(a.o);
+#ifdef ATTN_SINK_DEVICE_CHECKS
+  check_paged_kernel<<<a.B, 256, 0, stream>>>(
+      a.block_table, a.seqlens_k, a.cu_seqlens_q, a.B, a.total_q, a.max_seqlen_q, a.max_pages,
+      a.page_size, (int)(a.kv_rows / a.page_size), 0, -1, -1, 0);
+#endif
   // caches below 4 GiB through buffer resources, as in launch_extend_bf16
   const long long kv_bytes = a.kv_rows * a.Hkv * a.D * 2;
   const bool buf = kv_bytes > 0 && kv_bytes < (1LL << 32);
@@ -953,5 +970,9 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
                                                      a.Hq, a.Hkv, sl2, a.causal, a.w1, a.w2);
   return hipGetLastError();
 }
+
+#ifdef ATTN_SINK_DEVICE_CHECKS
+ATTN_SINK_DEFINE_CHECK_READER(read_check_word_prefill)
+#endif
 
 }  // namespace attn_sink
