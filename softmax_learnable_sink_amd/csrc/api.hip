@@ -467,7 +467,7 @@ int attn_sink_bwd(const void* q, const void* k, const void* v, const void* o, co
   REQUIRE((long long)Sk * Hkv * D * 2 <= kMaxSlice && (long long)Sq * Hq * D * 2 <= kMaxSlice,
           ATTN_SINK_ERR_UNSUPPORTED, "one batch's K/V or Q/dO slice exceeds 4 GiB");
   REQUIRE(Hq <= kMaxGridYZ &&
-              dispatch_fits(bwd_dkdv_workgroups(B, Sk, Hkv) + bwd_dq_workgroups(B, Sq, Hq, Hkv),
+              dispatch_fits(bwd_dkdv_workgroups(B, Sk, Hkv) + bwd_dq_workgroups(B, Sq, Hq, Hkv, D),
                             256),
           ATTN_SINK_ERR_UNSUPPORTED, "%s", kGridMsg);
   const size_t need = backward_workspace_bytes(B, Sq, Hq, (size_t)B * Sq);
@@ -521,7 +521,7 @@ int attn_sink_bwd_varlen(const void* q, const void* k, const void* v, const void
           ATTN_SINK_ERR_UNSUPPORTED, "one sequence's K/V or Q/dO slice exceeds 4 GiB");
   REQUIRE(Hq <= kMaxGridYZ &&
               dispatch_fits(bwd_dkdv_workgroups(B, max_seqlen_k, Hkv) +
-                                bwd_dq_workgroups(B, max_seqlen_q, Hq, Hkv),
+                                bwd_dq_workgroups(B, max_seqlen_q, Hq, Hkv, D),
                             256),
           ATTN_SINK_ERR_UNSUPPORTED, "%s", kGridMsg);
   const size_t need = backward_workspace_bytes(B, max_seqlen_q, Hq, (size_t)total_q);

@@ -193,7 +193,7 @@ struct DkdvLds {
   __bf16 q[2][kTile * (D + kPad)];
   __bf16 dO[2][kTile * (D + kPad)];
   alignas(16) float lse2[2][kTile];
-  alignas(16) float di[2][kTile];
+  alignas(16) float di[2][kTile];  // -Di of the tile's rows
 };
 
 #define DKDV_PARAMS                                                                             \
@@ -280,7 +280,7 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
     tdo.store(s.dO[buf], tid);
     if (tid < kTile) {
       s.lse2[buf][tid] = lse_r * kLog2e;
-      s.di[buf][tid] = di_r;
+      s.di[buf][tid] = -di_r;  // the dP accumulators start at -Di
     }
   };
 
@@ -309,11 +309,19 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
     // or not, chosen per row block); the accumulating MFMAs are common code.
     // (With the whole tile in each arm, the join of the two arms' dK/dV
     // accumulators cost 64 register copies per tile.)
+    // dP accumulators start at -Di (the rows' element i = row rbase + i), so
+    // that dS = P (dP - Di) is one multiply per score
     f32x16 sa[2], pa[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       sa[qb] = f32x16{};
-      pa[qb] = f32x16{};
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const f32x4 d2 =
+            *reinterpret_cast<const f32x4*>(&s.di[buf][32 * qb + 16 * hh + 4 * c4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pa[qb][4 * c4 + e] = d2[e];
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
@@ -346,14 +354,13 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           const f32x4 a = *reinterpret_cast<const f32x4*>(&s.lse2[buf][rbase + 4 * c4]);
-          const f32x4 d2 = *reinterpret_cast<const f32x4*>(&s.di[buf][rbase + 4 * c4]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * c4 + e;
             float p = exp2_fast(__builtin_fmaf(sa[qb][i], sl2, -a[e]));
             if constexpr (decltype(masked)::value) p = ((i >= lo) & (i < hi)) ? p : 0.f;
             pv[i] = p;
-            dsv[i] = p * (pa[qb][i] - d2[e]);
+            dsv[i] = p * pa[qb][i];
           }
         }
 #pragma unroll
@@ -458,14 +465,18 @@ __device__ __forceinline__ QRange kv_tiles(int Sk, int p_min, int p_max, int cau
       int hpw, float scale, float sl2, int causal, int w1, int w2
 
 // Work block w of the forward's XCD-aware order (row tile of one head group).
-template <int D>
+// A wave owns 32*QB rows of one head: with QB = 2 every K, V and K^T fragment
+// read from LDS feeds two MFMAs (one per 32-row block), which halves the LDS
+// traffic per MFMA; the transposing K^T reads are the slowest LDS reads.
+template <int D, int QB>
 __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
   constexpr int NS = D + kPad;
+  constexpr int RW = 32 * QB;  // rows per wave
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, l32 = lane & 31;
   const int g = Hq / Hkv;
   const int groups = g / hpw;
-  const int R = 32 * (4 / hpw);
+  const int R = RW * (4 / hpw);
   const WorkItem wi = work_item(w, B * Hkv, groups, (Sq + R - 1) / R);
   const int kvh = wi.pair % Hkv, b = wi.pair / Hkv;
   const SeqRows sr = seq_rows(cu_q, cu_k, b, Sq, Sk, Hq, total_q);
@@ -474,33 +485,42 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
   if (row0 >= nq) return;  // uniform over the workgroup
   const int h = kvh * g + wi.grp * hpw + (wave % hpw);
   const int rb = wave / hpw;
-  const int row = row0 + rb * 32 + l32;
+  const int wrow0 = row0 + rb * RW;
   const int off = nk - nq;
-  const int p = off + row;
   const int p_min = off + row0;
   const int p_max = off + min(nq, row0 + R) - 1;
 
-  bf16x8 qf[D / 16], of[D / 16];
-  float lse2 = 0.f, di_r = 0.f;
-  if (row < nq) {
-    const size_t base = ((size_t)(sr.q0 + row) * Hq + h) * D + 8 * hh;
+  // per row block qb: this lane's row wrow0 + 32*qb + l32, its Q / dO
+  // fragments, LSE (log2 units) and Di
+  bf16x8 qf[QB][D / 16], of[QB][D / 16];
+  float lse2[QB], di_r[QB];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(q + base + 16 * ks);
-      of[ks] = *reinterpret_cast<const bf16x8*>(dout + base + 16 * ks);
-    }
-    lse2 = lse[sr.l0 + h * sr.lh + row] * kLog2e;
-    di_r = di[sr.l0 + h * sr.lh + row];
-  } else {
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wrow0 + 32 * qb + l32;
+    di_r[qb] = 0.f;
+    lse2[qb] = 0.f;
+    if (row < nq) {
+      const size_t base = ((size_t)(sr.q0 + row) * Hq + h) * D + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      qf[ks] = bf16x8{};
-      of[ks] = bf16x8{};
+      for (int ks = 0; ks < D / 16; ++ks) {
+        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(q + base + 16 * ks);
+        of[qb][ks] = *reinterpret_cast<const bf16x8*>(dout + base + 16 * ks);
+      }
+      lse2[qb] = lse[sr.l0 + h * sr.lh + row] * kLog2e;
+      di_r[qb] = di[sr.l0 + h * sr.lh + row];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        qf[qb][ks] = bf16x8{};
+        of[qb][ks] = bf16x8{};
+      }
     }
   }
-  f32x16 dqa[D / 32];
+  f32x16 dqa[D / 32][QB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) dqa[db] = f32x16{};
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) dqa[db][qb] = f32x16{};
 
   const QRange tr = kv_tiles(nk, p_min, p_max, causal, w1, w2);
   const int ntiles = tr.count();
@@ -526,78 +546,81 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
       tk.load(kbase, rs, tr.tile(it + 1) * kTile, nk);
       tv.load(vbase, rs, tr.tile(it + 1) * kTile, nk);
     }
-    f32x16 st[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      st[kb] = f32x16{};
-      dp[kb] = f32x16{};
-    }
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = (32 * kb + l32) * NS + 16 * ks + 8 * hh;
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&s.k[buf][r]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&s.v[buf][r]);
-        st[kb] = mfma32(ka, qf[ks], st[kb]);
-        dp[kb] = mfma32(va, of[ks], dp[kb]);
-      }
     const bool need_mask = (key0 + kTile > nk) || (causal && key0 + kTile - 1 > p_min) ||
                            (w2 > 0 && key0 + kTile - 1 >= w1 && key0 <= p_max - w2) ||
                            (row0 + R > nq);
-    // dS^T = P^T (dP^T - Di); the mask is applied on one of two straight-line
-    // paths chosen once per tile
-    bf16x8 sb[2][2];
-    auto grad_scores = [&](auto masked) {
+    // one 32-key block at a time: S^T and dP^T of every row block, dS^T, then
+    // dQ^T += K^T dS^T
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // masked: element i (key jb + i) is visible iff i <= hi (the causal
-        // bound, the keys past nk, the rows past nq) and, with a window,
-        // i < a (first window) or i > bnd (last window)
-        const int jb = key0 + 32 * kb + 16 * hh;
-        int hi = 15, a = 16, bnd = -1;
-        if constexpr (decltype(masked)::value) {
-          hi = min(causal ? p - jb : 15, nk - 1 - jb);
-          if (row >= nq) hi = -1;
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 st[QB], dp[QB];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int r = (32 * kb + l32) * NS + 16 * ks + 8 * hh;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&s.k[buf][r]);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&s.v[buf][r]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          st[qb] = mfma32(ka, qf[qb][ks], ks == 0 ? f32x16{} : st[qb]);
+          dp[qb] = mfma32(va, of[qb][ks], ks == 0 ? f32x16{} : dp[qb]);
+        }
+      }
+      // dS^T = P^T (dP^T - Di); masked (one of two straight-line paths chosen
+      // per tile): element i (key jb + i) of row block qb is visible iff i <= hi
+      // (the causal bound, the keys past nk, the rows past nq) and, with a
+      // window, i < a (first window) or i > bnd (last window)
+      bf16x8 sb[QB][2];
+      auto grad_scores = [&](auto masked) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int row = wrow0 + 32 * qb + l32;
+          const int p = off + row;
+          const int jb = key0 + 32 * kb + 16 * hh;
+          int hi = 15, a = 16, bnd = -1;
+          if constexpr (decltype(masked)::value) {
+            hi = min(causal ? p - jb : 15, nk - 1 - jb);
+            if (row >= nq) hi = -1;
+            if (w2 > 0) {
+              a = w1 - jb;
+              bnd = p - w2 - jb;
+            }
+          }
+          float dsv[16];
           if (w2 > 0) {
-            a = w1 - jb;
-            bnd = p - w2 - jb;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              float pr = exp2_fast(__builtin_fmaf(st[qb][i], sl2, -lse2[qb]));
+              if constexpr (decltype(masked)::value)
+                pr = ((i <= hi) & ((i < a) | (i > bnd))) ? pr : 0.f;
+              dsv[i] = pr * (dp[qb][i] - di_r[qb]);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              float pr = exp2_fast(__builtin_fmaf(st[qb][i], sl2, -lse2[qb]));
+              if constexpr (decltype(masked)::value) pr = i <= hi ? pr : 0.f;
+              dsv[i] = pr * (dp[qb][i] - di_r[qb]);
+            }
           }
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            sb[qb][c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
+                                  dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6],
+                                  dsv[8 * c + 7]);
         }
-        float dsv[16];
-        if (w2 > 0) {
+      };
+      if (need_mask)
+        grad_scores(std::true_type{});
+      else
+        grad_scores(std::false_type{});
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float pr = exp2_fast(__builtin_fmaf(st[kb][i], sl2, -lse2));
-            if constexpr (decltype(masked)::value) pr = ((i <= hi) & ((i < a) | (i > bnd))) ? pr : 0.f;
-            dsv[i] = pr * (dp[kb][i] - di_r);
-          }
-        } else {
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float pr = exp2_fast(__builtin_fmaf(st[kb][i], sl2, -lse2));
-            if constexpr (decltype(masked)::value) pr = i <= hi ? pr : 0.f;
-            dsv[i] = pr * (dp[kb][i] - di_r);
-          }
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 ka = tr_frag<D>(s.k[buf], 32 * kb + 8 * c, db, lane);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) dqa[db][qb] = mfma32(ka, sb[qb][c], dqa[db][qb]);
         }
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          sb[kb][c] = to_bf16x8(dsv[8 * c], dsv[8 * c + 1], dsv[8 * c + 2], dsv[8 * c + 3],
-                                dsv[8 * c + 4], dsv[8 * c + 5], dsv[8 * c + 6], dsv[8 * c + 7]);
-      }
-    };
-    if (need_mask)
-      grad_scores(std::true_type{});
-    else
-      grad_scores(std::false_type{});
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int kb = t >> 1, c = t & 1;
-        const bf16x8 ka = tr_frag<D>(s.k[buf], 32 * kb + 8 * c, db, lane);
-        dqa[db] = mfma32(ka, sb[kb][c], dqa[db]);
-      }
     }
     if (it + 1 < ntiles) {
       tk.store(s.k[buf ^ 1], tid);
@@ -606,24 +629,33 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
     __syncthreads();
   }
 
-  if (row < nq) {
-    __bf16* dst = dq + ((size_t)(sr.q0 + row) * Hq + h) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wrow0 + 32 * qb + l32;
+    if (row < nq) {
+      __bf16* dst = dq + ((size_t)(sr.q0 + row) * Hq + h) * D;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * a + 4 * hh) =
-            to_bf16x4(dqa[db][4 * a] * scale, dqa[db][4 * a + 1] * scale,
-                      dqa[db][4 * a + 2] * scale, dqa[db][4 * a + 3] * scale);
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * a + 4 * hh) =
+              to_bf16x4(dqa[db][qb][4 * a] * scale, dqa[db][qb][4 * a + 1] * scale,
+                        dqa[db][qb][4 * a + 2] * scale, dqa[db][qb][4 * a + 3] * scale);
+    }
   }
 }
+
+// Rows per wave of the dQ blocks: two 32-row blocks at D = 64, one at D = 128
+// (registers).
+template <int D>
+constexpr int dq_qb() { return D == 64 ? 2 : 1; }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(DQ_PARAMS) {
   ATTN_SINK_CHECK_GUARD();
   __shared__ DqLds<D> s;
-  dq_block<D>(s, blockIdx.x, q, k, v, dout, lse, di, dq, cu_q, cu_k, B, Sq, Sk, Hq, Hkv, total_q,
-              hpw, scale, sl2, causal, w1, w2);
+  dq_block<D, dq_qb<D>()>(s, blockIdx.x, q, k, v, dout, lse, di, dq, cu_q, cu_k, B, Sq, Sk, Hq,
+                          Hkv, total_q, hpw, scale, sl2, causal, w1, w2);
 }
 
 // dK/dV and dQ in one launch: workgroups [0, nkv) are the dK/dV blocks in the
@@ -648,8 +680,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_main_kernel(
     dkdv_block<D>(s.kv, w % Hkv, (w / Hkv) % B, w / (Hkv * B), q, k, v, dout, lse, di, dk, dv,
                   cu_q, cu_k, Sq, Sk, Hq, Hkv, total_q, scale, sl2, causal, w1, w2);
   } else {
-    dq_block<D>(s.q, w - nkv, q, k, v, dout, lse, di, dq, cu_q, cu_k, B, Sq, Sk, Hq, Hkv, total_q,
-                hpw, scale, sl2, causal, w1, w2);
+    dq_block<D, dq_qb<D>()>(s.q, w - nkv, q, k, v, dout, lse, di, dq, cu_q, cu_k, B, Sq, Sk, Hq,
+                            Hkv, total_q, hpw, scale, sl2, causal, w1, w2);
   }
 }
 
@@ -686,7 +718,7 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
   const int tq = a.total_q;
   const dim3 pgrid(nblk, a.Hq, a.B);
   const dim3 kgrid(a.Hkv, a.B, (a.Sk + 127) / 128);
-  const dim3 qgrid((unsigned)bwd_dq_workgroups(a.B, a.Sq, a.Hq, a.Hkv));
+  const dim3 qgrid((unsigned)bwd_dq_workgroups(a.B, a.Sq, a.Hq, a.Hkv, a.D));
   const bool rows_q = a.Sq > 0, rows_k = a.Sk > 0;
 #ifdef ATTN_SINK_DEVICE_CHECKS
   if (cq)  // packed query and key offsets

@@ -28,9 +28,9 @@ inline long long index_workgroups(int B, int rows, int Hq, int Hkv, int D) {
   return (long long)B * Hkv * (Hq / Hkv / 4) * ((rows + R - 1) / R);
 }
 // Backward dQ and dK/dV workgroups.
-inline long long bwd_dq_workgroups(int B, int Sq, int Hq, int Hkv) {
+inline long long bwd_dq_workgroups(int B, int Sq, int Hq, int Hkv, int D) {
   const int g = Hq / Hkv, hpw = heads_per_wg(g);
-  const long long R = 32LL * (4 / hpw);
+  const long long R = (D == 64 ? 64LL : 32LL) * (4 / hpw);  // rows per workgroup
   return (long long)B * Hkv * (g / hpw) * ((Sq + R - 1) / R);
 }
 inline long long bwd_dkdv_workgroups(int B, int Sk, int Hkv) {
