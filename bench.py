@@ -197,13 +197,18 @@ def kernel_stats(trace_csv, parts):
               f"{max(v):9.1f} {100 * sum(v) / total:7.2f}")
 
 
-def sq_stats(counter_csv, parts, xcds=8, simds=1024):
-    """MFMA busy fraction, VALU instructions per MFMA and the waves' wait fraction
-    per (bench part, kernel) from the counter_collection.csv of a rocprofv3 run
-    with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, SQ_INSTS_VALU, SQ_WAIT_INST_ANY,
-    SQ_WAVE_CYCLES and GRBM_GUI_ACTIVE: mfma_busy = MFMA busy cycles /
-    (GRBM_GUI_ACTIVE / XCDs * SIMDs); SQ_INSTS_VALU counts the MFMA issues too.
-    The last launch of each (part, kernel) is reported."""
+def sq_stats(counter_csv, parts, xcds=8, simds=1024, cus=256):
+    """Per (bench part, kernel), from the counter_collection.csv of a rocprofv3 SQ
+    counter run (the last launch of each is reported; a metric is shown when its
+    counters were collected):
+      mfma_busy   SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs * SIMDs)
+      valu_act    4 * SQ_ACTIVE_INST_VALU / (same): the SQ's cycle counters tick
+                  once per 4 cycles
+      valu/mfma   SQ_INSTS_VALU / SQ_INSTS_MFMA (SQ_INSTS_VALU counts the MFMA issues)
+      wait        SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES
+      lds_act     4 * SQ_ACTIVE_INST_LDS / (GRBM_GUI_ACTIVE / XCDs * SIMDs)
+      lds_wait    SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES
+      bank_conf   SQ_LDS_BANK_CONFLICT / (GRBM_GUI_ACTIVE / XCDs * CUs)"""
     import csv
     disp = {}
     with open(counter_csv) as f:
@@ -217,16 +222,37 @@ def sq_stats(counter_csv, parts, xcds=8, simds=1024):
     for i, p in zip(ids, labels):
         if p:
             last[(p, disp[i]["name"])] = disp[i]
-    print(f"{'part':9s} {'kernel':34s} {'grid':>9s} {'mfma_busy':>9s} {'MFMA_instr':>10s} "
-          f"{'VALU_instr':>10s} {'valu/mfma':>9s} {'wait/wave_cyc':>13s}")
-    for (p, k), d in last.items():
-        mf, va = d.get("SQ_INSTS_MFMA", 0.0), d.get("SQ_INSTS_VALU", 0.0)
+
+    def metrics(d):
         gui = d.get("GRBM_GUI_ACTIVE", 0.0)
-        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui / xcds * simds) if gui else 0.0
-        wait = d.get("SQ_WAIT_INST_ANY", 0.0) / max(1.0, d.get("SQ_WAVE_CYCLES", 0.0))
-        ratio = f"{va / mf:9.1f}" if mf else f"{'-':>9s}"
-        print(f"{p:9s} {k:34s} {d['grid']:9d} {busy:9.3f} {mf:10.3g} {va:10.3g} {ratio} "
-              f"{wait:13.3f}")
+        simd_cyc = gui / xcds * simds
+        out = {}
+        if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in d:
+            out["mfma_busy"] = d["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cyc
+        if gui and "SQ_ACTIVE_INST_VALU" in d:
+            out["valu_act"] = 4 * d["SQ_ACTIVE_INST_VALU"] / simd_cyc
+        if d.get("SQ_INSTS_MFMA") and "SQ_INSTS_VALU" in d:
+            out["valu/mfma"] = d["SQ_INSTS_VALU"] / d["SQ_INSTS_MFMA"]
+        wave = max(1.0, d.get("SQ_WAVE_CYCLES", 0.0))
+        if "SQ_WAIT_INST_ANY" in d:
+            out["wait"] = d["SQ_WAIT_INST_ANY"] / wave
+        if gui and "SQ_ACTIVE_INST_LDS" in d:
+            out["lds_act"] = 4 * d["SQ_ACTIVE_INST_LDS"] / simd_cyc
+        if "SQ_WAIT_INST_LDS" in d:
+            out["lds_wait"] = d["SQ_WAIT_INST_LDS"] / wave
+        if gui and "SQ_LDS_BANK_CONFLICT" in d:
+            out["bank_conf"] = d["SQ_LDS_BANK_CONFLICT"] / (gui / xcds * cus)
+        return out
+    cols = []
+    for d in last.values():
+        for k in metrics(d):
+            if k not in cols:
+                cols.append(k)
+    print(f"{'part':9s} {'kernel':34s} {'grid':>9s} " + " ".join(f"{c:>9s}" for c in cols))
+    for (p, k), d in last.items():
+        m = metrics(d)
+        print(f"{p:9s} {k:34s} {d['grid']:9d} " +
+              " ".join(f"{m[c]:9.3f}" if c in m else f"{'-':>9s}" for c in cols))
 
 
 def load_traffic():

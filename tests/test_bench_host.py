@@ -89,12 +89,24 @@ def test_sq_summary_formula(tmp_path, capsys):
         w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
         for c, v in vals.items():
             w.writerow([1, "prefill_bf16_kernel<64,2>", 4096, c, v])
+    vals.update({"SQ_ACTIVE_INST_VALU": 1024 * 100.0, "SQ_ACTIVE_INST_LDS": 1024 * 50.0,
+                 "SQ_WAIT_INST_LDS": 10.0, "SQ_LDS_BANK_CONFLICT": 256 * 20.0})
+    with open(p, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        for c, v in vals.items():
+            w.writerow([1, "prefill_bf16_kernel<64,2>", 4096, c, v])
     bench.sq_stats(str(p), ["prefill"])
-    row = [ln for ln in capsys.readouterr().out.splitlines() if ln.startswith("prefill ")][0]
-    f = row.split()
-    assert float(f[3]) == pytest.approx(0.5)     # MFMA busy: 500 of 1000 cycles per SIMD
-    assert float(f[6]) == pytest.approx(12.0)    # VALU instructions per MFMA
-    assert float(f[7]) == pytest.approx(0.3)     # wait fraction
+    lines = capsys.readouterr().out.splitlines()
+    head = lines[0].split()
+    row = dict(zip(head[3:], [ln for ln in lines if ln.startswith("prefill ")][0].split()[3:]))
+    assert float(row["mfma_busy"]) == pytest.approx(0.5)   # 500 of 1000 cycles per SIMD
+    assert float(row["valu_act"]) == pytest.approx(0.4)    # 4 * 100 of 1000 (4-cycle ticks)
+    assert float(row["valu/mfma"]) == pytest.approx(12.0)  # VALU instructions per MFMA
+    assert float(row["wait"]) == pytest.approx(0.3)        # wait fraction
+    assert float(row["lds_act"]) == pytest.approx(0.2)
+    assert float(row["lds_wait"]) == pytest.approx(0.1)
+    assert float(row["bank_conf"]) == pytest.approx(0.02)  # 20 of 1000 cycles per CU
 
 
 def test_causal_pair_count():
