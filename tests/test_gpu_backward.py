@@ -98,12 +98,12 @@ def test_backward_deterministic():
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
 
 
-def test_config5_full_size_sampled():
+def test_training_full_size_sampled():
     """B2, S8192, 64/8 heads, D64, causal: dQ on sampled rows, dK/dV on the last 64 keys
     (only the last rows see them, so the oracle's sub-problem with those rows is exact),
     dSink of two heads over both sequences."""
     need_gpu()
-    say("case: config5 full size B2 S8192 H64/8 D64 causal")
+    say("case: training fwd+bwd full size B2 S8192 H64/8 D64 causal")
     B, S, Hq, Hkv, D = 2, 8192, 64, 8, 64
     scale = 0.125
     case = synth.prefill_case(B, S, S, Hq, Hkv, D, seed=0, dout=True)

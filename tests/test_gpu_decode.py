@@ -228,10 +228,10 @@ def test_select_slots_and_gather_bit_exact(P, window):
         assert np.all(ko_h[b, n:] == 0) and np.all(vo_h[b, n:] == 0)
 
 
-def test_config3_full_size():
+def test_paged_decode_full_size():
     """B64, 64/8 heads, D64, P16, L ~ U[1024, 32768], random page permutation, sink N(0,1)."""
     need_gpu()
-    say("case: config3 full size B64 H64/8 D64 P16 L[1024,32768]")
+    say("case: paged decode full size B64 H64/8 D64 P16 L[1024,32768]")
     case = synth.decode_case(64, 64, 8, 64, 16, 1024, 32768, seed=0)
     d = _dev(case)
     o, lse = _decode(d, 0.125, None)
@@ -242,12 +242,12 @@ def test_config3_full_size():
 
 @pytest.mark.parametrize("B", [1, 32])
 @pytest.mark.parametrize("use_sink", [False, True])
-def test_config4_full_size(B, use_sink):
+def test_window_decode_full_size(B, use_sink):
     """32/8 heads, D128, P16, window 1024+7168, L ~ U[16384, 65536]; unselected tokens
     hold NaN, so any read outside the selection shows up; selection checked bit-exact."""
     need_gpu()
     from softmax_learnable_sink_amd import binding
-    say(f"case: config4 full size B{B} sink={use_sink}")
+    say(f"case: window decode full size B{B} sink={use_sink}")
     w = (1024, 7168)
     case = synth.decode_case(B, 32, 8, 128, 16, 16384, 65536, seed=0, sink=use_sink)
     poison_unselected(case, w)

@@ -32,7 +32,7 @@ def _oracle(case, scale, causal, window, use_sink=True):
                           scale, causal=causal, window=window)
 
 
-def test_config1_fp32_tiny():
+def test_fp32_tiny_workload():
     """B1, S128, 2 heads / 2 KV heads, D64, causal, fp32, scale 1/8, seed 0: <= 1e-5."""
     need_gpu()
     say("case: fp32 B1 S128 H2/2 D64 causal seed0")
@@ -115,12 +115,12 @@ def test_prefill_deterministic():
     assert torch.equal(l1, l2)
 
 
-def test_config2_full_size_sampled_rows():
+def test_gqa_prefill_full_size_sampled_rows():
     """B4, S4096, 64/8 heads, D64, causal, bf16 -- sampled rows against the oracle."""
     need_gpu()
     from softmax_learnable_sink_amd import binding
     B, S, Hq, Hkv, D = 4, 4096, 64, 8, 64
-    say("case: config2 full size B4 S4096 H64/8 D64 causal")
+    say("case: GQA prefill full size B4 S4096 H64/8 D64 causal")
     case = synth.prefill_case(B, S, S, Hq, Hkv, D, seed=0)
     q, k, v = (dev_tensor(case[n], synth.BF16) for n in ("q", "k", "v"))
     sink = torch.from_numpy(case["sink"]).cuda()
