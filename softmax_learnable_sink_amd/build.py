@@ -86,6 +86,18 @@ def build_sanitized(out):
     return out
 
 
+def device_asm(source, out):
+    """Compile one HIP source's gfx950 device code to assembly text at `out`
+    (the release build's flags), for checks of the generated code."""
+    flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [hipcc(), *flags, "--cuda-device-only", "-S", "-I", INCLUDE, "-I", CSRC,
+           os.path.join(CSRC, source), "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+    return out
+
+
 def asan_runtime():
     """Path of the ASan runtime library of hipcc's clang."""
     res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],

@@ -11,7 +11,8 @@
 // kernels: its gradient is a by-product of the Di pass.
 //
 // Kernels (all deterministic, no atomics):
-//   bwd_preprocess   Di and per-(b, h, 64-row block) dSink partials
+//   bwd_preprocess   -Di, LSE * log2(e) and per-(b, h, 64-row block) dSink
+//                    partials
 //   bwd_dkdv         KV-stationary: a wave owns 32 keys and accumulates dK/dV
 //                    over all query heads of its GQA group and all query tiles
 //                    that can see them
@@ -32,8 +33,6 @@ constexpr int kThreads = 256;
 constexpr int kTile = 64;  // rows per query tile / keys per KV tile
 constexpr int kPad = 8;    // LDS row padding (elements, 16 B)
 
-__device__ __forceinline__ int perm_row(int j) { return ((j & 15) >> 2) * 8 + (j >> 4) * 4 + (j & 3); }
-__device__ __forceinline__ int lds_row(int j) { return (j & ~31) + perm_row(j & 31); }
 
 __device__ __forceinline__ uint32_t pick16(const uint4& x, int e) {
   const uint32_t w = e < 2 ? x.x : (e < 4 ? x.y : (e < 6 ? x.z : x.w));
@@ -41,54 +40,32 @@ __device__ __forceinline__ uint32_t pick16(const uint4& x, int e) {
 }
 
 // A operand (32 d x 16 rows) of an MFMA that contracts over tile rows, read
-// from a natural-layout tile (rows permuted within 32-blocks, see lds_row):
-// lane l gets d = 32*db + l%32 and logical rows r0 + 16*(l/32) .. +7.
-// ds_read_b64_tr_b16 hands lane i of each 16-lane group element i%4 of the
-// 4-element vectors that lanes 4j + i/4 (j = 0..3) of the group addressed, in
-// order of j; so lane s of a group addresses logical row (base + 4h + s/4),
-// columns (dbase + 4*(s%4)) .. +3, for the two loads h = 0, 1.
+// from a natural-layout tile (rows permuted within 32-blocks by perm_row):
+// lane l gets d = 32*db + l%32 and logical rows r0 + 16*(l/32) .. +7 (r0 a
+// multiple of 8).  ds_read_b64_tr_b16 hands lane i of each 16-lane group
+// element i%4 of the 4-element vectors that lanes 4j + i/4 (j = 0..3) of the
+// group addressed, in order of j; so lane s of a group addresses logical row
+// (r0 + 16*hh + 4h + s/4), columns (32*db + 16*gg + 4*(s%4)) .. +3, for the
+// two loads h = 0, 1.  Under perm_row those rows sit at LDS rows
+// (r0 & ~31) + 2*(r0 & 31) + 4*hh + s/4 + 8h.  The lane's part and the
+// constant part of the address are added once, so that the compiler keeps
+// the read tied to its LDS buffer (see the tile loads in common.h).
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 template <int D>
 __device__ __forceinline__ bf16x8 tr_frag(const __bf16* nat, int r0, int db, int lane) {
   constexpr int NS = D + kPad;
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   const int sl = lane & 15, gg = (lane >> 4) & 1, hh = lane >> 5;
-  const int col = 32 * db + 16 * gg + 4 * (sl & 3);
-  const int ra = r0 + 16 * hh + (sl >> 2);
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(nat + lds_row(ra) * NS + col));
-  const i16x4 b =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(nat + lds_row(ra + 4) * NS + col));
+  const int ol = (4 * hh + (sl >> 2)) * NS + 16 * gg + 4 * (sl & 3);
+  const int oc = ((r0 & ~31) + 2 * (r0 & 31)) * NS + 32 * db;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(nat + (ol + oc)));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(nat + (ol + oc + 8 * NS)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// 64 rows x D tile stored in natural layout only (rows permuted).
-template <int D>
-struct RowTile {
-  static constexpr int CH = D / 8;
-  static constexpr int N = kTile * CH / kThreads;
-  uint4 r[N];
-  uint32_t off[N];
-  __device__ __forceinline__ void init(size_t rs, int tid) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = tid + i * kThreads;
-      off[i] = (uint32_t)(((size_t)(idx / CH) * rs + 8 * (idx % CH)) * 2);
-    }
-  }
-  __device__ __forceinline__ void load(const __bf16* base, size_t rs, int row0, int nrows) {
-    const auto rsrc = make_rsrc(base + (size_t)row0 * rs, (uint32_t)((size_t)(nrows - row0) * rs * 2));
-#pragma unroll
-    for (int i = 0; i < N; ++i) r[i] = buf_load16(rsrc, off[i]);
-  }
-  __device__ __forceinline__ void store(__bf16* nat, int tid) const {
-    constexpr int NS = D + kPad;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = tid + i * kThreads;
-      *reinterpret_cast<uint4*>(nat + lds_row(idx / CH) * NS + 8 * (idx % CH)) = r[i];
-    }
-  }
-};
+// LDS tile buffers per pass: K/V or Q/dO tiles are loaded straight into LDS
+// one tile ahead of the one in use.
+constexpr int kBwdBufs = 2;
 
 // Rows of sequence b.  A dense batch (cu_q == NULL) has Sq query and Sk key
 // rows per sequence and LSE laid out [B, Hq, Sq]; a packed variable-length
@@ -107,14 +84,17 @@ __device__ __forceinline__ SeqRows seq_rows(const int32_t* cu_q, const int32_t* 
 }
 
 // ---------------------------------------------------------------------------
-// Di = <dO_i, O_i> and dSink partials.  Grid (ceil(Sq/64), Hq, B); 4 threads
-// per row.
+// Di = <dO_i, O_i> (stored negated: the dK/dV pass starts its dP
+// accumulators from it), LSE_i * log2(e) (the exponent offset of the base-2
+// probabilities) and dSink partials.  Grid (ceil(Sq/64), Hq, B); 4 threads per
+// row.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
     const __bf16* __restrict__ o, const __bf16* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ sink, float* __restrict__ di, float* __restrict__ dsink_part,
-    const int32_t* __restrict__ cu_q, int Sq, int Hq, int total_q) {
+    const float* __restrict__ sink, float* __restrict__ ndi, float* __restrict__ lse2,
+    float* __restrict__ dsink_part, const int32_t* __restrict__ cu_q, int Sq, int Hq,
+    int total_q) {
   ATTN_SINK_CHECK_GUARD();
   constexpr int PER = D / 4;  // elements per thread
   const int tid = threadIdx.x;
@@ -139,12 +119,13 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(
   float contrib = 0.f;
   if (row < sr.nq && part == 0) {
     const size_t x = sr.l0 + h * sr.lh + row;
-    di[x] = acc;
+    const float L = lse[x];
+    ndi[x] = -acc;
+    lse2[x] = L * kLog2e;
     if (sink) {
       // a head whose sink is -inf contributes nothing, also on rows that see
       // no key (LSE = -inf there, and -inf - -inf would be NaN)
       const float sh = sink[h];
-      const float L = lse[x];
       contrib = sh == kNegInf ? 0.f : -exp2_fast((sh - L) * kLog2e) * acc;
     }
   }
@@ -188,26 +169,31 @@ __global__ __launch_bounds__(kThreads) void bwd_dsink_reduce_kernel(
 //   dV^T += dO^T P,  dK^T += Q^T dS (A = dO^T, Q^T from LDS, transposed)
 // Lane (hh, l32) holds key l32 and query rows 32*qb + 16*hh + i.
 // ---------------------------------------------------------------------------
+// One tile buffer of the dK/dV pass: 64 rows of Q and of dO (rows permuted,
+// the tile-load layout) and the rows' LSE * log2(e) and -Di.
 template <int D>
-struct DkdvLds {
-  __bf16 q[2][kTile * (D + kPad)];
-  __bf16 dO[2][kTile * (D + kPad)];
-  alignas(16) float lse2[2][kTile];
-  alignas(16) float di[2][kTile];  // -Di of the tile's rows
+struct DkdvTile {
+  __bf16 q[kTile * (D + kPad)];
+  __bf16 dO[kTile * (D + kPad)];
+  alignas(16) float lse2[kTile];
+  alignas(16) float ndi[kTile];
 };
 
 #define DKDV_PARAMS                                                                             \
   const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,     \
-      const __bf16 *__restrict__ dout, const float *__restrict__ lse,                           \
-      const float *__restrict__ di, __bf16 *__restrict__ dk, __bf16 *__restrict__ dv,           \
+      const __bf16 *__restrict__ dout, const float *__restrict__ lse2,                          \
+      const float *__restrict__ ndi, __bf16 *__restrict__ dk, __bf16 *__restrict__ dv,          \
       const int32_t *__restrict__ cu_q, const int32_t *__restrict__ cu_k, int Sq, int Sk, int Hq, \
       int Hkv, int total_q, float scale, float sl2, int causal, int w1, int w2
 
-// Work block (kvh, b, kb): (KV head, sequence, block of 128 keys).
-template <int D>
-__device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb, DKDV_PARAMS) {
+// Work block (kvh, b, kb): (KV head, sequence, block of 128 keys); t0 .. t2
+// are the LDS tile buffers (NB of them; t2 unused when NB = 2).
+template <int D, int NB>
+__device__ __forceinline__ void dkdv_block(DkdvTile<D>& t0, DkdvTile<D>& t1, DkdvTile<D>& t2,
+                                           int kvh, int b, int kb, DKDV_PARAMS) {
   constexpr int NS = D + kPad;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loads and LDS bases
   const int hh = lane >> 5, l32 = lane & 31;
   const int g = Hq / Hkv;
   const SeqRows sr = seq_rows(cu_q, cu_k, b, Sq, Sk, Hq, total_q);
@@ -248,10 +234,6 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
   const int niter = ntq * g;
 
   const size_t rs = (size_t)Hq * D;
-  RowTile<D> tq, tdo;
-  tq.init(rs, tid);
-  tdo.init(rs, tid);
-  float lse_r = 0.f, di_r = 0.f;
   // iteration -> (query head, query tile): the last query tile first, all heads
   // of the group for each tile.  Every key block's range of tiles ends at the
   // sequence's last tile, so the key blocks of one KV head that run together
@@ -261,40 +243,55 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
   // first tile first, head by head; the time is the same.
   auto head_of = [&](int it) { return kvh * g + it % g; };
   auto row_of = [&](int it) { return (t_hi - 1 - it / g) * kTile; };
-  auto load_iter = [&](int it) {
-    const int h = head_of(it);
-    const int i0 = row_of(it);
-    const size_t base = ((size_t)sr.q0 * Hq + h) * D;
-    tq.load(q + base, rs, i0, nq);
-    tdo.load(dout + base, rs, i0, nq);
-    // per-row LSE and Di of the tile (zero past the last row)
-    const size_t x = sr.l0 + h * sr.lh + i0;
-    const uint32_t nb = (uint32_t)(nq - i0) * 4;
-    lse_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                          make_rsrc(lse + x, nb), (tid & 63) * 4, 0, 0));
-    di_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                         make_rsrc(di + x, nb), (tid & 63) * 4, 0, 0));
-  };
-  auto store_iter = [&](int buf) {
-    tq.store(s.q[buf], tid);
-    tdo.store(s.dO[buf], tid);
-    if (tid < kTile) {
-      s.lse2[buf][tid] = lse_r * kLog2e;
-      s.di[buf][tid] = -di_r;  // the dP accumulators start at -Di
+
+  // Tile loads straight into LDS: SP 1 KB loads of Q and SP of dO (rows
+  // permuted), 256 B of LSE * log2(e) and of -Di.  Waves 0 and 1 load Q,
+  // waves 2 and 3 dO, each every other load j = (wave & 1) + 2u; SP is odd,
+  // so the odd waves' last load (j = SP) is the row vector instead (wave 1
+  // the LSE, wave 3 -Di).  Every wave issues U loads per tile.
+  constexpr int SP = kDmaSlots(D), U = (SP + 1) / 2;
+  static_assert(SP % 2 == 1, "odd slot count per row");
+  const bool wq = wave < 2;
+  uint32_t doff[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = (wave & 1) + 2 * u;
+    doff[u] = j < SP ? dma_offset<D>(j, lane, (uint32_t)(rs * 2), true) : 4u * lane;
+  }
+  // iteration it into buffer t; past the last iteration the loads read an
+  // empty resource, so that every step issues the same loads
+  auto request = [&](int it, DkdvTile<D>& t) {
+    int h = 0, i0 = 0, nrow = 0;
+    if (it < niter) {
+      h = head_of(it);
+      i0 = row_of(it);
+      nrow = nq - i0;
+    }
+    const auto rt = make_rsrc((wq ? q : dout) + ((size_t)sr.q0 * Hq + h) * D + (size_t)i0 * rs,
+                              (uint32_t)((size_t)nrow * rs * 2));
+    const auto rr = make_rsrc((wq ? lse2 : ndi) + sr.l0 + h * sr.lh + i0, (uint32_t)nrow * 4u);
+    __bf16* dst = wq ? t.q : t.dO;
+    float* dstr = wq ? t.lse2 : t.ndi;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if ((wave & 1) + 2 * u < SP)
+        dma16(rt, dst + 512 * ((wave & 1) + 2 * u), doff[u]);
+      else
+        dma4(rr, dstr, doff[u]);
     }
   };
 
-  __builtin_amdgcn_s_waitcnt(0);
-  if (niter > 0) {
-    load_iter(0);
-    store_iter(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < niter; ++it) {
-    const int buf = it & 1;
+  // One step: wait until iteration it's tile has landed (the next NB - 2
+  // tiles' loads may stay in flight); after the barrier it has for every
+  // wave, and every wave is done with the previous tile's buffer, which the
+  // request overwrites.  Steps past the last iteration only keep the loads and
+  // waits uniform.
+  auto step = [&](int it, DkdvTile<D>& cur, DkdvTile<D>& ahead) {
+    wait_vmcnt<(NB - 2) * U>();
+    tile_barrier();
+    request(it + NB - 1, ahead);
+    if (it >= niter) return;
     const int i0 = row_of(it);
-    if (it + 1 < niter) load_iter(it + 1);
     const int p0 = off + i0;
     const bool need_mask = (i0 + kTile > nq) || (causal && p0 < k1 - 1) ||
                            (w2 > 0 && k1 - 1 >= w1 && p0 + kTile - 1 - w2 >= k0);
@@ -318,7 +315,7 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
         const f32x4 d2 =
-            *reinterpret_cast<const f32x4*>(&s.di[buf][32 * qb + 16 * hh + 4 * c4]);
+            *reinterpret_cast<const f32x4*>(&cur.ndi[32 * qb + 16 * hh + 4 * c4]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) pa[qb][4 * c4 + e] = d2[e];
       }
@@ -328,8 +325,8 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int r = (32 * qb + l32) * NS + 16 * ks + 8 * hh;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&s.q[buf][r]);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(&s.dO[buf][r]);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&cur.q[r]);
+        const bf16x8 da = *reinterpret_cast<const bf16x8*>(&cur.dO[r]);
         sa[qb] = mfma32(qa, kf[ks], sa[qb]);
         pa[qb] = mfma32(da, vf[ks], pa[qb]);
       }
@@ -353,7 +350,7 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
         float pv[16], dsv[16];
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(&s.lse2[buf][rbase + 4 * c4]);
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&cur.lse2[rbase + 4 * c4]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * c4 + e;
@@ -379,17 +376,32 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
       for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const bf16x8 dot = tr_frag<D>(s.dO[buf], 32 * qb + 8 * c, db, lane);
-          const bf16x8 qt = tr_frag<D>(s.q[buf], 32 * qb + 8 * c, db, lane);
+          const bf16x8 dot = tr_frag<D>(cur.dO, 32 * qb + 8 * c, db, lane);
+          const bf16x8 qt = tr_frag<D>(cur.q, 32 * qb + 8 * c, db, lane);
           dva[db] = mfma32(dot, pb[c], dva[db]);
           dka[db] = mfma32(qt, sb[c], dka[db]);
         }
       }
     }
+  };
 
-    if (it + 1 < niter) store_iter(buf ^ 1);
-    __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0);  // the K^T / V^T fragments
+  request(0, t0);
+  if constexpr (NB == 3) {
+    request(1, t1);
+    for (int it = 0; it < niter; it += 3) {
+      step(it, t0, t2);
+      step(it + 1, t1, t0);
+      step(it + 2, t2, t1);
+    }
+  } else {
+    for (int it = 0; it < niter; it += 2) {
+      step(it, t0, t1);
+      step(it + 1, t1, t0);
+    }
   }
+  // no load may still write this workgroup's LDS when it exits
+  wait_vmcnt<0>();
 
   if (key < nk) {
     const size_t base = ((size_t)(sr.k0 + key) * Hkv + kvh) * D;
@@ -412,9 +424,17 @@ __device__ __forceinline__ void dkdv_block(DkdvLds<D>& s, int kvh, int b, int kb
 template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(DKDV_PARAMS) {
   ATTN_SINK_CHECK_GUARD();
-  __shared__ DkdvLds<D> s;
-  dkdv_block<D>(s, blockIdx.x, blockIdx.y, blockIdx.z, q, k, v, dout, lse, di, dk, dv, cu_q, cu_k,
-                Sq, Sk, Hq, Hkv, total_q, scale, sl2, causal, w1, w2);
+  // one LDS variable per tile buffer, so that the compiler can tell the
+  // buffer a load in flight writes from the one being read
+  __shared__ DkdvTile<D> t0, t1;
+  if constexpr (kBwdBufs == 3) {
+    __shared__ DkdvTile<D> t2;
+    dkdv_block<D, 3>(t0, t1, t2, blockIdx.x, blockIdx.y, blockIdx.z, q, k, v, dout, lse2, ndi, dk,
+                     dv, cu_q, cu_k, Sq, Sk, Hq, Hkv, total_q, scale, sl2, causal, w1, w2);
+  } else {
+    dkdv_block<D, 2>(t0, t1, t0, blockIdx.x, blockIdx.y, blockIdx.z, q, k, v, dout, lse2, ndi, dk,
+                     dv, cu_q, cu_k, Sq, Sk, Hq, Hkv, total_q, scale, sl2, causal, w1, w2);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -424,10 +444,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(DKD
 //   S^T = K Q^T, dP^T = V dO^T (A = K, V from LDS natural layout)
 //   dS^T = P^T (dP^T - Di),  dQ^T += K^T dS^T (A = K^T from LDS transposed)
 // ---------------------------------------------------------------------------
+// One tile buffer of the dQ pass: 64 keys of K and V (rows permuted, the
+// tile-load layout).
 template <int D>
-struct DqLds {
-  __bf16 k[2][kTile * (D + kPad)];
-  __bf16 v[2][kTile * (D + kPad)];
+struct DqTile {
+  __bf16 k[kTile * (D + kPad)];
+  __bf16 v[kTile * (D + kPad)];
 };
 
 struct QRange {
@@ -459,8 +481,8 @@ __device__ __forceinline__ QRange kv_tiles(int Sk, int p_min, int p_max, int cau
 
 #define DQ_PARAMS                                                                               \
   const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,     \
-      const __bf16 *__restrict__ dout, const float *__restrict__ lse,                           \
-      const float *__restrict__ di, __bf16 *__restrict__ dq, const int32_t *__restrict__ cu_q,  \
+      const __bf16 *__restrict__ dout, const float *__restrict__ lse2,                          \
+      const float *__restrict__ ndi, __bf16 *__restrict__ dq, const int32_t *__restrict__ cu_q, \
       const int32_t *__restrict__ cu_k, int B, int Sq, int Sk, int Hq, int Hkv, int total_q,     \
       int hpw, float scale, float sl2, int causal, int w1, int w2
 
@@ -468,11 +490,13 @@ __device__ __forceinline__ QRange kv_tiles(int Sk, int p_min, int p_max, int cau
 // A wave owns 32*QB rows of one head: with QB = 2 every K, V and K^T fragment
 // read from LDS feeds two MFMAs (one per 32-row block), which halves the LDS
 // traffic per MFMA; the transposing K^T reads are the slowest LDS reads.
-template <int D, int QB>
-__device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
+template <int D, int QB, int NB>
+__device__ __forceinline__ void dq_block(DqTile<D>& t0, DqTile<D>& t1, DqTile<D>& t2, int w,
+                                         DQ_PARAMS) {
   constexpr int NS = D + kPad;
   constexpr int RW = 32 * QB;  // rows per wave
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loads and LDS bases
   const int hh = lane >> 5, l32 = lane & 31;
   const int g = Hq / Hkv;
   const int groups = g / hpw;
@@ -491,14 +515,14 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
   const int p_max = off + min(nq, row0 + R) - 1;
 
   // per row block qb: this lane's row wrow0 + 32*qb + l32, its Q / dO
-  // fragments, LSE (log2 units) and Di
+  // fragments, LSE (log2 units) and -Di
   bf16x8 qf[QB][D / 16], of[QB][D / 16];
-  float lse2[QB], di_r[QB];
+  float l2r[QB], ndi_r[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + 32 * qb + l32;
-    di_r[qb] = 0.f;
-    lse2[qb] = 0.f;
+    ndi_r[qb] = 0.f;
+    l2r[qb] = 0.f;
     if (row < nq) {
       const size_t base = ((size_t)(sr.q0 + row) * Hq + h) * D + 8 * hh;
 #pragma unroll
@@ -506,8 +530,8 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
         qf[qb][ks] = *reinterpret_cast<const bf16x8*>(q + base + 16 * ks);
         of[qb][ks] = *reinterpret_cast<const bf16x8*>(dout + base + 16 * ks);
       }
-      lse2[qb] = lse[sr.l0 + h * sr.lh + row] * kLog2e;
-      di_r[qb] = di[sr.l0 + h * sr.lh + row];
+      l2r[qb] = lse2[sr.l0 + h * sr.lh + row];
+      ndi_r[qb] = ndi[sr.l0 + h * sr.lh + row];
     } else {
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
@@ -527,25 +551,37 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
   const size_t rs = (size_t)Hkv * D;
   const __bf16* kbase = k + ((size_t)sr.k0 * Hkv + kvh) * D;
   const __bf16* vbase = v + ((size_t)sr.k0 * Hkv + kvh) * D;
-  RowTile<D> tk, tv;
-  tk.init(rs, tid);
-  tv.init(rs, tid);
-  __builtin_amdgcn_s_waitcnt(0);
-  if (ntiles > 0) {
-    tk.load(kbase, rs, tr.tile(0) * kTile, nk);
-    tv.load(vbase, rs, tr.tile(0) * kTile, nk);
-    tk.store(s.k[0], tid);
-    tv.store(s.v[0], tid);
+  // K/V tiles straight into LDS (rows permuted): waves 0 and 1 load K, waves
+  // 2 and 3 V, every other 1 KB load j = (wave & 1) + 2u; SP is odd, so the
+  // odd waves repeat their last load (same data to the same slots) and every
+  // wave issues U loads per tile.
+  constexpr int SP = kDmaSlots(D), U = (SP + 1) / 2;
+  static_assert(SP % 2 == 1, "odd slot count per row");
+  const bool wk = wave < 2;
+  uint32_t doff[U], dlds[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = (wave & 1) + 2 * u < SP ? (wave & 1) + 2 * u : (wave & 1) + 2 * u - 2;
+    doff[u] = dma_offset<D>(j, lane, (uint32_t)(rs * 2), true);
+    dlds[u] = 512 * j;  // elements
   }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
+  // tile it into buffer t; past the last tile the loads read an empty
+  // resource, so that every step issues the same loads
+  auto request = [&](int it, DqTile<D>& t) {
+    const int key0 = it < ntiles ? tr.tile(it) * kTile : 0;
+    const uint32_t bytes = it < ntiles ? (uint32_t)((size_t)(nk - key0) * rs * 2) : 0u;
+    const auto r = make_rsrc((wk ? kbase : vbase) + (size_t)key0 * rs, bytes);
+    __bf16* dst = wk ? t.k : t.v;
+#pragma unroll
+    for (int u = 0; u < U; ++u) dma16(r, dst + dlds[u], doff[u]);
+  };
+  // One step: as in the dK/dV pass.
+  auto step = [&](int it, DqTile<D>& cur, DqTile<D>& ahead) {
+    wait_vmcnt<(NB - 2) * U>();
+    tile_barrier();
+    request(it + NB - 1, ahead);
+    if (it >= ntiles) return;
     const int key0 = tr.tile(it) * kTile;
-    if (it + 1 < ntiles) {
-      tk.load(kbase, rs, tr.tile(it + 1) * kTile, nk);
-      tv.load(vbase, rs, tr.tile(it + 1) * kTile, nk);
-    }
     const bool need_mask = (key0 + kTile > nk) || (causal && key0 + kTile - 1 > p_min) ||
                            (w2 > 0 && key0 + kTile - 1 >= w1 && key0 <= p_max - w2) ||
                            (row0 + R > nq);
@@ -557,8 +593,8 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const int r = (32 * kb + l32) * NS + 16 * ks + 8 * hh;
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&s.k[buf][r]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&s.v[buf][r]);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&cur.k[r]);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&cur.v[r]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           st[qb] = mfma32(ka, qf[qb][ks], ks == 0 ? f32x16{} : st[qb]);
@@ -589,17 +625,17 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
           if (w2 > 0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              float pr = exp2_fast(__builtin_fmaf(st[qb][i], sl2, -lse2[qb]));
+              float pr = exp2_fast(__builtin_fmaf(st[qb][i], sl2, -l2r[qb]));
               if constexpr (decltype(masked)::value)
                 pr = ((i <= hi) & ((i < a) | (i > bnd))) ? pr : 0.f;
-              dsv[i] = pr * (dp[qb][i] - di_r[qb]);
+              dsv[i] = pr * (dp[qb][i] + ndi_r[qb]);
             }
           } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              float pr = exp2_fast(__builtin_fmaf(st[qb][i], sl2, -lse2[qb]));
+              float pr = exp2_fast(__builtin_fmaf(st[qb][i], sl2, -l2r[qb]));
               if constexpr (decltype(masked)::value) pr = i <= hi ? pr : 0.f;
-              dsv[i] = pr * (dp[qb][i] - di_r[qb]);
+              dsv[i] = pr * (dp[qb][i] + ndi_r[qb]);
             }
           }
 #pragma unroll
@@ -617,17 +653,30 @@ __device__ __forceinline__ void dq_block(DqLds<D>& s, int w, DQ_PARAMS) {
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const bf16x8 ka = tr_frag<D>(s.k[buf], 32 * kb + 8 * c, db, lane);
+          const bf16x8 ka = tr_frag<D>(cur.k, 32 * kb + 8 * c, db, lane);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) dqa[db][qb] = mfma32(ka, sb[qb][c], dqa[db][qb]);
         }
     }
-    if (it + 1 < ntiles) {
-      tk.store(s.k[buf ^ 1], tid);
-      tv.store(s.v[buf ^ 1], tid);
+  };
+
+  __builtin_amdgcn_s_waitcnt(0);  // the Q / dO fragments, LSE and Di
+  request(0, t0);
+  if constexpr (NB == 3) {
+    request(1, t1);
+    for (int it = 0; it < ntiles; it += 3) {
+      step(it, t0, t2);
+      step(it + 1, t1, t0);
+      step(it + 2, t2, t1);
     }
-    __syncthreads();
+  } else {
+    for (int it = 0; it < ntiles; it += 2) {
+      step(it, t0, t1);
+      step(it + 1, t1, t0);
+    }
   }
+  // no load may still write this workgroup's LDS when it exits
+  wait_vmcnt<0>();
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -653,10 +702,23 @@ constexpr int dq_qb() { return D == 64 ? 2 : 1; }
 template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(DQ_PARAMS) {
   ATTN_SINK_CHECK_GUARD();
-  __shared__ DqLds<D> s;
-  dq_block<D, dq_qb<D>()>(s, blockIdx.x, q, k, v, dout, lse, di, dq, cu_q, cu_k, B, Sq, Sk, Hq,
-                          Hkv, total_q, hpw, scale, sl2, causal, w1, w2);
+  __shared__ DqTile<D> t0, t1;  // one LDS variable per tile buffer
+  if constexpr (kBwdBufs == 3) {
+    __shared__ DqTile<D> t2;
+    dq_block<D, dq_qb<D>(), 3>(t0, t1, t2, blockIdx.x, q, k, v, dout, lse2, ndi, dq, cu_q, cu_k,
+                               B, Sq, Sk, Hq, Hkv, total_q, hpw, scale, sl2, causal, w1, w2);
+  } else {
+    dq_block<D, dq_qb<D>(), 2>(t0, t1, t0, blockIdx.x, q, k, v, dout, lse2, ndi, dq, cu_q, cu_k,
+                               B, Sq, Sk, Hq, Hkv, total_q, hpw, scale, sl2, causal, w1, w2);
+  }
 }
+
+// One tile buffer of the one-launch backward: a workgroup runs either pass.
+template <int D>
+union BwdTile {
+  DkdvTile<D> kv;
+  DqTile<D> q;
+};
 
 // dK/dV and dQ in one launch: workgroups [0, nkv) are the dK/dV blocks in the
 // order of bwd_dkdv_kernel's grid (KV head fastest, key block slowest), the
@@ -665,23 +727,33 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(DQ_PA
 template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_main_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
-    __bf16* __restrict__ dq, __bf16* __restrict__ dk, __bf16* __restrict__ dv,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int B, int Sq, int Sk,
-    int Hq, int Hkv, int total_q, int hpw, float scale, float sl2, int causal, int w1, int w2,
-    int nkv) {
+    const __bf16* __restrict__ dout, const float* __restrict__ lse2,
+    const float* __restrict__ ndi, __bf16* __restrict__ dq, __bf16* __restrict__ dk,
+    __bf16* __restrict__ dv, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    int B, int Sq, int Sk, int Hq, int Hkv, int total_q, int hpw, float scale, float sl2,
+    int causal, int w1, int w2, int nkv) {
   ATTN_SINK_CHECK_GUARD();
-  __shared__ union {
-    DkdvLds<D> kv;
-    DqLds<D> q;
-  } s;
+  __shared__ BwdTile<D> t0, t1;  // one LDS variable per tile buffer
   const int w = blockIdx.x;
-  if (w < nkv) {
-    dkdv_block<D>(s.kv, w % Hkv, (w / Hkv) % B, w / (Hkv * B), q, k, v, dout, lse, di, dk, dv,
-                  cu_q, cu_k, Sq, Sk, Hq, Hkv, total_q, scale, sl2, causal, w1, w2);
+  if constexpr (kBwdBufs == 3) {
+    __shared__ BwdTile<D> t2;
+    if (w < nkv)
+      dkdv_block<D, 3>(t0.kv, t1.kv, t2.kv, w % Hkv, (w / Hkv) % B, w / (Hkv * B), q, k, v, dout,
+                       lse2, ndi, dk, dv, cu_q, cu_k, Sq, Sk, Hq, Hkv, total_q, scale, sl2,
+                       causal, w1, w2);
+    else
+      dq_block<D, dq_qb<D>(), 3>(t0.q, t1.q, t2.q, w - nkv, q, k, v, dout, lse2, ndi, dq, cu_q,
+                                 cu_k, B, Sq, Sk, Hq, Hkv, total_q, hpw, scale, sl2, causal, w1,
+                                 w2);
   } else {
-    dq_block<D, dq_qb<D>()>(s.q, w - nkv, q, k, v, dout, lse, di, dq, cu_q, cu_k, B, Sq, Sk, Hq,
-                            Hkv, total_q, hpw, scale, sl2, causal, w1, w2);
+    if (w < nkv)
+      dkdv_block<D, 2>(t0.kv, t1.kv, t0.kv, w % Hkv, (w / Hkv) % B, w / (Hkv * B), q, k, v, dout,
+                       lse2, ndi, dk, dv, cu_q, cu_k, Sq, Sk, Hq, Hkv, total_q, scale, sl2,
+                       causal, w1, w2);
+    else
+      dq_block<D, dq_qb<D>(), 2>(t0.q, t1.q, t0.q, w - nkv, q, k, v, dout, lse2, ndi, dq, cu_q,
+                                 cu_k, B, Sq, Sk, Hq, Hkv, total_q, hpw, scale, sl2, causal, w1,
+                                 w2);
   }
 }
 
@@ -689,9 +761,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_main_kernel(
 
 size_t backward_workspace_bytes(int B, int max_sq, int Hq, size_t rows) {
   const size_t nblk = (size_t)(max_sq + 63) / 64;
-  const size_t di = (size_t)Hq * rows;
+  const size_t di = (size_t)Hq * rows;  // -Di, and as many LSE * log2(e)
   const size_t part = (size_t)B * Hq * nblk;
-  return (di + part) * sizeof(float);
+  return (2 * di + part) * sizeof(float);
 }
 
 // Dense batches: Sq, Sk are every sequence's lengths and cu arrays are NULL.
@@ -703,8 +775,11 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
   const float sl2 = a.scale * kLog2e;
   const int nblk = (a.Sq + 63) / 64;
   const size_t rows = a.cu_seqlens_q ? (size_t)a.total_q : (size_t)a.B * a.Sq;
-  float* di = static_cast<float*>(a.workspace);
-  float* part = di + (size_t)a.Hq * rows;
+  // workspace: -Di and LSE * log2(e) ([Hq, rows] each, in the LSE layout),
+  // then the dSink partials
+  float* ndi = static_cast<float*>(a.workspace);
+  float* lse2 = ndi + (size_t)a.Hq * rows;
+  float* part = lse2 + (size_t)a.Hq * rows;
   const auto* q = static_cast<const __bf16*>(a.q);
   const auto* k = static_cast<const __bf16*>(a.k);
   const auto* v = static_cast<const __bf16*>(a.v);
@@ -727,35 +802,35 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
 #endif
   if (a.D == 64) {
     if (rows_q)
-      bwd_preprocess_kernel<64><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di, part,
-                                                                cq, a.Sq, a.Hq, tq);
+      bwd_preprocess_kernel<64><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, ndi, lse2,
+                                                                part, cq, a.Sq, a.Hq, tq);
     // one launch for both passes (D 64; training workloads 3 % faster than two
     // launches); the D 128 path keeps two launches
     if (rows_k && rows_q) {
       const int nkv = (int)(kgrid.x * kgrid.y * kgrid.z);
       bwd_main_kernel<64><<<dim3(nkv + qgrid.x), kThreads, 0, stream>>>(
-          q, k, v, dout, a.lse, di, dq, dk, dv, cq, ck, a.B, a.Sq, a.Sk, a.Hq, a.Hkv, tq, hpw,
+          q, k, v, dout, lse2, ndi, dq, dk, dv, cq, ck, a.B, a.Sq, a.Sk, a.Hq, a.Hkv, tq, hpw,
           a.scale, sl2, a.causal, a.w1, a.w2, nkv);
     } else {
       if (rows_k)
-        bwd_dkdv_kernel<64><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dk, dv, cq,
+        bwd_dkdv_kernel<64><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, lse2, ndi, dk, dv, cq,
                                                             ck, a.Sq, a.Sk, a.Hq, a.Hkv, tq,
                                                             a.scale, sl2, a.causal, a.w1, a.w2);
       if (rows_q)
-        bwd_dq_kernel<64><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, cq, ck,
+        bwd_dq_kernel<64><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, lse2, ndi, dq, cq, ck,
                                                           a.B, a.Sq, a.Sk, a.Hq, a.Hkv, tq, hpw,
                                                           a.scale, sl2, a.causal, a.w1, a.w2);
     }
   } else {
     if (rows_q)
-      bwd_preprocess_kernel<128><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, di,
-                                                                 part, cq, a.Sq, a.Hq, tq);
+      bwd_preprocess_kernel<128><<<pgrid, kThreads, 0, stream>>>(o, dout, a.lse, a.sink, ndi,
+                                                                 lse2, part, cq, a.Sq, a.Hq, tq);
     if (rows_k)
-      bwd_dkdv_kernel<128><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dk, dv, cq,
+      bwd_dkdv_kernel<128><<<kgrid, kThreads, 0, stream>>>(q, k, v, dout, lse2, ndi, dk, dv, cq,
                                                            ck, a.Sq, a.Sk, a.Hq, a.Hkv, tq,
                                                            a.scale, sl2, a.causal, a.w1, a.w2);
     if (rows_q)
-      bwd_dq_kernel<128><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, a.lse, di, dq, cq, ck,
+      bwd_dq_kernel<128><<<qgrid, kThreads, 0, stream>>>(q, k, v, dout, lse2, ndi, dq, cq, ck,
                                                          a.B, a.Sq, a.Sk, a.Hq, a.Hkv, tq, hpw,
                                                          a.scale, sl2, a.causal, a.w1, a.w2);
   }

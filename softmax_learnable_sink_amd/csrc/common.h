@@ -65,6 +65,80 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// ---------------------------------------------------------------------------
+// Tiles loaded straight into LDS (buffer_load_dword{,x4} ... lds).  Lane l of
+// one such load writes its 4 or 16 bytes to LDS at base + l * size, and a lane
+// past the resource's end writes zeros.  The data never passes through VGPRs
+// and the waves write nothing to LDS themselves, so a tile can be requested
+// several tiles ahead at no register cost.
+//
+// A tile is 64 rows of D bf16 stored in LDS rows of D + 8 elements (16 bytes of
+// padding against bank conflicts): kDmaSlots(D) = D/8 + 1 16-byte slots per
+// row, the last one padding.  Load j of a tile fills slots 64 j .. 64 j + 63,
+// so a tile takes kDmaSlots(D) loads of 1 KB each; a lane whose slot is padding
+// reads its row's first chunk again.  Rows may be permuted inside 32-row
+// blocks (the layout the score MFMA's operand reads want, perm_row below).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kDmaSlots(int D) { return D / 8 + 1; }
+
+// Row permutation inside a 32-row block: logical row j is stored at LDS row
+// perm_row(j), so that the four rows an MFMA result register group covers are
+// contiguous.  dma_row inverts it.
+__device__ __forceinline__ int perm_row(int j) {
+  return ((j & 15) >> 2) * 8 + (j >> 4) * 4 + (j & 3);
+}
+__device__ __forceinline__ int dma_row(int p) {
+  return (p & ~31) + 16 * ((p >> 2) & 1) + 4 * ((p >> 3) & 3) + (p & 3);
+}
+
+// Byte offset (from the tile's first row, rows rs_bytes apart) that lane
+// `lane` reads for load j of a tile.
+template <int D>
+__device__ __forceinline__ uint32_t dma_offset(int j, int lane, uint32_t rs_bytes, bool permuted) {
+  constexpr int SP = kDmaSlots(D);
+  const int slot = 64 * j + lane;
+  const int p = slot / SP, c = slot % SP;
+  const int row = permuted ? dma_row(p) : p;
+  return (uint32_t)row * rs_bytes + (uint32_t)(c == SP - 1 ? 0 : c) * 16u;
+}
+
+// One 16-byte-per-lane (1 KB) load into LDS at lds (wave-uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+// One 4-byte-per-lane (256 B) load into LDS at lds (wave-uniform).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait until at most n (U or U - 1, wave-uniform) vector memory operations of
+// this wave are outstanding.
+template <int U>
+__device__ __forceinline__ void wait_vmcnt_u(int n) {
+  if (n >= U)
+    wait_vmcnt<U>();
+  else
+    wait_vmcnt<(U > 0 ? U - 1 : 0)>();
+}
+// Workgroup barrier that orders the compiler's LDS accesses but leaves the
+// vector-memory counter alone: the tiles requested ahead stay in flight.  The
+// caller waits for the tile it is about to read (wait_vmcnt) and for its own
+// LDS reads (lgkmcnt) first.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // max(x, x of lane ^ 32) without an LDS round trip.  v_permlane32_swap swaps
 // the upper half of its first operand with the lower half of its second; fed
 // two copies of x it leaves, per lane, x and its partner's x (in some order).

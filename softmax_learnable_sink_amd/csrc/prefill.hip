@@ -34,11 +34,10 @@ namespace {
 constexpr int kBN = 64;        // keys per KV tile
 constexpr int kThreads = 256;  // 4 waves of 64
 
-// LDS row (within a 32-key block) that holds key j of the block.  The MFMA
-// reading row r then sees key 16*((r>>2)&1) + 4*(r>>3) + (r&3), which puts
-// keys 16h .. 16h+15 of the block, in order, into accumulator half h.
-__device__ __forceinline__ int k_lds_row(int j) { return ((j & 15) >> 2) * 8 + (j >> 4) * 4 + (j & 3); }
-
+// K rows sit in LDS in the order perm_row (common.h): the MFMA reading row r
+// then sees key dma_row(r) = 16*((r>>2)&1) + 4*(r>>3) + (r&3) of its 32-key
+// block, which puts keys 16h .. 16h+15 of the block, in order, into
+// accumulator half h.
 template <int D>
 struct Lds {
   static constexpr int KS = D + 8;   // K row stride (elements), 16 B of padding
@@ -46,60 +45,12 @@ struct Lds {
   __bf16 k[2][kBN * KS];
   __bf16 v[2][kBN * VS];             // natural [key][d]; read transposed (ds_read_b64_tr_b16)
 };
-
+// One K/V tile buffer in the same layout (the prefill keeps each buffer in an
+// LDS variable of its own).
 template <int D>
-struct TileRegs {
-  static constexpr int NT = kThreads;
-  static constexpr int CH = D / 8;                        // 16-byte chunks per row
-  static constexpr int KN = kBN * CH / NT;                // K (and V) chunks per thread
-  uint4 kr[KN];
-  uint4 vr[KN];
-  uint32_t off[KN];      // byte offsets inside a tile (loop invariant)
-
-  __device__ __forceinline__ void init(size_t rs, int tid) {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const int idx = tid + i * NT;
-      off[i] = (uint32_t)(((size_t)(idx / CH) * rs + (idx % CH) * 8) * 2);
-    }
-  }
-
-  // Keys key0 .. key0+63 of one KV head; rows at or past Sk read as zero.
-  __device__ __forceinline__ void load_k(const __bf16* kbase, size_t rs, int key0, int Sk) {
-    const auto r = make_rsrc(kbase + (size_t)key0 * rs, (uint32_t)((size_t)(Sk - key0) * rs * 2));
-#pragma unroll
-    for (int i = 0; i < KN; ++i) kr[i] = buf_load16(r, off[i]);
-  }
-  __device__ __forceinline__ void load_v(const __bf16* vbase, size_t rs, int key0, int Sk) {
-    const auto r = make_rsrc(vbase + (size_t)key0 * rs, (uint32_t)((size_t)(Sk - key0) * rs * 2));
-#pragma unroll
-    for (int i = 0; i < KN; ++i) vr[i] = buf_load16(r, off[i]);
-  }
-  __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, size_t rs,
-                                       int key0, int Sk) {
-    load_k(kbase, rs, key0, Sk);
-    load_v(vbase, rs, key0, Sk);
-  }
-
-  __device__ __forceinline__ void store_k(__bf16* dst, int tid) const {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const int idx = tid + i * NT, key = idx / CH, c = idx % CH;
-      const int row = (key & ~31) + k_lds_row(key & 31);
-      *reinterpret_cast<uint4*>(dst + row * Lds<D>::KS + c * 8) = kr[i];
-    }
-  }
-  __device__ __forceinline__ void store_v(__bf16* dst, int tid) const {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const int idx = tid + i * NT, key = idx / CH, c = idx % CH;
-      *reinterpret_cast<uint4*>(dst + key * Lds<D>::VS + c * 8) = vr[i];
-    }
-  }
-  __device__ __forceinline__ void store(Lds<D>& s, int buf, int tid) const {
-    store_k(s.k[buf], tid);
-    store_v(s.v[buf], tid);
-  }
+struct KvTile {
+  __bf16 k[kBN * Lds<D>::KS];
+  __bf16 v[kBN * Lds<D>::VS];
 };
 
 // A operand of O^T += V^T P^T for d block db and the 16 keys of k-step (kb, c):
@@ -112,12 +63,14 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 template <int D>
 __device__ __forceinline__ bf16x8 vt_frag(const __bf16* vtile, int db, int kb, int c, int lane) {
   const int sl = lane & 15, gg = (lane >> 4) & 1, hh = lane >> 5;
-  const int row = 32 * kb + 16 * hh + 8 * c + (sl >> 2);
-  const int col = 32 * db + 16 * gg + 4 * (sl & 3);
+  // the lane's part of the address, then the constant part: each read's
+  // address is then at most two steps from the tile (see dma_offset)
+  const int ol = (16 * hh + (sl >> 2)) * Lds<D>::VS + 16 * gg + 4 * (sl & 3);
+  const int oc = (32 * kb + 8 * c) * Lds<D>::VS + 32 * db;
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const __bf16* p0 = vtile + row * Lds<D>::VS + col;
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * Lds<D>::VS));
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vtile + (ol + oc)));
+  const i16x4 b =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vtile + (ol + oc + 4 * Lds<D>::VS)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -363,7 +316,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int B, int Sq,
     int Sk, int Hq, int Hkv, int hpw, float sl2, int causal, int w1, int w2) {
-  __shared__ Lds<D> s;
+  constexpr int NB = D == 64 ? 3 : 2;  // LDS tile buffers
+  __shared__ KvTile<D> s0, s1;
   constexpr int RW = 32 * QB;  // query rows per wave
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -393,35 +347,83 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const TileRange tr = tile_range(Sk, geom.p_min, geom.p_max, causal, w1, w2);
   const int ntiles = tr.count();
 
-  // Q and the sink are loaded; start the tile loop with no VMEM load pending so
-  // that the compiler's wait tracking does not hold the first MFMA of every
-  // tile on the prefetch of the next one.
-  __builtin_amdgcn_s_waitcnt(0);
-  TileRegs<D> regs;
-  regs.init(rs, tid);
-  if (ntiles > 0) {
-    regs.load(kbase, vbase, rs, tr.tile(0) * kBN, Sk);
-    regs.store(s, 0, tid);
+  // K/V tiles go straight into LDS, NB - 1 tiles ahead of the one in use
+  // (three buffers at D = 64; two at D = 128, where three would not leave room
+  // for two workgroups per CU).  A tile is SP 1 KB loads of K (rows permuted)
+  // and SP of V (natural rows): waves 0 and 1 load K, waves 2 and 3 V, each
+  // taking every other load j = (wave & 1) + 2u.  SP is odd, so the odd wave
+  // repeats its last load (same data to the same slots): every wave then
+  // issues U loads per tile and the waits below are the same static count
+  // for all (the compiler's own wait tracking needs that to see which buffer
+  // a load in flight may still be writing).  Tile i sits in buffer
+  // i % NB; each buffer is an LDS variable of its own and the loop is unrolled
+  // by NB, so that every LDS read names a buffer no load in flight writes
+  // (otherwise the compiler waits for all loads in flight before such reads).
+  constexpr int SP = kDmaSlots(D), U = (SP + 1) / 2;
+  static_assert(SP % 2 == 1, "odd slot count per row");
+  const bool wk = wave < 2;
+  uint32_t doff[U], dlds[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = (wave & 1) + 2 * u < SP ? (wave & 1) + 2 * u : (wave & 1) + 2 * u - 2;
+    doff[u] = dma_offset<D>(j, lane, (uint32_t)(rs * 2), wk);
+    dlds[u] = 512 * j;  // elements
   }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int key0 = tr.tile(it) * kBN;
-    if (it + 1 < ntiles) regs.load(kbase, vbase, rs, tr.tile(it + 1) * kBN, Sk);
-    f32x16 st[2][QB];
-    bf16x8 pf[2][QB][2];
-    if (WaveRows<D, QB>::needs_mask(key0, geom)) {
-      wr.scores(s.k[buf], st, l32, hh);
-      wr.mask(st, key0, geom, hh);
-    } else {
-      wr.scores(s.k[buf], st, l32, hh);
+  // Tile it into dst_buf; past the last tile the loads read an empty
+  // resource (they write zeros to a buffer nobody reads), so that every step
+  // issues the same loads.
+  auto request = [&](int it, KvTile<D>& dst_buf) {
+    const int key0 = it < ntiles ? tr.tile(it) * kBN : 0;
+    const uint32_t bytes = it < ntiles ? (uint32_t)((size_t)(Sk - key0) * rs * 2) : 0u;
+    const auto r = make_rsrc((wk ? kbase : vbase) + (size_t)key0 * rs, bytes);
+    __bf16* dst = wk ? dst_buf.k : dst_buf.v;
+#pragma unroll
+    for (int u = 0; u < U; ++u) dma16(r, dst + dlds[u], doff[u]);
+  };
+  // One step: wait until tile it has landed (the next NB - 2 tiles' loads may
+  // stay in flight); after the barrier it has for every wave, and every wave
+  // is done with tile it - 1's buffer, which the request overwrites.  The loop
+  // runs whole groups of NB steps; steps past the last tile only keep the
+  // loads and waits uniform.
+  auto step = [&](int it, KvTile<D>& cur, KvTile<D>& ahead) {
+    wait_vmcnt<(NB - 2) * U>();
+    tile_barrier();
+    request(it + NB - 1, ahead);
+    if (it < ntiles) {
+      const int key0 = tr.tile(it) * kBN;
+      f32x16 st[2][QB];
+      bf16x8 pf[2][QB][2];
+      if (WaveRows<D, QB>::needs_mask(key0, geom)) {
+        wr.scores(cur.k, st, l32, hh);
+        wr.mask(st, key0, geom, hh);
+      } else {
+        wr.scores(cur.k, st, l32, hh);
+      }
+      wr.online(st, pf, sl2);
+      wr.pv(cur.v, pf, lane);
     }
-    wr.online(st, pf, sl2);
-    wr.pv(s.v[buf], pf, lane);
-    if (it + 1 < ntiles) regs.store(s, buf ^ 1, tid);
-    __syncthreads();
+  };
+
+  // Q and the sink are loaded before the first tile request, so that the
+  // vector-memory counter holds tile loads only.
+  __builtin_amdgcn_s_waitcnt(0);
+  request(0, s0);
+  if constexpr (NB == 3) {
+    __shared__ KvTile<D> s2;
+    request(1, s1);
+    for (int it = 0; it < ntiles; it += 3) {
+      step(it, s0, s2);
+      step(it + 1, s1, s0);
+      step(it + 2, s2, s1);
+    }
+  } else {
+    for (int it = 0; it < ntiles; it += 2) {
+      step(it, s0, s1);
+      step(it + 1, s1, s0);
+    }
   }
+  // no load may still write this workgroup's LDS when it exits
+  wait_vmcnt<0>();
   wr.finish(o + (size_t)b * Sq * Hq * D, lse ? lse + ((size_t)b * Hq + h) * Sq : nullptr, Sq, Hq,
             h, wrow0, hh, l32);
 }
@@ -497,7 +499,7 @@ struct PagedTile {
 #pragma unroll
     for (int i = 0; i < KN; ++i) {
       const int key = row_of(tid, i), c = chunk_of(tid, i);
-      const int row = (key & ~31) + k_lds_row(key & 31);
+      const int row = (key & ~31) + perm_row(key & 31);
       const bool ok = slot[i] >= 0;
       *reinterpret_cast<uint4*>(&s.k[buf][row * Lds<D>::KS + c * 8]) = kr[i];
       *reinterpret_cast<uint4*>(&s.v[buf][key * Lds<D>::VS + c * 8]) =
@@ -659,7 +661,7 @@ struct ListTile {
     for (int i = 0; i < KN; ++i) {
       const int key = row_of(tid, i), c = chunk_of(tid, i);
       const bool ok = tok[key] != INT_MAX;
-      const int row = (key & ~31) + k_lds_row(key & 31);
+      const int row = (key & ~31) + perm_row(key & 31);
       *reinterpret_cast<uint4*>(&s.k[buf][row * Lds<D>::KS + c * 8]) = kr[i];
       *reinterpret_cast<uint4*>(&s.v[buf][key * Lds<D>::VS + c * 8]) =
           uint4{ok ? vr[i].x : 0u, ok ? vr[i].y : 0u, ok ? vr[i].z : 0u, ok ? vr[i].w : 0u};

@@ -250,7 +250,7 @@ def test_bwd_rejects(lib, kw, status, msg):
 def test_bwd_workspace_query(lib):
     B, S, Hq = 2, 8192, 64
     n = binding.attn_sink_bwd_workspace_bytes(B, S, S, Hq, 8, 64)
-    assert n == 4 * (B * Hq * S + B * Hq * (S // 64))
+    assert n == 4 * (2 * B * Hq * S + B * Hq * (S // 64))  # -Di, LSE log2 e, dSink partials
     assert binding.attn_sink_bwd_workspace_bytes(B, S, S, Hq, 7, 64) == 0
 
 
@@ -386,7 +386,7 @@ def test_bwd_varlen_rejects(lib, kw, status, msg):
 def test_bwd_varlen_workspace_query(lib):
     B, tq, mq, Hq = 3, 5000, 4096, 16
     n = binding.attn_sink_bwd_varlen_workspace_bytes(B, tq, mq, Hq)
-    assert n == 4 * (Hq * tq + B * Hq * (mq // 64))
+    assert n == 4 * (2 * Hq * tq + B * Hq * (mq // 64))
     assert binding.attn_sink_bwd_varlen_workspace_bytes(0, tq, mq, Hq) == 0
 
 
