@@ -108,6 +108,11 @@ __device__ __forceinline__ uint32_t dma_offset(int j, int lane, uint32_t rs_byte
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
 }
+// The same from a 64-bit address per lane (global_load_lds_dwordx4).
+typedef __attribute__((address_space(1))) void global_void;
+__device__ __forceinline__ void dma16_global(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)lds, 16, 0, 0);
+}
 // One 4-byte-per-lane (256 B) load into LDS at lds (wave-uniform).
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
@@ -118,15 +123,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// Wait until at most n (U or U - 1, wave-uniform) vector memory operations of
-// this wave are outstanding.
-template <int U>
-__device__ __forceinline__ void wait_vmcnt_u(int n) {
-  if (n >= U)
-    wait_vmcnt<U>();
-  else
-    wait_vmcnt<(U > 0 ? U - 1 : 0)>();
 }
 // Workgroup barrier that orders the compiler's LDS accesses but leaves the
 // vector-memory counter alone: the tiles requested ahead stay in flight.  The

@@ -438,72 +438,51 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 // on K/V tiles gathered from the cache through the block table.
 // ---------------------------------------------------------------------------
 
-// One 64-key tile of K and V gathered row by row.  Each thread owns KN (row,
-// 16-byte chunk) items.  With a block table the rows are cache slots, from
-// block-table entries fetched two tiles ahead; without one (packed
-// variable-length K/V) key j of the sequence is row kbase + j.  Keys at or
-// past L read row 0 and are written to LDS as zero V rows (their scores are
-// masked anyway).
-template <int D>
-struct PagedTile {
-  static constexpr int CH = D / 8;
-  static constexpr int KN = kBN * CH / kThreads;
-  uint4 kr[KN], vr[KN];
-  int page[KN];   // block-table entries of the tile being fetched
-  int slot[KN];   // slots of the tile to load next (-1: past the context)
+// One 64-key tile of K or V gathered row by row straight into LDS, in the
+// prefill's tile layout (K rows permuted, V natural).  Waves 0 and 1 load K,
+// waves 2 and 3 V, each every other 1 KB load of the tile (the odd wave
+// repeating its last, so that every wave issues U loads); this lane's slot in
+// load u is tile row row[u], chunk offset cb[u].  slot[u] is the cache row (or
+// packed K/V row) behind it, -1 for none (a key past the context, an empty
+// list entry): that slot reads zeros, from an offset past the buffer resource
+// or from a zero row.
+__device__ __align__(16) uint4 g_zero_row[1];  // 16 zero bytes
 
-  __device__ __forceinline__ static int row_of(int tid, int i) { return (tid + i * kThreads) / CH; }
-  __device__ __forceinline__ static int chunk_of(int tid, int i) { return (tid + i * kThreads) % CH; }
+constexpr uint32_t kNoRow = 0xFFFFFF00u;  // past any resource of these kernels
 
-  __device__ __forceinline__ void fetch_pages(const int32_t* bt_row, int key0, int L, int shift,
-                                              int tid) {
-    if (!bt_row) {
+template <int D, bool BUF>
+struct GatherDma {
+  static constexpr int SP = kDmaSlots(D), U = (SP + 1) / 2;
+  int row[U];
+  uint32_t cb[U];
+  int dl[U];      // LDS element offset of load u
+  int page[U];    // block-table entries behind row[u] of the tile fetched ahead
+  int slot[U];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-      for (int i = 0; i < KN; ++i) page[i] = 0;
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < KN; ++i) page[i] = bt_row[min(key0 + row_of(tid, i), L - 1) >> shift];
-  }
-  __device__ __forceinline__ void pages_to_slots(const int32_t* bt_row, int kbase, int key0, int L,
-                                                 int shift, int tid) {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const int key = key0 + row_of(tid, i);
-      const int row = bt_row ? (page[i] << shift) | (key & ((1 << shift) - 1)) : kbase + key;
-      slot[i] = key < L ? row : -1;
-    }
-  }
-  __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, size_t rs,
-                                       int tid) {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const size_t off = (size_t)max(slot[i], 0) * rs + chunk_of(tid, i) * 8;
-      kr[i] = *reinterpret_cast<const uint4*>(kbase + off);
-      vr[i] = *reinterpret_cast<const uint4*>(vbase + off);
+    for (int u = 0; u < U; ++u) {
+      const int j = (wave & 1) + 2 * u < SP ? (wave & 1) + 2 * u : (wave & 1) + 2 * u - 2;
+      const int s = 64 * j + lane, p = s / SP, c = s % SP;
+      row[u] = wave < 2 ? dma_row(p) : p;
+      cb[u] = (uint32_t)(c == SP - 1 ? 0 : c) * 16u;
+      dl[u] = 512 * j;
     }
   }
-  // The same through buffer resources over the whole K and V arrays (all of
-  // whose bytes, seen from this KV head, lie below 4 GiB): 32-bit offsets, no
-  // 64-bit address per chunk.
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                       uint32_t rs_bytes, int tid) {
+  // the loads of one tile into dst (this wave's K or V buffer); r covers the
+  // wave's array from its KV head (BUF), base is the same array otherwise
+  __device__ __forceinline__ void issue(__bf16* dst, __amdgpu_buffer_rsrc_t r, const __bf16* base,
+                                        uint32_t rs_bytes) const {
 #pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const uint32_t off = (uint32_t)max(slot[i], 0) * rs_bytes + chunk_of(tid, i) * 16;
-      kr[i] = buf_load16(rk, off);
-      vr[i] = buf_load16(rv, off);
-    }
-  }
-  __device__ __forceinline__ void store(Lds<D>& s, int buf, int tid) const {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const int key = row_of(tid, i), c = chunk_of(tid, i);
-      const int row = (key & ~31) + perm_row(key & 31);
-      const bool ok = slot[i] >= 0;
-      *reinterpret_cast<uint4*>(&s.k[buf][row * Lds<D>::KS + c * 8]) = kr[i];
-      *reinterpret_cast<uint4*>(&s.v[buf][key * Lds<D>::VS + c * 8]) =
-          uint4{ok ? vr[i].x : 0u, ok ? vr[i].y : 0u, ok ? vr[i].z : 0u, ok ? vr[i].w : 0u};
+    for (int u = 0; u < U; ++u) {
+      if constexpr (BUF) {
+        dma16(r, dst + dl[u], slot[u] >= 0 ? (uint32_t)slot[u] * rs_bytes + cb[u] : kNoRow);
+      } else {
+        const void* src = slot[u] >= 0 ? (const void*)(reinterpret_cast<const char*>(base) +
+                                                       (size_t)slot[u] * rs_bytes + cb[u])
+                                       : (const void*)g_zero_row;
+        dma16_global(src, dst + dl[u]);
+      }
     }
   }
 };
@@ -521,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
     int total_q, int max_sq, int Hq, int Hkv, int hpw, int page_shift, int max_pages, float sl2,
     int causal, int w1, int w2, uint32_t kv_bytes) {
   ATTN_SINK_CHECK_GUARD();
-  __shared__ Lds<D> s;
+  __shared__ KvTile<D> s0, s1;  // one LDS variable per tile buffer
   constexpr int RW = 32 * QB;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -549,53 +528,67 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
   WaveRows<D, QB> wr;
   wr.init(q + (size_t)qbase * Hq * D, sink, nq, Hq, h, wrow0, hh, l32);
 
-  const size_t rs = (size_t)Hkv * D;
-  const __bf16* kb_ = kc + (size_t)kvh * D;
-  const __bf16* vb_ = vc + (size_t)kvh * D;
-  const uint32_t head_bytes = (uint32_t)(kvh * D * 2);
-  const auto rk = make_rsrc(kb_, kv_bytes - head_bytes), rv = make_rsrc(vb_, kv_bytes - head_bytes);
-  const uint32_t rs_bytes = (uint32_t)(rs * 2);
-  auto load_tile = [&](PagedTile<D>& t) {
-    if constexpr (BUF)
-      t.load(rk, rv, rs_bytes, tid);
-    else
-      t.load(kb_, vb_, rs, tid);
-  };
+  // K/V tiles gathered straight into LDS one tile ahead; the block-table
+  // entries of a tile are read a tile before that
+  const uint32_t rs_bytes = (uint32_t)(Hkv * D * 2);
+  const bool wk = wave < 2;
+  const __bf16* base = (wk ? kc : vc) + (size_t)kvh * D;
+  const auto rsrc = make_rsrc(base, kv_bytes - (uint32_t)(kvh * D * 2));
   const int32_t* bt_row = bt ? bt + (size_t)b * max_pages : nullptr;
+  const int pmask = (1 << page_shift) - 1;
   const TileRange tr = tile_range(L, geom.p_min, geom.p_max, causal, w1, w2);
   const int nt = tr.count();
+  constexpr int GU = GatherDma<D, BUF>::U;
+  GatherDma<D, BUF> gd;
+  gd.init(wave, lane);
+  auto fetch = [&](int it) {  // block-table entries of tile it's rows (clamped to the context)
+    if (bt_row) {
+#pragma unroll
+      for (int u = 0; u < GU; ++u)
+        gd.page[u] = bt_row[min(tr.tile(it) * kBN + gd.row[u], L - 1) >> page_shift];
+    }
+  };
+  auto request = [&](int it, KvTile<D>& dst) {  // slots of tile it's rows, then the loads
+    const int key0 = tr.tile(it) * kBN;
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const int key = key0 + gd.row[u];
+      gd.slot[u] = key >= L ? -1 : bt_row ? (gd.page[u] << page_shift) | (key & pmask) : kbase + key;
+    }
+    gd.issue(wk ? dst.k : dst.v, rsrc, base, rs_bytes);
+  };
+  // one tile: wait until it has landed (and the entries of the next one);
+  // after the barrier it has for every wave, and every wave is done with the
+  // previous tile's buffer, which the next tile's loads overwrite
+  auto step = [&](int it, KvTile<D>& cur, KvTile<D>& ahead) {
+    wait_vmcnt<0>();
+    tile_barrier();
+    if (it + 1 < nt) request(it + 1, ahead);
+    if (it + 2 < nt) fetch(it + 2);
+    const int key0 = tr.tile(it) * kBN;
+    f32x16 st[2][QB];
+    bf16x8 pf[2][QB][2];
+    if (WaveRows<D, QB>::needs_mask(key0, geom)) {
+      wr.scores(cur.k, st, l32, hh);
+      wr.mask(st, key0, geom, hh);
+    } else {
+      wr.scores(cur.k, st, l32, hh);
+    }
+    wr.online(st, pf, sl2);
+    wr.pv(cur.v, pf, lane);
+  };
 
-  __builtin_amdgcn_s_waitcnt(0);
   if (nt > 0) {
-    PagedTile<D> pt;
-    pt.fetch_pages(bt_row, tr.tile(0) * kBN, L, page_shift, tid);
-    pt.pages_to_slots(bt_row, kbase, tr.tile(0) * kBN, L, page_shift, tid);
-    load_tile(pt);
-    pt.store(s, 0, tid);
-    if (nt > 1) {
-      pt.fetch_pages(bt_row, tr.tile(1) * kBN, L, page_shift, tid);
-      pt.pages_to_slots(bt_row, kbase, tr.tile(1) * kBN, L, page_shift, tid);
+    fetch(0);
+    __builtin_amdgcn_s_waitcnt(0);  // Q, the sink and tile 0's entries
+    request(0, s0);
+    if (nt > 1) fetch(1);
+    for (int it = 0; it < nt; it += 2) {
+      step(it, s0, s1);
+      if (it + 1 < nt) step(it + 1, s1, s0);
     }
-    __syncthreads();
-    for (int it = 0; it < nt; ++it) {
-      const int buf = it & 1;
-      if (it + 1 < nt) load_tile(pt);
-      if (it + 2 < nt) pt.fetch_pages(bt_row, tr.tile(it + 2) * kBN, L, page_shift, tid);
-      const int key0 = tr.tile(it) * kBN;
-      f32x16 st[2][QB];
-      bf16x8 pf[2][QB][2];
-      if (WaveRows<D, QB>::needs_mask(key0, geom)) {
-        wr.scores(s.k[buf], st, l32, hh);
-        wr.mask(st, key0, geom, hh);
-      } else {
-        wr.scores(s.k[buf], st, l32, hh);
-      }
-      wr.online(st, pf, sl2);
-      wr.pv(s.v[buf], pf, lane);
-      if (it + 1 < nt) pt.store(s, buf ^ 1, tid);
-      if (it + 2 < nt) pt.pages_to_slots(bt_row, kbase, tr.tile(it + 2) * kBN, L, page_shift, tid);
-      __syncthreads();
-    }
+    // no load may still write this workgroup's LDS when it exits
+    wait_vmcnt<0>();
   }
   wr.finish(o + (size_t)qbase * Hq * D, lse ? lse + (size_t)h * total_q + qbase : nullptr, nq,
             Hq, h, wrow0, hh, l32);
@@ -609,66 +602,6 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kMaxList = 2048;  // longest list (LDS-resident, 8 KB)
 
-template <int D>
-struct ListTile {
-  static constexpr int CH = D / 8;
-  static constexpr int KN = kBN * CH / kThreads;
-  uint4 kr[KN], vr[KN];
-  int ps[KN];  // block-table pages, then slots, of the tile two ahead
-
-  __device__ __forceinline__ static int row_of(int tid, int i) { return (tid + i * kThreads) / CH; }
-  __device__ __forceinline__ static int chunk_of(int tid, int i) { return (tid + i * kThreads) % CH; }
-
-  // tok: the tile's 64 tokens (INT_MAX: empty entry)
-  __device__ __forceinline__ void fetch_pages(const int* tok, const int32_t* bt_row, int shift,
-                                              int tid) {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const int t = tok[row_of(tid, i)];
-      ps[i] = bt_row[(t == INT_MAX ? 0 : t) >> shift];
-    }
-  }
-  __device__ __forceinline__ void pages_to_slots(const int* tok, int shift, int tid) {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const int t = tok[row_of(tid, i)];
-      ps[i] = t == INT_MAX ? 0 : (ps[i] << shift) | (t & ((1 << shift) - 1));
-    }
-  }
-  __device__ __forceinline__ void load(const __bf16* kbase, const __bf16* vbase, size_t rs,
-                                       int tid) {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const size_t off = (size_t)ps[i] * rs + chunk_of(tid, i) * 8;
-      kr[i] = *reinterpret_cast<const uint4*>(kbase + off);
-      vr[i] = *reinterpret_cast<const uint4*>(vbase + off);
-    }
-  }
-  // through buffer resources over caches below 4 GiB (32-bit offsets)
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                       uint32_t rs_bytes, int tid) {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const uint32_t off = (uint32_t)ps[i] * rs_bytes + chunk_of(tid, i) * 16;
-      kr[i] = buf_load16(rk, off);
-      vr[i] = buf_load16(rv, off);
-    }
-  }
-  // V rows of empty entries are written as zeros (the slot they read is only
-  // a stand-in); their scores are masked.
-  __device__ __forceinline__ void store(Lds<D>& s, int buf, const int* tok, int tid) const {
-#pragma unroll
-    for (int i = 0; i < KN; ++i) {
-      const int key = row_of(tid, i), c = chunk_of(tid, i);
-      const bool ok = tok[key] != INT_MAX;
-      const int row = (key & ~31) + perm_row(key & 31);
-      *reinterpret_cast<uint4*>(&s.k[buf][row * Lds<D>::KS + c * 8]) = kr[i];
-      *reinterpret_cast<uint4*>(&s.v[buf][key * Lds<D>::VS + c * 8]) =
-          uint4{ok ? vr[i].x : 0u, ok ? vr[i].y : 0u, ok ? vr[i].z : 0u, ok ? vr[i].w : 0u};
-    }
-  }
-};
-
 // Packed new queries against a paged cache (as extend_kernel); the rows of
 // each block of block_q rows of a sequence attend to the tokens of one list
 // (kv_index row cu_blocks[b] + row / block_q) at or before their positions.
@@ -681,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_kernel(
     float* __restrict__ lse, int B, int total_q, int max_sq, int Hq, int Hkv, int page_shift,
     int max_pages, int block_q, int topk, float sl2, uint32_t kv_bytes) {
   ATTN_SINK_CHECK_GUARD();
-  __shared__ Lds<D> s;
+  __shared__ KvTile<D> s0, s1;  // one LDS variable per tile buffer
   __shared__ __attribute__((aligned(16))) int tokl[kMaxList];
   __shared__ int tmax[kMaxList / kBN];  // largest token of each tile (INT_MAX if one is empty)
   constexpr int RW = 32 * QB;  // rows per wave = rows per workgroup (4 heads of a group)
@@ -723,49 +656,61 @@ __global__ __launch_bounds__(kThreads, 2) void index_kernel(
   WaveRows<D, QB> wr;
   wr.init(q + (size_t)qbase * Hq * D, sink, nq, Hq, h, row0, hh, l32);
 
-  const size_t rs = (size_t)Hkv * D;
-  const __bf16* kb_ = kc + (size_t)kvh * D;
-  const __bf16* vb_ = vc + (size_t)kvh * D;
+  // K/V tiles gathered straight into LDS one tile ahead; the block-table
+  // entries of a tile are read a tile before that
+  const uint32_t rs_bytes = (uint32_t)(Hkv * D * 2);
+  const bool wk = wave < 2;
+  const __bf16* base = (wk ? kc : vc) + (size_t)kvh * D;
+  const auto rsrc = make_rsrc(base, kv_bytes - (uint32_t)(kvh * D * 2));
   const int32_t* bt_row = bt + (size_t)b * max_pages;
-  const uint32_t head_bytes = (uint32_t)(kvh * D * 2);
-  const auto rk = make_rsrc(kb_, kv_bytes - head_bytes), rv = make_rsrc(vb_, kv_bytes - head_bytes);
-  const uint32_t rs_bytes = (uint32_t)(rs * 2);
-  auto load_tile = [&](ListTile<D>& t) {
-    if constexpr (BUF)
-      t.load(rk, rv, rs_bytes, tid);
-    else
-      t.load(kb_, vb_, rs, tid);
+  const int pmask = (1 << page_shift) - 1;
+  constexpr int GU = GatherDma<D, BUF>::U;
+  GatherDma<D, BUF> gd;
+  gd.init(wave, lane);
+  auto fetch = [&](int it) {  // block-table entries of tile it's tokens
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const int t = tokl[it * kBN + gd.row[u]];
+      gd.page[u] = bt_row[(t == INT_MAX ? 0 : t) >> page_shift];
+    }
   };
-
-  __syncthreads();
-  ListTile<D> lt;
-  lt.fetch_pages(tokl, bt_row, page_shift, tid);
-  lt.pages_to_slots(tokl, page_shift, tid);
-  load_tile(lt);
-  lt.store(s, 0, tokl, tid);
-  if (nt > 1) {
-    lt.fetch_pages(tokl + kBN, bt_row, page_shift, tid);
-    lt.pages_to_slots(tokl + kBN, page_shift, tid);
-  }
-  __syncthreads();
-  for (int it = 0; it < nt; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < nt) load_tile(lt);
-    if (it + 2 < nt) lt.fetch_pages(tokl + (it + 2) * kBN, bt_row, page_shift, tid);
+  auto request = [&](int it, KvTile<D>& dst) {  // slots of tile it's tokens, then the loads
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const int t = tokl[it * kBN + gd.row[u]];
+      gd.slot[u] = t == INT_MAX ? -1 : (gd.page[u] << page_shift) | (t & pmask);
+    }
+    gd.issue(wk ? dst.k : dst.v, rsrc, base, rs_bytes);
+  };
+  // one tile, as in extend_kernel
+  auto step = [&](int it, KvTile<D>& cur, KvTile<D>& ahead) {
+    wait_vmcnt<0>();
+    tile_barrier();
+    if (it + 1 < nt) request(it + 1, ahead);
+    if (it + 2 < nt) fetch(it + 2);
     f32x16 st[2][QB];
     bf16x8 pf[2][QB][2];
     if (__builtin_amdgcn_readfirstlane(tmax[it]) > p_first) {
-      wr.scores(s.k[buf], st, l32, hh);
+      wr.scores(cur.k, st, l32, hh);
       wr.mask_tokens(st, tokl + it * kBN, p_lane, hh);
     } else {
-      wr.scores(s.k[buf], st, l32, hh);
+      wr.scores(cur.k, st, l32, hh);
     }
     wr.online(st, pf, sl2);
-    wr.pv(s.v[buf], pf, lane);
-    if (it + 1 < nt) lt.store(s, buf ^ 1, tokl + (it + 1) * kBN, tid);
-    if (it + 2 < nt) lt.pages_to_slots(tokl + (it + 2) * kBN, page_shift, tid);
-    __syncthreads();
+    wr.pv(cur.v, pf, lane);
+  };
+
+  __syncthreads();  // the list
+  fetch(0);
+  __builtin_amdgcn_s_waitcnt(0);  // Q, the sink and tile 0's entries
+  request(0, s0);
+  if (nt > 1) fetch(1);
+  for (int it = 0; it < nt; it += 2) {
+    step(it, s0, s1);
+    if (it + 1 < nt) step(it + 1, s1, s0);
   }
+  // no load may still write this workgroup's LDS when it exits
+  wait_vmcnt<0>();
   wr.finish(o + (size_t)qbase * Hq * D, lse ? lse + (size_t)h * total_q + qbase : nullptr, nq,
             Hq, h, row0, hh, l32);
 }
@@ -884,7 +829,7 @@ hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream) {
   // offsets (chunked-prefill workload: 2.33 -> 2.07 ms against 64-bit
   // addresses per 16-byte chunk); larger ones through global addresses
   const long long kv_bytes = a.kv_rows * a.Hkv * a.D * 2;
-  const bool buf = kv_bytes > 0 && kv_bytes < (1LL << 32);
+  const bool buf = kv_bytes > 0 && kv_bytes <= (long long)kNoRow;
   auto run = [&](auto d, auto qb, auto use_buf) {
     constexpr int D = decltype(d)::value, QB = decltype(qb)::value;
     const dim3 grid((unsigned)fwd_workgroups(a.B, a.max_seqlen_q, a.Hq, a.Hkv, D));
@@ -928,7 +873,7 @@ hipError_t launch_index_bf16(const IndexArgs& a, hipStream_t stream) {
 #endif
   // caches below 4 GiB through buffer resources, as in launch_extend_bf16
   const long long kv_bytes = a.kv_rows * a.Hkv * a.D * 2;
-  const bool buf = kv_bytes > 0 && kv_bytes < (1LL << 32);
+  const bool buf = kv_bytes > 0 && kv_bytes <= (long long)kNoRow;
   auto run = [&](auto d, auto qb, auto use_buf) {
     constexpr int D = decltype(d)::value, QB = decltype(qb)::value;
     const dim3 grid((unsigned)index_workgroups(a.B, a.max_seqlen_q, a.Hq, a.Hkv, D));
