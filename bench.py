@@ -181,8 +181,10 @@ def kernel_stats(trace_csv, parts):
     kernel_trace.csv of a `rocprofv3 --kernel-trace` run of this script with
     these parts."""
     import csv
+    # submission order (a kernel's start timestamp can precede the end of the
+    # one submitted before it)
     with open(trace_csv) as f:
-        recs = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+        recs = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
     names = [_short(r["Kernel_Name"]) for r in recs]
     rows = {}
     for r, n, p in zip(recs, names, _label(names, parts)):

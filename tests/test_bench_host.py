@@ -49,13 +49,15 @@ def test_a_dispatch_out_of_order_is_an_error():
 
 
 def _write_trace(path, rows):
-    cols = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y",
-            "Grid_Size_Z"]
+    """rows in submission order; written shuffled by start time like a trace
+    whose kernels overlap at their ends."""
+    cols = ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X",
+            "Grid_Size_Y", "Grid_Size_Z"]
     with open(path, "w", newline="") as f:
         w = csv.writer(f)
         w.writerow(cols)
-        for name, t0, t1, g in rows:
-            w.writerow([name, t0, t1, g, 1, 1])
+        for i, (name, t0, t1, g) in enumerate(rows):
+            w.writerow([i + 1, name, t0, t1, g, 1, 1])
 
 
 def test_kernel_stats_per_part(tmp_path, capsys):
@@ -69,6 +71,10 @@ def test_kernel_stats_per_part(tmp_path, capsys):
         for name, dur in step:
             rows.append((name, t, t + dur, 4096))
             t += dur + 1
+    # the dSink reduction's start stamped before the start of the main kernel
+    # submitted ahead of it: labels follow the submission order
+    name, t0, t1, g = rows[4]
+    rows[4] = (name, rows[3][1] - 5, rows[3][1], g)
     _write_trace(p, rows)
     bench.kernel_stats(str(p), ["prefill", "train"])
     out = capsys.readouterr().out.splitlines()
