@@ -41,8 +41,9 @@
  *     library never synchronises: work is enqueued on `hip_stream` (a
  *     hipStream_t; NULL = the default stream).  It allocates no device memory
  *     at run time.  Its state: a thread-local error message; per device, the
- *     number of paged-decode workgroups resident at once (queried from HIP on
- *     the first decode call with equal token ranges, then reused); and, for
+ *     number of paged-decode workgroups resident at once and of chunked-prefill
+ *     workgroups resident per XCD (queried from HIP on the first call that
+ *     needs them, then reused); and, for
  *     attn_sink_fwd_decode_paged_noalloc only, a fixed device array per device
  *     (below).
  *   - Outputs are overwritten (never accumulated into) and must not alias

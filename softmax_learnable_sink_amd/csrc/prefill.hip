@@ -21,6 +21,7 @@
 // tokens of one index list).
 //
 // fp32 path: a plain VALU kernel, one thread per query row, K/V tiles in LDS.
+#include <atomic>
 #include <climits>
 #include <type_traits>
 
@@ -498,7 +499,7 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
     const int32_t* __restrict__ seqlens, const int32_t* __restrict__ cu_k,
     const float* __restrict__ sink, __bf16* __restrict__ o, float* __restrict__ lse, int B,
     int total_q, int max_sq, int Hq, int Hkv, int hpw, int page_shift, int max_pages, float sl2,
-    int causal, int w1, int w2, uint32_t kv_bytes) {
+    int causal, int w1, int w2, uint32_t kv_bytes, int round_wgs) {
   ATTN_SINK_CHECK_GUARD();
   __shared__ KvTile<D> s0, s1;  // one LDS variable per tile buffer
   constexpr int RW = 32 * QB;
@@ -538,6 +539,14 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
   const int pmask = (1 << page_shift) - 1;
   const TileRange tr = tile_range(L, geom.p_min, geom.p_max, causal, w1, w2);
   const int nt = tr.count();
+  // Key order.  With the XCD-aware order each XCD walks its pairs' workgroups
+  // in sequence, round_wgs at a time (those resident on it at once), and every
+  // round streams the whole context of its pair.  Odd rounds walk the keys
+  // backwards, so they start on the keys the round before them read last,
+  // which are still in that XCD's L2 (chunked-prefill workload: 1.56 -> 1.36x
+  // the algorithmic HBM bytes).  The softmax does not depend on the order.
+  const bool rev = round_wgs > 0 && (B * Hkv) % 8 == 0 && ((blockIdx.x / 8) / round_wgs) % 2 == 1;
+  auto tile_at = [&](int it) { return rev ? tr.tile(nt - 1 - it) : tr.tile(it); };
   constexpr int GU = GatherDma<D, BUF>::U;
   GatherDma<D, BUF> gd;
   gd.init(wave, lane);
@@ -545,11 +554,11 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
     if (bt_row) {
 #pragma unroll
       for (int u = 0; u < GU; ++u)
-        gd.page[u] = bt_row[min(tr.tile(it) * kBN + gd.row[u], L - 1) >> page_shift];
+        gd.page[u] = bt_row[min(tile_at(it) * kBN + gd.row[u], L - 1) >> page_shift];
     }
   };
   auto request = [&](int it, KvTile<D>& dst) {  // slots of tile it's rows, then the loads
-    const int key0 = tr.tile(it) * kBN;
+    const int key0 = tile_at(it) * kBN;
 #pragma unroll
     for (int u = 0; u < GU; ++u) {
       const int key = key0 + gd.row[u];
@@ -565,7 +574,7 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
     tile_barrier();
     if (it + 1 < nt) request(it + 1, ahead);
     if (it + 2 < nt) fetch(it + 2);
-    const int key0 = tr.tile(it) * kBN;
+    const int key0 = tile_at(it) * kBN;
     f32x16 st[2][QB];
     bf16x8 pf[2][QB][2];
     if (WaveRows<D, QB>::needs_mask(key0, geom)) {
@@ -806,6 +815,31 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+namespace {
+// Workgroups of extend_kernel<D, QB, BUF> resident on one XCD at once (the
+// device's CUs / 8 x workgroups per CU), per device, computed on the first
+// call; 0 (keys in order everywhere) if HIP cannot tell.
+template <int D, int QB, bool BUF>
+int extend_round_wgs() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, extend_kernel<D, QB, BUF>, kThreads,
+                                                   0) != hipSuccess ||
+      cus < 8 || per_cu <= 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  c = cus / 8 * per_cu;
+  cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+}  // namespace
+
 hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream) {
   const int g = a.Hq / a.Hkv;
   const int hpw = heads_per_wg(g);
@@ -832,11 +866,12 @@ hipError_t launch_extend_bf16(const ExtendArgs& a, hipStream_t stream) {
   const bool buf = kv_bytes > 0 && kv_bytes <= (long long)kNoRow;
   auto run = [&](auto d, auto qb, auto use_buf) {
     constexpr int D = decltype(d)::value, QB = decltype(qb)::value;
+    constexpr bool BUF = decltype(use_buf)::value;
     const dim3 grid((unsigned)fwd_workgroups(a.B, a.max_seqlen_q, a.Hq, a.Hkv, D));
-    extend_kernel<D, QB, decltype(use_buf)::value><<<grid, kThreads, 0, stream>>>(
+    extend_kernel<D, QB, BUF><<<grid, kThreads, 0, stream>>>(
         q, kc, vc, a.block_table, a.cu_seqlens_q, a.seqlens_k, a.cu_seqlens_k, a.sink, o, a.lse,
         a.B, a.total_q, a.max_seqlen_q, a.Hq, a.Hkv, hpw, shift, a.max_pages, sl2, a.causal, a.w1,
-        a.w2, (uint32_t)(buf ? kv_bytes : 0));
+        a.w2, (uint32_t)(buf ? kv_bytes : 0), extend_round_wgs<D, QB, BUF>());
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
