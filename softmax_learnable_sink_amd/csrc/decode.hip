@@ -621,15 +621,56 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
     nsp = nsel > 0 ? min(max_splits, (nsel + chunk - 1) / chunk) : 0;
   }
   const float sig2 = sink ? sink[h] * kLog2e : kNegInf;
+  constexpr int DPL = D / 64;
+  float od[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) od[i] = 0.f;
+  float M = sig2, z = 0.f;
+
+  if (nsp <= 8) {
+    // up to 8 pieces (the equal-range grids have about B_total/B + 1 per
+    // sequence): every lane loads every piece's (m, l) and its own d of the
+    // accumulators at once, one memory round trip instead of three
+    float mk[8], lk[8], ak[8][DPL];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      mk[j] = kNegInf;
+      lk[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) ak[j][i] = 0.f;
+      if (j < nsp) {  // wave-uniform
+        const float* pk = base + (size_t)j * (D + 2);
+        mk[j] = pk[D];
+        lk[j] = pk[D + 1];
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) ak[j][i] = pk[lane + 64 * i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) M = fmaxf(M, mk[j]);
+    const float Mu = M == kNegInf ? 0.f : M;  // nothing visible and no sink
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = exp2_fast(mk[j] - Mu);  // 0 for pieces past the end
+      z += f * lk[j];
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) od[i] += f * ak[j][i];
+    }
+    if (sig2 != kNegInf) z += exp2_fast(sig2 - Mu);
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) o[(size_t)bh * D + lane + 64 * i] = (__bf16)(od[i] * inv);
+    if (lse && lane == 0)
+      lse[LIST ? (size_t)h * B + b : (size_t)bh] = z > 0.f ? (Mu + log2_fast(z)) * kLn2 : kNegInf;
+    return;
+  }
 
   // pass 1: lane k reads chunk k's (m, l); the max and the weighted sum of l
   // are wave reductions, so no load waits on another
-  float M = sig2;
   for (int k = lane; k < nsp; k += 64) M = fmaxf(M, base[(size_t)k * (D + 2) + D]);
 #pragma unroll
   for (int x = 32; x >= 1; x >>= 1) M = wave_max_xor(M, x);
   const float Mu = M == kNegInf ? 0.f : M;  // nothing visible and no sink
-  float z = 0.f;
   for (int k = lane; k < nsp; k += 64) {
     const float* pk = base + (size_t)k * (D + 2);
     z += exp2_fast(pk[D] - Mu) * pk[D + 1];
@@ -638,10 +679,6 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(
   for (int x = 32; x >= 1; x >>= 1) z += __shfl_xor(z, x, 64);
 
   // pass 2: lane = d; chunks in groups of 8 with all loads issued first
-  constexpr int DPL = D / 64;
-  float od[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) od[i] = 0.f;
   for (int k0 = 0; k0 < nsp; k0 += 8) {
     float mk[8], ak[8][DPL];
 #pragma unroll
