@@ -86,3 +86,21 @@ def test_decode_on_a_cache_past_4gib(window):
     check_close("O", host64(o), ro, TOL_O)
     check_close("LSE", host64(lse), rl, TOL_LSE)
     del k, v
+
+
+def test_index_rows_on_a_cache_past_4gib():
+    need_gpu()
+    from softmax_learnable_sink_amd import binding
+    say("case: index rows B3 H8/2 D64 P16 q~U[1,40] ctx~U[0,3000] topk 256, cache > 4 GiB, "
+        "seed 13")
+    case = synth.index_case(3, 8, 2, 64, 16, 1, 40, 0, 3000, 1, 256, seed=13, nan_poison=True)
+    k, v, bt = _embed(case)
+    o, lse = binding.attn_sink_fwd_index_rows_paged(
+        dev_tensor(case["q"], synth.BF16), k, v, bt, tidx._i32(case["cu_seqlens_q"]),
+        tidx._i32(case["seqlens"]), tidx._i32(case["kv_index"]),
+        torch.from_numpy(case["sink"]).cuda(), softmax_scale=0.125)
+    torch.cuda.synchronize()
+    ro, rl = tidx._oracle_rows(case, 0.125)
+    check_close("O", host64(o), ro, TOL_O)
+    check_close("LSE", host64(lse), rl, TOL_LSE)
+    del k, v
