@@ -104,3 +104,36 @@ def test_index_rows_on_a_cache_past_4gib():
     check_close("O", host64(o), ro, TOL_O)
     check_close("LSE", host64(lse), rl, TOL_LSE)
     del k, v
+
+
+def test_varlen_forward_on_keys_past_4gib():
+    """Packed K/V whose rows of the real sequences lie past 4 GiB: a first
+    sequence with no queries owns the first 4 GiB of (never read) key rows."""
+    need_gpu()
+    import numpy as np
+
+    import oracle
+    from softmax_learnable_sink_amd import binding
+    from tests.gpu_util import vals
+    say("case: varlen forward B2 H8/2 D64 nq~U[1,300] causal sink behind a 4 GiB empty-query "
+        "sequence, seed 11")
+    case = synth.varlen_case(2, 8, 2, 64, 1, 300, None, None, seed=11)
+    total_k, Hkv, D = case["k"].shape
+    skip = (4 << 30) // (Hkv * D * 2) + 16  # rows of the query-less first sequence
+    k = torch.empty((skip + total_k, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((skip + total_k, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    k[skip:] = dev_tensor(case["k"], synth.BF16)
+    v[skip:] = dev_tensor(case["v"], synth.BF16)
+    cq = np.concatenate([[0], case["cu_seqlens_q"]]).astype(np.int32)
+    ck = np.concatenate([[0], skip + case["cu_seqlens_k"]]).astype(np.int32)
+    o, lse = binding.attn_sink_fwd_varlen(
+        dev_tensor(case["q"], synth.BF16), k, v, tidx._i32(cq), tidx._i32(ck),
+        case["max_seqlen_q"], torch.from_numpy(case["sink"]).cuda(), causal=True,
+        softmax_scale=0.125)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_varlen(vals(case["q"], synth.BF16), case["cu_seqlens_q"],
+                                   vals(case["k"], synth.BF16), vals(case["v"], synth.BF16),
+                                   case["cu_seqlens_k"], case["sink"], 0.125, causal=True)
+    check_close("O", host64(o), ro, TOL_O)
+    check_close("LSE", host64(lse), rl, TOL_LSE)
+    del k, v
