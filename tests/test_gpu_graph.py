@@ -104,3 +104,49 @@ def test_backward_replays_in_a_graph():
 
     cap, eager = buffers(), buffers()
     _replay_and_compare(lambda: run(cap), list(cap[:4]), lambda: run(eager))
+
+
+def test_chunked_prefill_replays_in_a_graph():
+    """The extend kernel's tiles are gathered straight into LDS and its key order
+    depends on the workgroups resident per XCD (queried on the first call)."""
+    need_gpu()
+    from softmax_learnable_sink_amd import binding
+    say("case: graph extend B3 H16/2 D64 P16 q~U[1,300] ctx~U[0,900] window (40,200)")
+    c = synth.extend_case(3, 16, 2, 64, 16, 1, 300, 0, 900, seed=8)
+    q, kc, vc = (dev_tensor(c[n], synth.BF16) for n in ("q", "k_cache", "v_cache"))
+    bt = torch.from_numpy(c["block_table"]).cuda()
+    cu = torch.from_numpy(c["cu_seqlens_q"]).cuda()
+    sl = torch.from_numpy(c["seqlens"]).cuda()
+    sink = torch.from_numpy(c["sink"]).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((16, q.shape[0]), dtype=torch.float32, device=q.device)
+
+    def run(out, l):
+        return binding.attn_sink_fwd_extend_paged(q, kc, vc, bt, cu, sl, c["max_seqlen_q"], sink,
+                                                  softmax_scale=0.125, window=(40, 200),
+                                                  out=out, lse=l)
+
+    o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+    _replay_and_compare(lambda: run(o, lse), [o, lse], lambda: run(o2, lse2))
+
+
+def test_index_lists_replay_in_a_graph():
+    need_gpu()
+    from softmax_learnable_sink_amd import binding
+    say("case: graph index B2 H16/2 D64 P16 q~U[60,200] ctx~U[100,2000] block 128 topk 256")
+    c = synth.index_case(2, 16, 2, 64, 16, 60, 200, 100, 2000, 128, 256, seed=4, shuffle=True)
+    q, kc, vc = (dev_tensor(c[n], synth.BF16) for n in ("q", "k_cache", "v_cache"))
+    i32 = {n: torch.from_numpy(c[n].astype("int32")).cuda()
+           for n in ("block_table", "cu_seqlens_q", "seqlens", "kv_index", "cu_blocks")}
+    sink = torch.from_numpy(c["sink"]).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((16, q.shape[0]), dtype=torch.float32, device=q.device)
+
+    def run(out, l):
+        return binding.attn_sink_fwd_index_paged(
+            q, kc, vc, i32["block_table"], i32["cu_seqlens_q"], i32["seqlens"], c["max_seqlen_q"],
+            i32["kv_index"], i32["cu_blocks"], c["block_q"], sink, softmax_scale=0.125, out=out,
+            lse=l)
+
+    o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+    _replay_and_compare(lambda: run(o, lse), [o, lse], lambda: run(o2, lse2))
