@@ -20,6 +20,7 @@
 //                    and accumulates dQ in registers
 //   bwd_main         (D 64) the dK/dV and dQ blocks in one launch
 //   bwd_dsink_reduce fixed-order sum of the dSink partials
+#include <cstddef>
 #include <type_traits>
 
 #include "checks.h"
@@ -64,8 +65,12 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16* nat, int r0, int db, int
 }
 
 // LDS tile buffers per pass: K/V or Q/dO tiles are loaded straight into LDS
-// one tile ahead of the one in use.
-constexpr int kBwdBufs = 2;
+// one tile (two buffers) or two tiles (three) ahead of the one in use.  D = 64
+// runs two workgroups per CU and keeps two buffers (three measured 1.3 %
+// slower on training: the longer unrolled loop spills); D = 128 runs one
+// workgroup per CU and takes three (backward 3 % faster).
+template <int D>
+constexpr int bwd_bufs() { return D == 64 ? 2 : 3; }
 
 // Rows of sequence b.  A dense batch (cu_q == NULL) has Sq query and Sk key
 // rows per sequence and LSE laid out [B, Hq, Sq]; a packed variable-length
@@ -170,13 +175,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dsink_reduce_kernel(
 // Lane (hh, l32) holds key l32 and query rows 32*qb + 16*hh + i.
 // ---------------------------------------------------------------------------
 // One tile buffer of the dK/dV pass: 64 rows of Q and of dO (rows permuted,
-// the tile-load layout) and the rows' LSE * log2(e) and -Di.
+// the tile-load layout) and the rows' LSE * log2(e) and -Di (the first 64 of
+// each row vector; one 1 KB load fills it, zeros past the rows).
 template <int D>
 struct DkdvTile {
   __bf16 q[kTile * (D + kPad)];
   __bf16 dO[kTile * (D + kPad)];
-  alignas(16) float lse2[kTile];
-  alignas(16) float ndi[kTile];
+  alignas(16) float lse2[4 * kTile];
+  alignas(16) float ndi[4 * kTile];
 };
 
 #define DKDV_PARAMS                                                                             \
@@ -245,10 +251,12 @@ __device__ __forceinline__ void dkdv_block(DkdvTile<D>& t0, DkdvTile<D>& t1, Dkd
   auto row_of = [&](int it) { return (t_hi - 1 - it / g) * kTile; };
 
   // Tile loads straight into LDS: SP 1 KB loads of Q and SP of dO (rows
-  // permuted), 256 B of LSE * log2(e) and of -Di.  Waves 0 and 1 load Q,
+  // permuted), and the 64 rows' LSE * log2(e) and -Di.  Waves 0 and 1 load Q,
   // waves 2 and 3 dO, each every other load j = (wave & 1) + 2u; SP is odd,
   // so the odd waves' last load (j = SP) is the row vector instead (wave 1
-  // the LSE, wave 3 -Di).  Every wave issues U loads per tile.
+  // the LSE, wave 3 -Di).  Every wave issues U loads per tile, all of the
+  // same kind with no branch between them: a branch there made the compiler
+  // hold the first LDS read of each step on the loads of the tile after next.
   constexpr int SP = kDmaSlots(D), U = (SP + 1) / 2;
   static_assert(SP % 2 == 1, "odd slot count per row");
   const bool wq = wave < 2;
@@ -256,7 +264,7 @@ __device__ __forceinline__ void dkdv_block(DkdvTile<D>& t0, DkdvTile<D>& t1, Dkd
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int j = (wave & 1) + 2 * u;
-    doff[u] = j < SP ? dma_offset<D>(j, lane, (uint32_t)(rs * 2), true) : 4u * lane;
+    doff[u] = j < SP ? dma_offset<D>(j, lane, (uint32_t)(rs * 2), true) : 16u * lane;
   }
   // iteration it into buffer t; past the last iteration the loads read an
   // empty resource, so that every step issues the same loads
@@ -270,14 +278,15 @@ __device__ __forceinline__ void dkdv_block(DkdvTile<D>& t0, DkdvTile<D>& t1, Dkd
     const auto rt = make_rsrc((wq ? q : dout) + ((size_t)sr.q0 * Hq + h) * D + (size_t)i0 * rs,
                               (uint32_t)((size_t)nrow * rs * 2));
     const auto rr = make_rsrc((wq ? lse2 : ndi) + sr.l0 + h * sr.lh + i0, (uint32_t)nrow * 4u);
-    __bf16* dst = wq ? t.q : t.dO;
-    float* dstr = wq ? t.lse2 : t.ndi;
+    // destinations as byte offsets from the buffer
+    char* tb = reinterpret_cast<char*>(&t);
+    const uint32_t fo = wq ? offsetof(DkdvTile<D>, q) : offsetof(DkdvTile<D>, dO);
+    const uint32_t ro = wq ? offsetof(DkdvTile<D>, lse2) : offsetof(DkdvTile<D>, ndi);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if ((wave & 1) + 2 * u < SP)
-        dma16(rt, dst + 512 * ((wave & 1) + 2 * u), doff[u]);
-      else
-        dma4(rr, dstr, doff[u]);
+      const int j = (wave & 1) + 2 * u;
+      const bool row = j >= SP;
+      dma16(row ? rr : rt, tb + (row ? ro : fo + 1024u * j), doff[u]);
     }
   };
 
@@ -442,7 +451,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(DKD
   // one LDS variable per tile buffer, so that the compiler can tell the
   // buffer a load in flight writes from the one being read
   __shared__ DkdvTile<D> t0, t1;
-  if constexpr (kBwdBufs == 3) {
+  if constexpr (bwd_bufs<D>() == 3) {
     __shared__ DkdvTile<D> t2;
     dkdv_block<D, 3>(t0, t1, t2, blockIdx.x, blockIdx.y, blockIdx.z, q, k, v, dout, lse2, ndi, dk,
                      dv, cu_q, cu_k, Sq, Sk, Hq, Hkv, total_q, scale, sl2, causal, w1, w2);
@@ -718,7 +727,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dq_kernel(DQ_PARAMS) {
   ATTN_SINK_CHECK_GUARD();
   __shared__ DqTile<D> t0, t1;  // one LDS variable per tile buffer
-  if constexpr (kBwdBufs == 3) {
+  if constexpr (bwd_bufs<D>() == 3) {
     __shared__ DqTile<D> t2;
     dq_block<D, dq_qb<D>(), 3>(t0, t1, t2, blockIdx.x, q, k, v, dout, lse2, ndi, dq, cu_q, cu_k,
                                B, Sq, Sk, Hq, Hkv, total_q, hpw, scale, sl2, causal, w1, w2);
@@ -750,7 +759,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_main_kernel(
   ATTN_SINK_CHECK_GUARD();
   __shared__ BwdTile<D> t0, t1;  // one LDS variable per tile buffer
   const int w = blockIdx.x;
-  if constexpr (kBwdBufs == 3) {
+  if constexpr (bwd_bufs<D>() == 3) {
     __shared__ BwdTile<D> t2;
     if (w < nkv)
       dkdv_block<D, 3>(t0.kv, t1.kv, t2.kv, w % Hkv, (w / Hkv) % B, w / (Hkv * B), q, k, v, dout,

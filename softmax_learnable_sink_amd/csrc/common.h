@@ -66,8 +66,8 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
 }
 
 // ---------------------------------------------------------------------------
-// Tiles loaded straight into LDS (buffer_load_dword{,x4} ... lds).  Lane l of
-// one such load writes its 4 or 16 bytes to LDS at base + l * size, and a lane
+// Tiles loaded straight into LDS (buffer_load_dwordx4 ... lds).  Lane l of
+// one such load writes its 16 bytes to LDS at base + 16 l, and a lane
 // past the resource's end writes zeros.  The data never passes through VGPRs
 // and the waves write nothing to LDS themselves, so a tile can be requested
 // several tiles ahead at no register cost.
@@ -112,10 +112,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint3
 typedef __attribute__((address_space(1))) void global_void;
 __device__ __forceinline__ void dma16_global(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)lds, 16, 0, 0);
-}
-// One 4-byte-per-lane (256 B) load into LDS at lds (wave-uniform).
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
