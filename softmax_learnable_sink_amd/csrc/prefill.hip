@@ -124,6 +124,8 @@ struct WaveRows {
   float sig2;
 
   // qrow0: row 0 of this sequence in a [rows, Hq, D] layout; rows >= Sq are zero.
+  // NTQ: read Q non-temporally (it is read once; the L2 is kept for K/V).
+  template <bool NTQ = false>
   __device__ __forceinline__ void init(const __bf16* qrow0, const float* sink, int Sq, int Hq,
                                        int h, int wrow0, int hh, int l32) {
     // Q^T fragments (B operand): query row wrow0 + 32*qb + l32, d = 16*ks + 8*hh ..
@@ -133,8 +135,12 @@ struct WaveRows {
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         if (row < Sq) {
-          qf[qb][ks] = *reinterpret_cast<const bf16x8*>(
+          const bf16x8* src = reinterpret_cast<const bf16x8*>(
               qrow0 + ((size_t)row * Hq + h) * D + 16 * ks + 8 * hh);
+          if constexpr (NTQ)
+            qf[qb][ks] = __builtin_nontemporal_load(src);
+          else
+            qf[qb][ks] = *src;
         } else {
           qf[qb][ks] = bf16x8{};
         }
@@ -284,28 +290,48 @@ struct WaveRows {
 
   // Fold the sink into the denominator once, normalise, store O and LSE.
   // orow0: row 0 of this sequence in O [rows, Hq, D]; lse_row0: this head's
-  // LSE of row 0 (rows contiguous), or NULL.
+  // LSE of row 0 (rows contiguous), or NULL.  The wave's O rows pass through
+  // its LDS region `stage` (rows of D + 8 elements), so that every store
+  // instruction writes whole lines of O (the prefill and index-list kernels
+  // 1.5 % faster than with each lane storing its 8-byte pieces).  NTO: write
+  // O non-temporally, which only whole-line stores make cheap.
+  template <bool NTO = false>
   __device__ __forceinline__ void finish(__bf16* orow0, float* lse_row0, int Sq, int Hq, int h,
-                                         int wrow0, int hh, int l32) {
+                                         int wrow0, int hh, int l32, __bf16* stage, int lane) {
+    constexpr int SS = D + 8, RW = 32 * QB, CPR = D / 8;  // stage stride, rows, chunks per row
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int row = wrow0 + 32 * qb + l32;
       float lt = l[qb] + __shfl_xor(l[qb], 32, 64);
       if (sig2 != kNegInf) lt += exp2_fast(sig2 - m[qb]);
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      if (row < Sq) {
-        __bf16* orow = orow0 + ((size_t)row * Hq + h) * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const f32x16& x = acc[db][qb];
-            *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * a + 4 * hh) =
-                to_bf16x4(x[4 * a] * inv, x[4 * a + 1] * inv, x[4 * a + 2] * inv,
-                          x[4 * a + 3] * inv);
-          }
-        if (lse_row0 && hh == 0)
-          lse_row0[row] = lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : kNegInf;
+        for (int a = 0; a < 4; ++a) {
+          const f32x16& x = acc[db][qb];
+          *reinterpret_cast<bf16x4*>(stage + (32 * qb + l32) * SS + 32 * db + 8 * a + 4 * hh) =
+              to_bf16x4(x[4 * a] * inv, x[4 * a + 1] * inv, x[4 * a + 2] * inv,
+                        x[4 * a + 3] * inv);
+        }
+      if (lse_row0 && hh == 0 && row < Sq)
+        lse_row0[row] = lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : kNegInf;
+    }
+    // the wave's own LDS writes are in order before its reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int c0 = 0; c0 < RW * CPR; c0 += 64) {
+      const int r = (c0 + lane) / CPR, ch = (c0 + lane) % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * SS + 8 * ch);
+      if (wrow0 + r < Sq) {
+        u32x4* dst =
+            reinterpret_cast<u32x4*>(orow0 + ((size_t)(wrow0 + r) * Hq + h) * D + 8 * ch);
+        if constexpr (NTO)
+          __builtin_nontemporal_store(v, dst);
+        else
+          *dst = v;
       }
     }
   }
@@ -423,10 +449,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       step(it + 1, s1, s0);
     }
   }
-  // no load may still write this workgroup's LDS when it exits
+  // no load may still write this workgroup's LDS; then the tile buffers stage O
   wait_vmcnt<0>();
+  __syncthreads();
+  __bf16* stage = wave < 2 ? (wave == 0 ? s0.k : s0.v) : (wave == 2 ? s1.k : s1.v);
   wr.finish(o + (size_t)b * Sq * Hq * D, lse ? lse + ((size_t)b * Hq + h) * Sq : nullptr, Sq, Hq,
-            h, wrow0, hh, l32);
+            h, wrow0, hh, l32, stage, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -526,8 +554,11 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
   const RowGeom geom{L, causal, w1, w2, off + row0, off + min(nq, row0 + R) - 1,
                      off + wrow0 + l32};
 
+  // Q is read and O written non-temporally: with them out of the L2, more of
+  // the pair's context stays there between the rounds below (chunked-prefill
+  // workload: 1.35 -> 1.06x the algorithmic HBM bytes, the same time).
   WaveRows<D, QB> wr;
-  wr.init(q + (size_t)qbase * Hq * D, sink, nq, Hq, h, wrow0, hh, l32);
+  wr.template init<true>(q + (size_t)qbase * Hq * D, sink, nq, Hq, h, wrow0, hh, l32);
 
   // K/V tiles gathered straight into LDS one tile ahead; the block-table
   // entries of a tile are read a tile before that
@@ -596,11 +627,14 @@ __global__ __launch_bounds__(kThreads, 2) void extend_kernel(
       step(it, s0, s1);
       if (it + 1 < nt) step(it + 1, s1, s0);
     }
-    // no load may still write this workgroup's LDS when it exits
+    // no load may still write this workgroup's LDS
     wait_vmcnt<0>();
   }
-  wr.finish(o + (size_t)qbase * Hq * D, lse ? lse + (size_t)h * total_q + qbase : nullptr, nq,
-            Hq, h, wrow0, hh, l32);
+  __syncthreads();  // the tile buffers stage O
+  __bf16* stage = wave < 2 ? (wave == 0 ? s0.k : s0.v) : (wave == 2 ? s1.k : s1.v);
+  wr.template finish<true>(o + (size_t)qbase * Hq * D,
+                           lse ? lse + (size_t)h * total_q + qbase : nullptr, nq, Hq, h, wrow0,
+                           hh, l32, stage, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -718,10 +752,12 @@ __global__ __launch_bounds__(kThreads, 2) void index_kernel(
     step(it, s0, s1);
     if (it + 1 < nt) step(it + 1, s1, s0);
   }
-  // no load may still write this workgroup's LDS when it exits
+  // no load may still write this workgroup's LDS; then the tile buffers stage O
   wait_vmcnt<0>();
+  __syncthreads();
+  __bf16* stage = wave < 2 ? (wave == 0 ? s0.k : s0.v) : (wave == 2 ? s1.k : s1.v);
   wr.finish(o + (size_t)qbase * Hq * D, lse ? lse + (size_t)h * total_q + qbase : nullptr, nq,
-            Hq, h, row0, hh, l32);
+            Hq, h, row0, hh, l32, stage, lane);
 }
 
 // ---------------------------------------------------------------------------
