@@ -64,6 +64,27 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16* nat, int r0, int db, int
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Rows [0, NR) of a wave's LDS region `stage` (rows of D + 8 elements) to
+// global memory, 16 bytes per lane, eight lanes per row at D = 64: every store
+// instruction writes whole rows instead of 8-byte pieces of 32 rows.  row_ptr(r)
+// is row r's destination, NULL to skip it.  The caller has written the rows.
+template <int D, int NR, typename RowPtr>
+__device__ __forceinline__ void store_staged(const __bf16* stage, int lane, RowPtr row_ptr) {
+  constexpr int SS = D + kPad, CPR = D / 8;
+  static_assert((NR * CPR) % 64 == 0, "whole store instructions");
+  // the wave's own LDS writes are in order before its reads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int c0 = 0; c0 < NR * CPR; c0 += 64) {
+    const int r = (c0 + lane) / CPR, ch = (c0 + lane) % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * SS + 8 * ch);
+    __bf16* dst = row_ptr(r);
+    if (dst) *reinterpret_cast<u32x4*>(dst + 8 * ch) = v;
+  }
+}
+
 // LDS tile buffers per pass: K/V or Q/dO tiles are loaded straight into LDS
 // one tile (two buffers) or two tiles (three) ahead of the one in use.  D = 64
 // runs two workgroups per CU and keeps two buffers (three measured 1.3 %
@@ -424,23 +445,28 @@ __device__ __forceinline__ void dkdv_block(DkdvTile<D>& t0, DkdvTile<D>& t1, Dkd
       step(it + 1, t1, t0);
     }
   }
-  // no load may still write this workgroup's LDS when it exits
+  // no load may still write this workgroup's LDS; then the tile buffers stage
+  // dK (rows 0 .. 31 of the wave's region) and dV (rows 32 .. 63)
   wait_vmcnt<0>();
-
-  if (key < nk) {
-    const size_t base = ((size_t)(sr.k0 + key) * Hkv + kvh) * D;
+  __syncthreads();
+  constexpr int NS2 = D + kPad;
+  __bf16* stage = wave < 2 ? (wave == 0 ? t0.q : t0.dO) : (wave == 2 ? t1.q : t1.dO);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d = 32 * db + 8 * a + 4 * hh;
-        *reinterpret_cast<bf16x4*>(dk + base + d) =
-            to_bf16x4(dka[db][4 * a] * scale, dka[db][4 * a + 1] * scale,
-                      dka[db][4 * a + 2] * scale, dka[db][4 * a + 3] * scale);
-        *reinterpret_cast<bf16x4*>(dv + base + d) =
-            to_bf16x4(dva[db][4 * a], dva[db][4 * a + 1], dva[db][4 * a + 2], dva[db][4 * a + 3]);
-      }
-  }
+    for (int a = 0; a < 4; ++a) {
+      const int d = 32 * db + 8 * a + 4 * hh;
+      *reinterpret_cast<bf16x4*>(stage + l32 * NS2 + d) =
+          to_bf16x4(dka[db][4 * a] * scale, dka[db][4 * a + 1] * scale,
+                    dka[db][4 * a + 2] * scale, dka[db][4 * a + 3] * scale);
+      *reinterpret_cast<bf16x4*>(stage + (32 + l32) * NS2 + d) =
+          to_bf16x4(dva[db][4 * a], dva[db][4 * a + 1], dva[db][4 * a + 2], dva[db][4 * a + 3]);
+    }
+  store_staged<D, 64>(stage, lane, [&](int r) -> __bf16* {
+    const int kr = k0 + 32 * wave + (r & 31);
+    if (kr >= nk) return nullptr;
+    return (r < 32 ? dk : dv) + ((size_t)(sr.k0 + kr) * Hkv + kvh) * D;
+  });
 }
 
 // grid: (Hkv, B, key blocks) with the key block slowest, so the key blocks
@@ -699,23 +725,22 @@ __device__ __forceinline__ void dq_block(DqTile<D>& t0, DqTile<D>& t1, DqTile<D>
       step(it + 1, t1, t0);
     }
   }
-  // no load may still write this workgroup's LDS when it exits
+  // no load may still write this workgroup's LDS; then the tile buffers stage dQ
   wait_vmcnt<0>();
-
+  __syncthreads();
+  __bf16* stage = wave < 2 ? (wave == 0 ? t0.k : t0.v) : (wave == 2 ? t1.k : t1.v);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = wrow0 + 32 * qb + l32;
-    if (row < nq) {
-      __bf16* dst = dq + ((size_t)(sr.q0 + row) * Hq + h) * D;
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-          *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * a + 4 * hh) =
-              to_bf16x4(dqa[db][qb][4 * a] * scale, dqa[db][qb][4 * a + 1] * scale,
-                        dqa[db][qb][4 * a + 2] * scale, dqa[db][qb][4 * a + 3] * scale);
-    }
-  }
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<bf16x4*>(stage + (32 * qb + l32) * NS + 32 * db + 8 * a + 4 * hh) =
+            to_bf16x4(dqa[db][qb][4 * a] * scale, dqa[db][qb][4 * a + 1] * scale,
+                      dqa[db][qb][4 * a + 2] * scale, dqa[db][qb][4 * a + 3] * scale);
+  store_staged<D, RW>(stage, lane, [&](int r) -> __bf16* {
+    return wrow0 + r < nq ? dq + ((size_t)(sr.q0 + wrow0 + r) * Hq + h) * D : nullptr;
+  });
 }
 
 // Rows per wave of the dQ blocks: two 32-row blocks at D = 64, one at D = 128
