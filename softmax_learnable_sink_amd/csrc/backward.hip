@@ -268,8 +268,9 @@ __device__ __forceinline__ void dkdv_block(DkdvTile<D>& t0, DkdvTile<D>& t1, Dkd
   // Q/dO tiles at the same time and share them in L2.  Training workload
   // (B2 S8192 64/8 heads): 6.6 -> 1.6 GB of HBM reads per launch against the
   // first tile first, head by head; the time is the same.
-  auto head_of = [&](int it) { return kvh * g + it % g; };
-  auto row_of = [&](int it) { return (t_hi - 1 - it / g) * kTile; };
+  // The iterations are requested and computed in order, so both walk the
+  // (head, tile) sequence with counters instead of dividing by g (fewer scalar
+  // instructions per step: training -0.9 %).
 
   // Tile loads straight into LDS: SP 1 KB loads of Q and SP of dO (rows
   // permuted), and the 64 rows' LSE * log2(e) and -Di.  Waves 0 and 1 load Q,
@@ -287,18 +288,16 @@ __device__ __forceinline__ void dkdv_block(DkdvTile<D>& t0, DkdvTile<D>& t1, Dkd
     const int j = (wave & 1) + 2 * u;
     doff[u] = j < SP ? dma_offset<D>(j, lane, (uint32_t)(rs * 2), true) : 16u * lane;
   }
-  // iteration it into buffer t; past the last iteration the loads read an
+  // the next iteration to request: its head (within the group), its first
+  // row and the rows' addresses; past the last iteration the loads read an
   // empty resource, so that every step issues the same loads
-  auto request = [&](int it, DkdvTile<D>& t) {
-    int h = 0, i0 = 0, nrow = 0;
-    if (it < niter) {
-      h = head_of(it);
-      i0 = row_of(it);
-      nrow = nq - i0;
-    }
-    const auto rt = make_rsrc((wq ? q : dout) + ((size_t)sr.q0 * Hq + h) * D + (size_t)i0 * rs,
-                              (uint32_t)((size_t)nrow * rs * 2));
-    const auto rr = make_rsrc((wq ? lse2 : ndi) + sr.l0 + h * sr.lh + i0, (uint32_t)nrow * 4u);
+  int rq_h = 0, rq_i0 = (t_hi - 1) * kTile, rq_left = niter;
+  const __bf16* rq_t = (wq ? q : dout) + ((size_t)sr.q0 * Hq + kvh * g) * D + (size_t)rq_i0 * rs;
+  const float* rq_r = (wq ? lse2 : ndi) + sr.l0 + (size_t)(kvh * g) * sr.lh + rq_i0;
+  auto request = [&](DkdvTile<D>& t) {
+    const int nrow = rq_left > 0 ? nq - rq_i0 : 0;
+    const auto rt = make_rsrc(rq_t, (uint32_t)((size_t)nrow * rs * 2));
+    const auto rr = make_rsrc(rq_r, (uint32_t)nrow * 4u);
     // destinations as byte offsets from the buffer
     char* tb = reinterpret_cast<char*>(&t);
     const uint32_t fo = wq ? offsetof(DkdvTile<D>, q) : offsetof(DkdvTile<D>, dO);
@@ -309,7 +308,18 @@ __device__ __forceinline__ void dkdv_block(DkdvTile<D>& t0, DkdvTile<D>& t1, Dkd
       const bool row = j >= SP;
       dma16(row ? rr : rt, tb + (row ? ro : fo + 1024u * j), doff[u]);
     }
+    --rq_left;
+    if (++rq_h == g) {  // past the group's last head: head 0 of the previous tile
+      rq_h = 0;
+      rq_i0 -= kTile;
+      rq_t -= (size_t)(g - 1) * D + (size_t)kTile * rs;
+      rq_r -= (size_t)(g - 1) * sr.lh + kTile;
+    } else {
+      rq_t += D;
+      rq_r += sr.lh;
+    }
   };
+  int st_h = 0, st_i0 = (t_hi - 1) * kTile;  // the same walk for the steps
 
   // One step: wait until iteration it's tile has landed (the next NB - 2
   // tiles' loads may stay in flight); after the barrier it has for every
@@ -319,9 +329,13 @@ __device__ __forceinline__ void dkdv_block(DkdvTile<D>& t0, DkdvTile<D>& t1, Dkd
   auto step = [&](int it, DkdvTile<D>& cur, DkdvTile<D>& ahead) {
     wait_vmcnt<(NB - 2) * U>();
     tile_barrier();
-    request(it + NB - 1, ahead);
+    request(ahead);
     if (it >= niter) return;
-    const int i0 = row_of(it);
+    const int i0 = st_i0;
+    if (++st_h == g) {
+      st_h = 0;
+      st_i0 -= kTile;
+    }
     const int p0 = off + i0;
     const bool need_mask = (i0 + kTile > nq) || (causal && p0 < k1 - 1) ||
                            (w2 > 0 && k1 - 1 >= w1 && p0 + kTile - 1 - w2 >= k0);
@@ -431,9 +445,9 @@ __device__ __forceinline__ void dkdv_block(DkdvTile<D>& t0, DkdvTile<D>& t1, Dkd
   };
 
   __builtin_amdgcn_s_waitcnt(0);  // the K^T / V^T fragments
-  request(0, t0);
+  request(t0);
   if constexpr (NB == 3) {
-    request(1, t1);
+    request(t1);
     for (int it = 0; it < niter; it += 3) {
       step(it, t0, t2);
       step(it + 1, t1, t0);
