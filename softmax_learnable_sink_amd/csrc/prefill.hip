@@ -678,23 +678,60 @@ __global__ __launch_bounds__(kThreads, 2) void index_kernel(
   const int p_lane = L - nq + row0 + l32;
   const int nt = (topk + kBN - 1) / kBN;
 
-  // the block's list -> LDS, padded to whole tiles; entries outside [0, L) are
-  // empty.  Wave w stages tiles w, w + 4, ... and records each tile's largest
-  // token, so tiles whose tokens all precede the workgroup's first row skip
+  // The block's list -> LDS, padded to whole tiles, entries outside [0, L)
+  // empty (INT_MAX), with the tokens that every row of the workgroup sees (at
+  // or before its first row) moved in front of the others.  The attention does
+  // not depend on the order of the keys, and then only the tiles after those
+  // tokens need the mask, whatever order the list comes in (a top-k list
+  // ordered by score, not by position).  Thread i partitions entries
+  // [i EPT, (i + 1) EPT) after a scan of the counts.  Then each tile's largest
+  // token is recorded, so tiles whose tokens all precede the first row skip
   // the mask.
+  const int p_first = L - nq + row0;
   {
+    constexpr int EPT = kMaxList / kThreads;
+    __shared__ int wsum[kThreads / 64];
     const int32_t* list = kv_index + (size_t)(cu_blocks[b] + row0 / block_q) * topk;
-    for (int e = tid; e < nt * kBN; e += kThreads) {
+    const int n = nt * kBN;
+    int tk[EPT], ne = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid * EPT + i;
       const int x = e < topk ? list[e] : -1;
-      const int t = ((x >= 0) & (x < L)) ? x : INT_MAX;
-      tokl[e] = t;
-      int mx = t;
+      tk[i] = ((x >= 0) & (x < L)) ? x : INT_MAX;
+      ne += (e < n) & (tk[i] <= p_first);
+    }
+    int incl = ne;  // inclusive scan of the early counts over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = incl - ne, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      before += w < wave ? wsum[w] : 0;
+      total += wsum[w];
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid * EPT + i;
+      if (e < n) {
+        const bool early = tk[i] <= p_first;
+        tokl[early ? before : total + (e - before)] = tk[i];
+        before += early;
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < n; e += kThreads) {
+      int mx = tokl[e];
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d, 64));
       if (lane == 0) tmax[e / kBN] = mx;
     }
   }
-  const int p_first = L - nq + row0;
 
   WaveRows<D, QB> wr;
   wr.init(q + (size_t)qbase * Hq * D, sink, nq, Hq, h, row0, hh, l32);
