@@ -150,3 +150,61 @@ def test_index_lists_replay_in_a_graph():
 
     o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
     _replay_and_compare(lambda: run(o, lse), [o, lse], lambda: run(o2, lse2))
+
+
+def test_packed_training_replays_in_a_graph():
+    """The packed forward and backward (their grids are sized by the longest
+    sequence; workgroups past a sequence's rows exit at once)."""
+    need_gpu()
+    from softmax_learnable_sink_amd import binding
+    say("case: graph varlen fwd+bwd B4 H16/2 D64 q~U[1,300] causal")
+    c = synth.varlen_case(4, 16, 2, 64, 1, 300, seed=6, dout=True)
+    q, k, v, do = (dev_tensor(c[n], synth.BF16) for n in ("q", "k", "v", "dout"))
+    cq = torch.from_numpy(c["cu_seqlens_q"]).cuda()
+    ck = torch.from_numpy(c["cu_seqlens_k"]).cuda()
+    sink = torch.from_numpy(c["sink"]).cuda()
+    mq, mk = c["max_seqlen_q"], c["max_seqlen_k"]
+    tq = q.shape[0]
+    o, lse = torch.empty_like(q), torch.empty((16, tq), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ds = torch.empty_like(sink)
+    ws = torch.empty(binding.attn_sink_bwd_varlen_workspace_bytes(4, tq, mq, 16),
+                     dtype=torch.uint8, device=q.device)
+
+    def run(outs):
+        o_, l_, dq_, dk_, dv_, ds_ = outs
+        binding.attn_sink_fwd_varlen(q, k, v, cq, ck, mq, sink, causal=True, softmax_scale=0.125,
+                                     out=o_, lse=l_)
+        binding.attn_sink_bwd_varlen(q, k, v, o_, do, l_, cq, ck, mq, mk, sink, causal=True,
+                                     softmax_scale=0.125, dq=dq_, dk=dk_, dv=dv_, dsink=ds_,
+                                     workspace=ws)
+        return outs
+
+    mine = [o, lse, dq, dk, dv, ds]
+    other = [torch.empty_like(t) for t in mine]
+    _replay_and_compare(lambda: run(mine), mine, lambda: run(other))
+
+
+def test_index_rows_replay_in_a_graph():
+    """Per-row lists run the decode kernels in list mode (workspace given)."""
+    need_gpu()
+    from softmax_learnable_sink_amd import binding
+    say("case: graph index rows B2 H16/2 D64 P16 q~U[5,40] ctx~U[100,900] topk 128 shuffled")
+    c = synth.index_case(2, 16, 2, 64, 16, 5, 40, 100, 900, 1, 128, seed=7, shuffle=True)
+    q, kc, vc = (dev_tensor(c[n], synth.BF16) for n in ("q", "k_cache", "v_cache"))
+    i32 = {n: torch.from_numpy(c[n].astype("int32")).cuda()
+           for n in ("block_table", "cu_seqlens_q", "seqlens", "kv_index")}
+    sink = torch.from_numpy(c["sink"]).cuda()
+    tq = q.shape[0]
+    ws = torch.empty(max(binding.attn_sink_index_rows_workspace_bytes(tq, 16, 2, 64, 128), 16),
+                     dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((16, tq), dtype=torch.float32, device=q.device)
+
+    def run(out, l):
+        return binding.attn_sink_fwd_index_rows_paged(
+            q, kc, vc, i32["block_table"], i32["cu_seqlens_q"], i32["seqlens"], i32["kv_index"],
+            sink, softmax_scale=0.125, out=out, lse=l, workspace=ws)
+
+    o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+    _replay_and_compare(lambda: run(o, lse), [o, lse], lambda: run(o2, lse2))
