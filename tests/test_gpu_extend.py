@@ -38,6 +38,8 @@ def _oracle(case, scale, window, use_sink=True):
     (2, 8, 2, 128, 16, 1, 140, 0, 250, None),         # D=128
     (2, 8, 2, 64, 16, 100, 200, 300, 500, (40, 90)),  # first/last window
     (2, 8, 1, 128, 8, 50, 120, 200, 400, (16, 64)),   # window, D=128, g=8
+    (2, 8, 2, 64, 256, 30, 200, 300, 1000, None),     # page 256: four tiles per page
+    (2, 8, 1, 128, 128, 50, 150, 200, 700, (16, 64)),  # page 128, window, D=128
 ])
 @pytest.mark.parametrize("use_sink", [True, False])
 def test_extend_matches_oracle(B, Hq, Hkv, D, P, qlo, qhi, clo, chi, window, use_sink):
