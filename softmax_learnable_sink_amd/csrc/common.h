@@ -24,6 +24,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+// Start of a running max that has seen nothing: finite, below every score.
+constexpr float kMaxFloor = -3.4028234663852886e38f;  // -FLT_MAX
 
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -144,6 +146,16 @@ __device__ __forceinline__ float max_xor32(float x) {
       "v_max_f32 %0, %0, %1"
       : "+v"(a), "=&v"(b));
   return __builtin_bit_cast(float, a);
+}
+
+// max(a, b) as one v_max_f32 for operands that are never NaN: fmaxf adds an
+// instruction that quiets a loop-carried operand first (the compiler cannot
+// see that it is already quiet), and it turns v_med3 with +inf back into that
+// pair.
+__device__ __forceinline__ float max_no_quiet(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 __device__ __forceinline__ float wave_max_xor(float x, int mask) {

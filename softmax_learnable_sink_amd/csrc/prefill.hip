@@ -149,7 +149,7 @@ struct WaveRows {
     sig2 = sink ? sink[h] * kLog2e : kNegInf;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      m[qb] = sig2;
+      m[qb] = sig2 == kNegInf ? kMaxFloor : sig2;
       l[qb] = 0.f;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db][qb] = f32x16{};
@@ -234,7 +234,9 @@ struct WaveRows {
   }
 
   // Online softmax in base 2 with the exact running max of the tile, P rounded
-  // to bf16 for P V.
+  // to bf16 for P V.  The running max never is -inf (a row without a sink
+  // starts at kMaxFloor, below every score), so it needs no guard before it
+  // is subtracted: a row that has seen no key keeps p = 0 and alpha = 1.
   __device__ __forceinline__ void online(f32x16 (&st)[2][QB], bf16x8 (&pf)[2][QB][2], float sl2) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -244,18 +246,17 @@ struct WaveRows {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb][qb][i]);
       mx = max_xor32(mx);
-      const float m_new = fmaxf(m[qb], mx * sl2);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_fast(m[qb] - m_use);
+      const float m_new = max_no_quiet(m[qb], mx * sl2);
+      const float alpha = exp2_fast(m[qb] - m_new);
       m[qb] = m_new;
-      float rsum = 0.f;
+      float rsum;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = exp2_fast(__builtin_fmaf(st[kb][qb][i], sl2, -m_use));
+          const float p = exp2_fast(__builtin_fmaf(st[kb][qb][i], sl2, -m_new));
           st[kb][qb][i] = p;
-          rsum += p;
+          rsum = kb == 0 && i == 0 ? p : rsum + p;
         }
       l[qb] = l[qb] * alpha + rsum;
       // alpha == 1 exactly when no row of this block's max grew
